@@ -1,0 +1,64 @@
+"""The oracle against its pins, and the pins against planted mistakes (CPU only)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(oracle.Oracle())
+
+
+# Each mutation edits one spot of a private copy of oracle.c; the pins must notice.
+MUTATIONS = {
+    "drop_last_k_term": ("for (int k = 0; k < K; ++k) {\n          double a = (double)A",
+                         "for (int k = 0; k < K - 1; ++k) {\n          double a = (double)A"),
+    "beta_sign": ("cterm = beta * c;\n          cmag", "cterm = -beta * c;\n          cmag"),
+    "transposed_B_index": ("const float *brow = B + (size_t)k * ldb;",
+                           "const float *brow = B + (size_t)k;"),
+    "alpha_dropped": ("double r = skip_product ? 0.0 : alpha * acc[j];",
+                      "double r = skip_product ? 0.0 : acc[j];"),
+    "beta_zero_reads_C": ("if (beta != 0.0) {\n          double c = (double)C0[(size_t)i * ldc + j];",
+                          "if (1) {\n          double c = (double)C0[(size_t)i * ldc + j];"),
+    "lda_ignored": ("double a = (double)A[(size_t)i * lda + k];",
+                    "double a = (double)A[(size_t)i * K + k];"),
+    "gelu_cubic_constant": ("0.044715 * x * x * x", "0.04715 * x * x * x"),
+    "gelu_half_factor": ("return 0.5 * x * (1.0 + tanh(inner));", "return x * (1.0 + tanh(inner));"),
+    "half_exponent_bias": ("v = ldexp((double)(frac + 1024), expo - 25);",
+                           "v = ldexp((double)(frac + 1024), expo - 24);"),
+    "half_subnormal_scale": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
+    "hgemm_bias_row_index": ("double b = bias ? (double)bias[j] : 0.0;",
+                             "double b = bias ? (double)bias[i % N] : 0.0;"),
+    "den_missing_beta": ("cmag = fabs(beta) * fabs(c);\n        }\n        ref[",
+                         "cmag = 0.0;\n        }\n        ref["),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    src = open(oracle.SOURCE).read()
+    old, new = MUTATIONS[name]
+    assert src.count(old) >= 1, "mutation anchor %r not found in oracle.c" % name
+    mutated = src.replace(old, new, 1)
+    path = tmp_path / "oracle_mut.c"
+    path.write_text(mutated)
+    lib = tmp_path / "liboracle_mut.so"
+    oracle.build(True, str(path), str(lib))
+    # A mutant may crash (e.g. by reading a NULL C); run it in a child process, where a
+    # crash also counts as caught.
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import ctypes, json, oracle; from tests import oracle_pins; "
+            "o = oracle.Oracle(oracle._bind(ctypes.CDLL(%r))); "
+            "print(json.dumps(oracle_pins.failing_pins(o)))" % str(lib))
+    proc = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                          timeout=600, env=dict(os.environ, OMP_NUM_THREADS="2"))
+    if proc.returncode != 0:
+        return  # crashed: caught
+    bad = json.loads(proc.stdout.strip().splitlines()[-1])
+    assert bad, "no pin noticed the planted mistake %s" % name
