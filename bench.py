@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X GEMM library on one GPU.
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload sgemm_4096]
+
+One step is one library call on the named workload (default: FP32
+C = alpha*A*B + beta*C at M = N = K = 4096, alpha = 1, beta = 0.5, inputs
+U[-1, 1] from seed 1).  C is restored from a pristine copy before every call,
+outside the timed events.  Each call is bracketed by HIP events on the stream
+it is launched on; TFLOP/s = 2*M*N*K / mean call time.  The run prints ONE JSON
+line with the throughput, the roofline position of the GEMM kernel and the CPU
+oracle's own throughput on a bounded sample of the same workload (parity of
+this exact launch configuration is checked by the GPU test suite).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOPS at 4096³ FP32 (α,β) + % of MI355X matrix peak per dtype"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "sgemm": os.path.join(ROOT, "linear_algebra_sgemm_amd", "csrc", "sgemm_kernels.hip"),
+    "hgemm_bias_gelu": os.path.join(ROOT, "linear_algebra_sgemm_amd", "csrc", "hgemm_kernels.hip"),
+}
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="sgemm_4096")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def profiled_traffic(workload: str, op: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this workload,
+    or None when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, "%s_counters.md" % workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_src and m_bytes):
+        return None
+    if m_src.group(1) != source_digest(KERNEL_SOURCES[op]):
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, A, B, C, target_seconds: float):
+    """Time the CPU oracle (as it stands) on the first rows of the same workload."""
+    import torch
+
+    import oracle
+    from linear_algebra_sgemm_amd import cost
+    threads = oracle.max_threads()
+    M, N, K = w.M, w.N, w.K
+
+    def run(rows):
+        t0 = time.perf_counter()
+        if w.op == "sgemm":
+            oracle.sgemm(rows, N, K, w.alpha, A[:rows].numpy(), K, B.numpy(), N, w.beta,
+                         C[:rows].numpy(), N, with_den=False)
+        else:
+            a = A[:rows].contiguous().view(torch.int16).numpy().view("uint16")
+            b = B.contiguous().view(torch.int16).numpy().view("uint16")
+            oracle.hgemm_bias_act(rows, N, K, w.alpha, a, K, b, N, C.numpy(),
+                                  oracle.ACT_GELU_TANH, with_den=False)
+        return time.perf_counter() - t0
+
+    probe = min(M, 16)
+    t_probe = run(probe)
+    rows = int(max(probe, min(M, probe * target_seconds / max(t_probe, 1e-6))))
+    rows = max(probe, (rows // 8) * 8) if rows < M else M
+    t = run(rows)
+    tf = cost.gemm_flops(rows, N, K) / t / 1e12
+    return {"value": tf, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d output rows (%d x %d x %d), fp64 accumulation, %.1f s"
+                      % (rows, M, rows, N, K, t)}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+              "(--gpus %d was asked for)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_algebra_sgemm_amd as lib
+    from linear_algebra_sgemm_amd import cost, inputs
+
+    if args.workload not in inputs.WORKLOADS:
+        sys.exit("unknown workload %s (known: %s)" % (args.workload, ", ".join(inputs.WORKLOADS)))
+    w = inputs.WORKLOADS[args.workload]
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    steps = max(1, args.steps)
+
+    A, B, C = inputs.workload_inputs(w)   # C is the bias vector for the half-precision product
+    M, N, K = w.M, w.N, w.K
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, A, B, C, args.cpu_seconds)
+
+    lib.gemm_create()
+    dev = torch.device("cuda:0")
+    dA, dB = A.to(dev), B.to(dev)
+    stream = torch.cuda.current_stream()
+    if w.op == "sgemm":
+        dC0 = C.to(dev)
+        dC = dC0.clone()
+
+        def call():
+            lib.sgemm(M, N, K, w.alpha, dA, K, dB, N, w.beta, dC, N, stream=stream)
+
+        def reset():
+            dC.copy_(dC0)
+        dtype, flops_dtype = "f32", "f32"
+        nbytes = cost.sgemm_bytes(M, N, K, w.beta)
+    else:
+        dbias = C.to(dev)
+        dC = torch.empty((M, N), dtype=torch.float16, device=dev)
+
+        def call():
+            lib.hgemm_bias_act(M, N, K, w.alpha, dA, K, dB, N, dbias, lib.ACT_GELU_TANH, dC, N,
+                               stream=stream)
+
+        def reset():
+            pass
+        dtype, flops_dtype = "f16", "f16"
+        nbytes = cost.hgemm_bias_act_bytes(M, N, K)
+    flops = cost.gemm_flops(M, N, K)
+
+    for _ in range(args.warmup):
+        reset()
+        call()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        reset()
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    mean_ms = statistics.fmean(ms)
+    tflops = flops / (mean_ms * 1e-3) / 1e12
+    peak = cost.PEAK_TFLOPS[flops_dtype]
+
+    traffic = profiled_traffic(w.name, w.op)
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": w.op, "M": M, "N": N, "K": K, "alpha": w.alpha,
+                   "beta": w.beta, "layout": "row-major, packed",
+                   "inputs": "%s, seed %d" % (w.dist_ab, w.seed),
+                   "timing": "per-call HIP events on the launch stream, C reset before each "
+                             "call outside the events; ms_per_step is wall time per step "
+                             "including that reset"},
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "call_ms": {"mean": round(mean_ms, 5), "median": round(statistics.median(ms), 5),
+                    "min": round(min(ms), 5), "max": round(max(ms), 5)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes": nbytes,
+                     "kernel": "sgemm_mfma_kernel" if w.op == "sgemm" else "hgemm_mfma_kernel"},
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
+    }
+    lib.gemm_destroy()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,33 @@
+/*
+ * gemm_debug.h -- test hooks of the GEMM library (not needed by applications).
+ *
+ * The library picks a tile configuration from the problem shape.  Tests use
+ * these hooks to run every configuration, fast path and bounds-checked path,
+ * on the same inputs and to check the host-side choice without a GPU.
+ */
+#ifndef LINEAR_ALGEBRA_SGEMM_AMD_GEMM_DEBUG_H
+#define LINEAR_ALGEBRA_SGEMM_AMD_GEMM_DEBUG_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Force the tile configuration of later calls in this process: op 0 = sgemm,
+ * op 1 = hgemm_bias_act; tile -1 = choose by shape (the default), 0 = the
+ * largest tile, 1 = medium, 2 = small.  Whether the aligned fast path or the
+ * bounds-checked path runs still follows the shape and alignment.  Returns
+ * GEMM_STATUS_INVALID_VALUE for an unknown op or tile.  Pure host state: no
+ * HIP call.  Not synchronised with calls in flight on other threads.
+ */
+int gemm_debug_force_tile(int op, int tile);
+
+/* The tile configuration the library would choose for an M x N output on a
+ * device with `cus` compute units (op 0 = sgemm).  Pure host computation. */
+int gemm_debug_pick_tile(int op, int M, int N, int cus);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINEAR_ALGEBRA_SGEMM_AMD_GEMM_DEBUG_H */

@@ -1,0 +1,44 @@
+// Internal interface between the C ABI (gemm_capi.cpp) and the kernel files.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lasg {
+
+struct SgemmCall {
+  int M, N, K;
+  float alpha, beta;
+  const float* A;
+  int lda;
+  const float* B;
+  int ldb;
+  float* C;
+  int ldc;
+};
+
+struct HgemmCall {
+  int M, N, K;
+  float alpha;
+  const uint16_t* A;
+  int lda;
+  const uint16_t* B;
+  int ldb;
+  const float* bias;
+  int act;
+  uint16_t* C;
+  int ldc;
+};
+
+// Tile configuration choice for a shape on a device with `cus` compute units
+// (0 = 256x256, 1 = 128x128, 2 = 64x64).
+int sgemm_pick_tile(int M, int N, int cus);
+
+// force_tile < 0 lets the shape decide; otherwise it names the tile configuration.
+hipError_t launch_sgemm(const SgemmCall& c, int cus, int force_tile, hipStream_t s);
+hipError_t launch_sgemm_scale(int M, int N, float beta, float* C, int ldc, hipStream_t s);
+
+hipError_t launch_hgemm(const HgemmCall& c, int cus, int force_tile, hipStream_t s);
+
+}  // namespace lasg
