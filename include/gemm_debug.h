@@ -15,7 +15,9 @@ extern "C" {
 /*
  * Force the tile configuration of later calls in this process: op 0 = sgemm,
  * op 1 = hgemm_bias_act; tile -1 = choose by shape (the default), 0 = the
- * largest tile, 1 = medium, 2 = small.  Whether the aligned fast path or the
+ * largest tile, 1 = medium, 2 = small; sgemm also has 3 = largest tile with a
+ * K step of 32 and 4 = 128 x 256 tiles at two workgroups per compute unit.
+ * Whether the aligned fast path or the
  * bounds-checked path runs still follows the shape and alignment.  Returns
  * GEMM_STATUS_INVALID_VALUE for an unknown op or tile.  Pure host state: no
  * HIP call.  Not synchronised with calls in flight on other threads.

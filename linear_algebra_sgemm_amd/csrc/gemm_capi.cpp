@@ -139,7 +139,8 @@ const char* gemm_status_string(int status) {
 }
 
 int gemm_debug_force_tile(int op, int tile) {
-  if (tile < -1 || tile > 2) return GEMM_STATUS_INVALID_VALUE;
+  const int count = op == 0 ? lasg::kSgemmTileCount : lasg::kHgemmTileCount;
+  if (tile < -1 || tile >= count) return GEMM_STATUS_INVALID_VALUE;
   if (op == 0) {
     g_force_sgemm_tile.store(tile);
   } else if (op == 1) {

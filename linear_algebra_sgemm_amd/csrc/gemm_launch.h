@@ -31,8 +31,15 @@ struct HgemmCall {
   int ldc;
 };
 
-// Tile configuration choice for a shape on a device with `cus` compute units
-// (0 = 256x256, 1 = 128x128, 2 = 64x64).
+// Tile configurations.  SGEMM: 0 = 256x256 (K step 16), 1 = 128x128, 2 = 64x64,
+// 3 = 256x256 with K step 32, 4 = 128x256 at two workgroups per CU.
+// HGEMM: 0 = 256x256, 1 = 128x128, 2 = 64x64 (register-staged, K step 64),
+// 3 = 256x256 direct-to-LDS, 4 stages of K step 32 (whole tiles only; other
+// shapes fall back to 0).
+constexpr int kSgemmTileCount = 5;
+constexpr int kHgemmTileCount = 4;
+
+// Tile configuration the shape selects on a device with `cus` compute units.
 int sgemm_pick_tile(int M, int N, int cus);
 
 // force_tile < 0 lets the shape decide; otherwise it names the tile configuration.

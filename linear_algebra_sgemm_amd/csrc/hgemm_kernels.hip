@@ -246,9 +246,223 @@ __global__ void __launch_bounds__(T::THREADS) hgemm_mfma_kernel(HgemmArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant for whole tiles (M % BM == N % BN == K % BK == 0, A and
+// B rows 16-byte aligned).
+//
+// Loads go straight from global memory into LDS with global_load_lds_dwordx4
+// (lane l of one instruction writes its 16 bytes at base + 16 l), so no staging
+// registers are needed and STAGES - 1 K tiles can be in flight at once.  Since
+// each instruction picks the global chunk of every LDS slot, the stages are laid
+// out in the order the MFMA operands are read, which makes every fragment read
+// one contiguous, conflict-free block:
+//  * A, block (m-block ib, k-step s) = 1 KiB: slot l holds A[32 ib + l % 32]
+//    [16 s + 8 (l / 32) .. +7], read by lane l with one ds_read_b128.
+//  * B, block (k-step s, half t, n-block jb) = 512 B: 32 chunks of 8 columns of
+//    one row, in the order (h, cg, q, c2) so that lane l reads bytes [8l, 8l+8)
+//    with ds_read_b64_tr_b16.  That instruction transposes inside groups of 16
+//    lanes (lane 4a + b of a group receives element b of the rows loaded by
+//    lanes a, a + 4, a + 8, a + 12), so lane l ends up with B[16 s + 8 h + 4 t +
+//    e][32 jb + l % 32], e = 0..3: four consecutive k of its own column, the
+//    operand layout the MFMA wants, without any transposition in registers.
+// The MFMA is issued with the B fragment as its first operand and the A fragment
+// as its second, which yields C^T blocks: lane l then holds four consecutive
+// columns of one row of C and stores them with one 8-byte write.
+// ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+template <int BM_, int BN_, int BK_, int STAGES_>
+struct HDmaTile {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int WAVES_M = 2, WAVES_N = 2, WAVES = 4;
+  static constexpr int THREADS = WAVES * kWave;
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int KSTEPS = BK / 16;
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int B_BYTES = BK * BN * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_INSTR = A_BYTES / 1024;   // 1 KiB direct loads per stage
+  static constexpr int B_INSTR = B_BYTES / 1024;
+  static constexpr int A_PER_WAVE = A_INSTR / WAVES;
+  static constexpr int B_PER_WAVE = B_INSTR / WAVES;
+  static constexpr int LOADS_PER_TILE = A_PER_WAVE + B_PER_WAVE;   // per lane, counted by vmcnt
+
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert(BK % 16 == 0 && BN % 64 == 0, "k steps of 16; B loads cover 64 columns");
+  static_assert(A_INSTR % WAVES == 0 && B_INSTR % WAVES == 0, "loads split evenly over waves");
+  static_assert(STAGES >= 2 && STAGES * STAGE_BYTES <= 160 * 1024, "stages must fit in LDS");
+  static_assert((STAGES - 2) * LOADS_PER_TILE <= 63, "in-flight loads must fit vmcnt");
+  static_assert(FM * FN * 16 <= 256, "accumulators must fit in 256 registers per lane");
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// All LDS reads of this wave are complete, then the workgroup barrier.  (HIP's
+// __syncthreads would also wait for every outstanding global load, which would
+// drain the prefetch pipeline.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One direct global -> LDS copy of 16 bytes per lane: lane l writes LDS bytes
+// [lds_base + 16 l, +16).  Written as inline assembly so that the compiler does
+// not add its own "wait for every LDS-bound load" before later LDS reads; the
+// kernel orders these copies itself with wait_vmcnt and lds_barrier.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is listed as clobbered on purpose
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_base), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+template <class T>
+__device__ __forceinline__ void hdma_issue(const HgemmArgs& p, int m0, int n0, int k0,
+                                           uint8_t* stage, int wave, int lane) {
+#pragma unroll
+  for (int v = 0; v < T::A_PER_WAVE; ++v) {
+    const int ia = wave * T::A_PER_WAVE + v;      // = ib * KSTEPS + s
+    const int ib = ia / T::KSTEPS, s = ia % T::KSTEPS;
+    const int row = m0 + 32 * ib + lane % 32;
+    const int col = k0 + 16 * s + 8 * (lane / 32);
+    dma16(p.A + (size_t)row * p.lda + col, lds_offset(stage + ia * 1024));
+  }
+  uint8_t* bstage = stage + T::A_BYTES;
+#pragma unroll
+  for (int v = 0; v < T::B_PER_WAVE; ++v) {
+    const int ibb = wave * T::B_PER_WAVE + v;     // = (s * 2 + t) * (BN / 64) + jp
+    const int jp = ibb % (T::BN / 64);
+    const int st = ibb / (T::BN / 64);
+    const int s = st / 2, t = st % 2;
+    const int jb = 2 * jp + lane / 32;
+    const int pidx = lane % 32;                   // ((h * 2 + cg) * 4 + q) * 2 + c2
+    const int c2 = pidx & 1, q = (pidx >> 1) & 3, cg = (pidx >> 3) & 1, h = pidx >> 4;
+    const int row = k0 + 16 * s + 8 * h + 4 * t + q;
+    const int col = n0 + 32 * jb + 16 * cg + 8 * c2;
+    dma16(p.B + (size_t)row * p.ldb + col, lds_offset(bstage + ibb * 1024));
+  }
+}
+
+template <class T>
+__global__ void __launch_bounds__(T::THREADS) hgemm_dma_kernel(HgemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[T::STAGES * T::STAGE_BYTES];
+
+  int tile_m, tile_n;
+  tile_of_workgroup(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
+  const int m0 = tile_m * T::BM;
+  const int n0 = tile_n * T::BN;
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = wave / T::WAVES_N;
+  const int wn = wave % T::WAVES_N;
+
+  // acc[j][i]: C^T block of n-block j and m-block i of this wave.
+  f32x16 acc[T::FN][T::FM];
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+
+  const int ktiles = p.K / T::BK;
+#pragma unroll
+  for (int st = 0; st < T::STAGES - 1; ++st)
+    if (st < ktiles) hdma_issue<T>(p, m0, n0, st * T::BK, lds + st * T::STAGE_BYTES, wave, lane);
+
+  for (int kt = 0; kt < ktiles; ++kt) {
+    // Tile kt must have landed; the tiles issued after it may stay in flight.
+    const int ahead = ktiles - 1 - kt;
+    if (ahead >= T::STAGES - 2) {
+      wait_vmcnt<(T::STAGES - 2) * T::LOADS_PER_TILE>();
+    } else if (T::STAGES > 3 && ahead == 1) {
+      wait_vmcnt<(T::STAGES > 3 ? T::LOADS_PER_TILE : 0)>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    if (kt + T::STAGES - 1 < ktiles)
+      hdma_issue<T>(p, m0, n0, (kt + T::STAGES - 1) * T::BK,
+                    lds + ((kt + T::STAGES - 1) % T::STAGES) * T::STAGE_BYTES, wave, lane);
+
+    const uint8_t* As = lds + (kt % T::STAGES) * T::STAGE_BYTES;
+    const uint8_t* Bs = As + T::A_BYTES;
+#pragma unroll
+    for (int s = 0; s < T::KSTEPS; ++s) {
+      f16x8 af[T::FM], bf[T::FN];
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+        af[i] = *reinterpret_cast<const f16x8*>(As + ((wm * T::FM + i) * T::KSTEPS + s) * 1024 +
+                                                16 * lane);
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) {
+        const int jb = wn * T::FN + j;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(Bs + ((s * 2 + 0) * (T::BN / 32) + jb) * 512 + 8 * lane));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(Bs + ((s * 2 + 1) * (T::BN / 32) + jb) * 512 + 8 * lane));
+        const s16x4 both[2] = {lo, hi};
+        bf[j] = __builtin_bit_cast(f16x8, both);
+      }
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[j][i], 0, 0, 0);
+    }
+  }
+
+  // Epilogue.  Lane l holds, for n-block j, m-block i and q = 0..3, the four
+  // columns n = 8 q + 4 (l / 32) + 0..3 of row m = l % 32.
+  const float alpha = p.alpha;
+  const bool gelu = p.act == 1;
+  const bool vec_store = (p.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.C) & 7u) == 0);
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int col = n0 + wn * T::WTN + 32 * j + 8 * q + 4 * (lane / 32);
+      float bias4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (p.bias != nullptr) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bias4[e] = p.bias[col + e];
+      }
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) {
+        const int row = m0 + wm * T::WTM + 32 * i + lane % 32;
+        _Float16 h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = __builtin_fmaf(alpha, acc[j][i][4 * q + e], bias4[e]);
+          if (gelu) x = gelu_tanh(x);
+          h[e] = (_Float16)x;
+        }
+        uint16_t* dst = p.C + (size_t)row * p.ldc + col;
+        if (vec_store) {
+          *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, h);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[e] = __builtin_bit_cast(uint16_t, h[e]);
+        }
+      }
+    }
+  }
+}
+
 using HTileLarge = HgemmTile<256, 256, 64, 2, 2>;
 using HTileMedium = HgemmTile<128, 128, 64, 2, 2>;
 using HTileSmall = HgemmTile<64, 64, 64, 2, 2>;
+using HDmaLarge = HDmaTile<256, 256, 32, 4>;     // 4 stages x 32 KiB
 
 template <class T>
 static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s) {
@@ -273,13 +487,44 @@ static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <class T>
+static bool dma_fits(const HgemmCall& c) {
+  return c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % T::BK == 0 && c.lda % 8 == 0 &&
+         c.ldb % 8 == 0 && (reinterpret_cast<uintptr_t>(c.A) & 15u) == 0 &&
+         (reinterpret_cast<uintptr_t>(c.B) & 15u) == 0;
+}
+
+template <class T>
+static hipError_t launch_hdma(const HgemmCall& c, int group_m, hipStream_t s) {
+  HgemmArgs p;
+  p.M = c.M; p.N = c.N; p.K = c.K;
+  p.alpha = c.alpha;
+  p.A = c.A; p.lda = c.lda; p.B = c.B; p.ldb = c.ldb;
+  p.bias = c.bias; p.act = c.act;
+  p.C = c.C; p.ldc = c.ldc;
+  p.tiles_m = c.M / T::BM;
+  p.tiles_n = c.N / T::BN;
+  p.group_m = group_m;
+  hipLaunchKernelGGL((hgemm_dma_kernel<T>), dim3(p.tiles_m * p.tiles_n), dim3(T::THREADS), 0, s,
+                     p);
+  return hipGetLastError();
+}
+
 hipError_t launch_hgemm(const HgemmCall& c, int cus, int force_tile, hipStream_t s) {
   int tile = force_tile;
-  if (tile < 0) tile = sgemm_pick_tile(c.M, c.N, cus);
+  if (tile < 0) {
+    tile = sgemm_pick_tile(c.M, c.N, cus);
+    if (tile == 0) tile = 3;    // whole 256x256 tiles: the direct-to-LDS kernel
+  }
+  // The direct-to-LDS kernel needs whole tiles; otherwise fall back to the
+  // register-staged kernel of the same tile size, which handles every shape.
+  if (tile == 3 && !dma_fits<HDmaLarge>(c)) tile = 0;
   switch (tile) {
     case 0: return launch_htile<HTileLarge>(c, 4, s);
     case 1: return launch_htile<HTileMedium>(c, 8, s);
-    default: return launch_htile<HTileSmall>(c, 8, s);
+    case 2: return launch_htile<HTileSmall>(c, 8, s);
+    case 3: return launch_hdma<HDmaLarge>(c, 4, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

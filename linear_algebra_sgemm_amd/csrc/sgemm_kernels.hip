@@ -28,10 +28,13 @@
 
 namespace lasg {
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int WAVES_PER_SIMD_ = 1>
 struct SgemmTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  // Waves of this kernel that must fit on one SIMD at once (register budget:
+  // 512 / WAVES_PER_SIMD registers per lane, accumulators included).
+  static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;
   static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
   static constexpr int WTM = BM / WAVES_M;     // wave sub-tile rows
   static constexpr int WTN = BN / WAVES_N;     // wave sub-tile columns
@@ -51,7 +54,7 @@ struct SgemmTile {
   static_assert((BK * BN / 4) % THREADS == 0, "B tile must split evenly into float4 loads");
   static_assert(THREADS % (BK / 4) == 0 && THREADS % (BN / 4) == 0, "load rows must not wrap");
   static_assert(LDS_FLOATS * 4 <= 160 * 1024, "two stages must fit gfx950's 160 KiB of LDS");
-  static_assert(FM * FN * 16 <= 256, "accumulators must fit in 256 registers per lane");
+  static_assert(FM * FN * 16 <= 256 / WAVES_PER_SIMD, "accumulators must leave room for operands");
 };
 
 struct SgemmArgs {
@@ -128,7 +131,8 @@ struct Stage {
 };
 
 template <class T, bool EDGE>
-__global__ void __launch_bounds__(T::THREADS) sgemm_mfma_kernel(SgemmArgs p) {
+__global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(T::WAVES_PER_SIMD)))
+sgemm_mfma_kernel(SgemmArgs p) {
   __shared__ __attribute__((aligned(16))) float lds[T::LDS_FLOATS];
   float* const As0 = lds;
   float* const Bs0 = lds + T::A_STAGE;
@@ -198,10 +202,26 @@ __global__ void __launch_bounds__(T::THREADS) sgemm_mfma_kernel(SgemmArgs p) {
     __syncthreads();
   }
 
-  // Epilogue: C = alpha * acc + beta * C, C read only when beta != 0.
+  // Epilogue: C = alpha * acc + beta * C, C read only when beta != 0.  For each
+  // row of blocks, all C loads are issued before the first one is consumed, so
+  // their latencies overlap instead of adding up.
   const float alpha = p.alpha, beta = p.beta;
+  const bool read_c = beta != 0.0f;
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
+    float cv[T::FN][16];
+    if (read_c) {
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) {
+        const int col = n0 + wn * T::WTN + j * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * T::WTM + i * 32 + mfma32_row(r, lane);
+          const bool ok = !EDGE || (row < p.M && col < p.N);
+          cv[j][r] = ok ? p.C[(size_t)row * p.ldc + col] : 0.0f;
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) {
       const int col = n0 + wn * T::WTN + j * 32 + l32;
@@ -209,9 +229,8 @@ __global__ void __launch_bounds__(T::THREADS) sgemm_mfma_kernel(SgemmArgs p) {
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * T::WTM + i * 32 + mfma32_row(r, lane);
         if (EDGE && (row >= p.M || col >= p.N)) continue;
-        float* dst = p.C + (size_t)row * p.ldc + col;
         const float v = alpha * acc[i][j][r];
-        *dst = (beta != 0.0f) ? __builtin_fmaf(beta, *dst, v) : v;
+        p.C[(size_t)row * p.ldc + col] = read_c ? __builtin_fmaf(beta, cv[j][r], v) : v;
       }
     }
   }
@@ -232,9 +251,11 @@ __global__ void __launch_bounds__(256) sgemm_scale_kernel(int M, int N, float be
 // ---------------------------------------------------------------------------
 // Host-side launchers.
 // ---------------------------------------------------------------------------
-using TileLarge = SgemmTile<256, 256, 16, 2, 2>;   // 4 waves, 128 x 128 each
-using TileMedium = SgemmTile<128, 128, 16, 2, 2>;  // 4 waves, 64 x 64 each
-using TileSmall = SgemmTile<64, 64, 16, 2, 2>;     // 4 waves, 32 x 32 each
+using TileLarge = SgemmTile<256, 256, 16, 2, 2>;     // 4 waves, 128 x 128 each, 1 wave/SIMD
+using TileMedium = SgemmTile<128, 128, 16, 2, 2>;    // 4 waves, 64 x 64 each
+using TileSmall = SgemmTile<64, 64, 16, 2, 2>;       // 4 waves, 32 x 32 each
+using TileLargeK32 = SgemmTile<256, 256, 32, 2, 2>;  // as TileLarge, half the barriers
+using TileTall = SgemmTile<128, 256, 16, 2, 2, 2>;   // 4 waves, 64 x 128 each, 2 workgroups/CU
 
 template <class T>
 static hipError_t launch_tile(const SgemmCall& c, bool edge, int group_m, hipStream_t s) {
@@ -276,7 +297,10 @@ hipError_t launch_sgemm(const SgemmCall& c, int cus, int force_tile, hipStream_t
   switch (tile) {
     case 0: return launch_tile<TileLarge>(c, !fits_fast_path<TileLarge>(c), 4, s);
     case 1: return launch_tile<TileMedium>(c, !fits_fast_path<TileMedium>(c), 8, s);
-    default: return launch_tile<TileSmall>(c, !fits_fast_path<TileSmall>(c), 8, s);
+    case 2: return launch_tile<TileSmall>(c, !fits_fast_path<TileSmall>(c), 8, s);
+    case 3: return launch_tile<TileLargeK32>(c, !fits_fast_path<TileLargeK32>(c), 4, s);
+    case 4: return launch_tile<TileTall>(c, !fits_fast_path<TileTall>(c), 8, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -17,7 +17,7 @@ from tests.gpu_helpers import FP32_TOL, note, run_sgemm, sgemm_error
 
 pytestmark = pytest.mark.gpu
 
-TILES = (0, 1, 2)   # 256x256, 128x128, 64x64
+TILES = (0, 1, 2, 3, 4)   # 256x256, 128x128, 64x64, 256x256 (K step 32), 128x256
 
 
 @pytest.fixture(scope="module", autouse=True)
