@@ -111,7 +111,9 @@ def test_tile_choice(so):
     assert lib.gemm_debug_pick_tile(0, 256, 256, 256) == 2
     assert lib.gemm_debug_pick_tile(0, 1000, 3000, 256) in (1, 2)
     assert lib.gemm_debug_force_tile(0, 5) == lib.STATUS_INVALID_VALUE
-    assert lib.gemm_debug_force_tile(1, 3) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(1, 4) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(1, 3) == lib.STATUS_SUCCESS
+    assert lib.gemm_debug_force_tile(1, -1) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(0, 4) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(5, 0) == lib.STATUS_INVALID_VALUE
     assert lib.gemm_debug_force_tile(0, -1) == lib.STATUS_SUCCESS
