@@ -176,6 +176,11 @@ def main():
     peak = cost.PEAK_TFLOPS[flops_dtype]
 
     traffic = profiled_traffic(w.name, w.op)
+    if w.op == "sgemm":
+        tile = lib.gemm_debug_pick_tile(0, M, N, torch.cuda.get_device_properties(0).multi_processor_count)
+        kernel_name = "sgemm_mfma_kernel, tile config %d" % tile
+    else:
+        kernel_name = "hgemm_dma_kernel (256x256, direct-to-LDS)"
     line = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -202,7 +207,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": traffic,
                      "algorithmic_bytes": nbytes,
-                     "kernel": "sgemm_mfma_kernel" if w.op == "sgemm" else "hgemm_mfma_kernel"},
+                     "kernel": kernel_name},
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),
     }

@@ -39,8 +39,11 @@ struct HgemmCall {
 constexpr int kSgemmTileCount = 5;
 constexpr int kHgemmTileCount = 4;
 
-// Tile configuration the shape selects on a device with `cus` compute units.
+// Tile configuration the shape selects on a device with `cus` compute units
+// (for the half product, `dma_ok` says whether operand alignment and leading
+// dimensions allow the direct-to-LDS kernel).
 int sgemm_pick_tile(int M, int N, int cus);
+int hgemm_pick_tile(int M, int N, int K, int cus, bool dma_ok);
 
 // force_tile < 0 lets the shape decide; otherwise it names the tile configuration.
 hipError_t launch_sgemm(const SgemmCall& c, int cus, int force_tile, hipStream_t s);

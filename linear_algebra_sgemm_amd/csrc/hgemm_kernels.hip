@@ -305,9 +305,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // All LDS reads of this wave are complete, then the workgroup barrier.  (HIP's
 // __syncthreads would also wait for every outstanding global load, which would
-// drain the prefetch pipeline.)
+// drain the prefetch pipeline.)  The wait is the compiler's own s_waitcnt so that
+// its wait-count bookkeeping knows the LDS reads before it are done; the empty
+// asm statements keep the compiler from moving memory accesses across.
 __device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // One direct global -> LDS copy of 16 bytes per lane: lane l writes LDS bytes
@@ -326,35 +331,98 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// Global address of the 16-byte chunk that lane `lane` of direct load `v` (0 ..
+// LOADS_PER_TILE - 1) of wave `wave` copies, and the offset of its LDS slot
+// inside one stage.
 template <class T>
-__device__ __forceinline__ void hdma_issue(const HgemmArgs& p, int m0, int n0, int k0,
-                                           uint8_t* stage, int wave, int lane) {
-#pragma unroll
-  for (int v = 0; v < T::A_PER_WAVE; ++v) {
+__device__ __forceinline__ const uint16_t* hdma_source(const HgemmArgs& p, int m0, int n0, int k0,
+                                                       int v, int wave, int lane,
+                                                       uint32_t& stage_offset) {
+  if (v < T::A_PER_WAVE) {
     const int ia = wave * T::A_PER_WAVE + v;      // = ib * KSTEPS + s
     const int ib = ia / T::KSTEPS, s = ia % T::KSTEPS;
+    stage_offset = ia * 1024;
     const int row = m0 + 32 * ib + lane % 32;
     const int col = k0 + 16 * s + 8 * (lane / 32);
-    dma16(p.A + (size_t)row * p.lda + col, lds_offset(stage + ia * 1024));
+    return p.A + (size_t)row * p.lda + col;
   }
-  uint8_t* bstage = stage + T::A_BYTES;
+  const int ibb = wave * T::B_PER_WAVE + (v - T::A_PER_WAVE);   // = (s * 2 + t) * (BN / 64) + jp
+  const int jp = ibb % (T::BN / 64);
+  const int st = ibb / (T::BN / 64);
+  const int s = st / 2, t = st % 2;
+  const int jb = 2 * jp + lane / 32;
+  const int pidx = lane % 32;                     // ((h * 2 + cg) * 4 + q) * 2 + c2
+  const int c2 = pidx & 1, q = (pidx >> 1) & 3, cg = (pidx >> 3) & 1, h = pidx >> 4;
+  stage_offset = T::A_BYTES + ibb * 1024;
+  const int row = k0 + 16 * s + 8 * h + 4 * t + q;
+  const int col = n0 + 32 * jb + 16 * cg + 8 * c2;
+  return p.B + (size_t)row * p.ldb + col;
+}
+
+template <class T>
+__device__ __forceinline__ void hdma_issue_all(const HgemmArgs& p, int m0, int n0, int k0,
+                                               uint32_t stage_base, int wave, int lane) {
 #pragma unroll
-  for (int v = 0; v < T::B_PER_WAVE; ++v) {
-    const int ibb = wave * T::B_PER_WAVE + v;     // = (s * 2 + t) * (BN / 64) + jp
-    const int jp = ibb % (T::BN / 64);
-    const int st = ibb / (T::BN / 64);
-    const int s = st / 2, t = st % 2;
-    const int jb = 2 * jp + lane / 32;
-    const int pidx = lane % 32;                   // ((h * 2 + cg) * 4 + q) * 2 + c2
-    const int c2 = pidx & 1, q = (pidx >> 1) & 3, cg = (pidx >> 3) & 1, h = pidx >> 4;
-    const int row = k0 + 16 * s + 8 * h + 4 * t + q;
-    const int col = n0 + 32 * jb + 16 * cg + 8 * c2;
-    dma16(p.B + (size_t)row * p.ldb + col, lds_offset(bstage + ibb * 1024));
+  for (int v = 0; v < T::LOADS_PER_TILE; ++v) {
+    uint32_t off;
+    const uint16_t* src = hdma_source<T>(p, m0, n0, k0, v, wave, lane, off);
+    dma16(src, stage_base + off);
+  }
+}
+
+// MFMA operand fragments of one k step of one wave.
+template <class T>
+struct HFrags {
+  f16x8 a[T::FM];
+  f16x8 b[T::FN];
+};
+
+template <class T>
+__device__ __forceinline__ void hload_frags(HFrags<T>& f, const uint8_t* stage, int s, int wm,
+                                            int wn, int lane) {
+  const uint8_t* As = stage;
+  const uint8_t* Bs = stage + T::A_BYTES;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+    f.a[i] = *reinterpret_cast<const f16x8*>(As + ((wm * T::FM + i) * T::KSTEPS + s) * 1024 +
+                                             16 * lane);
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j) {
+    const int jb = wn * T::FN + j;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)(Bs + ((s * 2 + 0) * (T::BN / 32) + jb) * 512 + 8 * lane));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)(Bs + ((s * 2 + 1) * (T::BN / 32) + jb) * 512 + 8 * lane));
+    const s16x4 both[2] = {lo, hi};
+    f.b[j] = __builtin_bit_cast(f16x8, both);
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void hmfma(f32x16 (&acc)[T::FN][T::FM], const HFrags<T>& f, int idx) {
+  const int j = idx / T::FM, i = idx % T::FM;
+  acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[j][i], 0, 0, 0);
+}
+
+// Wait until at most `ahead` tiles of direct loads are still in flight.
+template <class T>
+__device__ __forceinline__ void wait_tiles_in_flight(int ahead) {
+  static_assert(T::STAGES <= 5, "extend the cases below for deeper pipelines");
+  if (ahead >= 3 && T::STAGES >= 5) {
+    wait_vmcnt<(T::STAGES >= 5 ? 3 * T::LOADS_PER_TILE : 0)>();
+  } else if (ahead >= 2 && T::STAGES >= 4) {
+    wait_vmcnt<(T::STAGES >= 4 ? 2 * T::LOADS_PER_TILE : 0)>();
+  } else if (ahead >= 1 && T::STAGES >= 3) {
+    wait_vmcnt<(T::STAGES >= 3 ? T::LOADS_PER_TILE : 0)>();
+  } else {
+    wait_vmcnt<0>();
   }
 }
 
 template <class T>
 __global__ void __launch_bounds__(T::THREADS) hgemm_dma_kernel(HgemmArgs p) {
+  static_assert(T::KSTEPS % 2 == 0, "fragments ping-pong between two register sets");
+  static_assert(T::LOADS_PER_TILE <= T::FM * T::FN, "one direct load per MFMA at most");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[T::STAGES * T::STAGE_BYTES];
 
   int tile_m, tile_n;
@@ -365,6 +433,7 @@ __global__ void __launch_bounds__(T::THREADS) hgemm_dma_kernel(HgemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wm = wave / T::WAVES_N;
   const int wn = wave % T::WAVES_N;
+  const uint32_t lds_base = lds_offset(lds);
 
   // acc[j][i]: C^T block of n-block j and m-block i of this wave.
   f32x16 acc[T::FN][T::FM];
@@ -375,50 +444,78 @@ __global__ void __launch_bounds__(T::THREADS) hgemm_dma_kernel(HgemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
+  // Pipeline.  Tile kt lives in stage kt % STAGES.  Its direct loads are issued
+  // in the middle of tile kt - STAGES + 1; in the middle of every tile kt the
+  // waves wait for tile kt + 1 to land, meet at one barrier (which also frees
+  // stage (kt - 1) % STAGES), issue the loads of tile kt + STAGES - 1 into that
+  // stage between the MFMAs of kt's last k step, and read the first fragments
+  // of tile kt + 1.  Fragments of the next k step are always read while the
+  // MFMAs of the current one run.
   const int ktiles = p.K / T::BK;
+  HFrags<T> fa, fb;
+  if (ktiles > 0) {
 #pragma unroll
-  for (int st = 0; st < T::STAGES - 1; ++st)
-    if (st < ktiles) hdma_issue<T>(p, m0, n0, st * T::BK, lds + st * T::STAGE_BYTES, wave, lane);
+    for (int st = 0; st < T::STAGES - 1; ++st)
+      if (st < ktiles) hdma_issue_all<T>(p, m0, n0, st * T::BK, lds_base + st * T::STAGE_BYTES,
+                                         wave, lane);
+    wait_tiles_in_flight<T>(ktiles - 1 < T::STAGES - 2 ? ktiles - 1 : T::STAGES - 2);
+    lds_barrier();
+    hload_frags<T>(fa, lds, 0, wm, wn, lane);
+  }
 
   for (int kt = 0; kt < ktiles; ++kt) {
-    // Tile kt must have landed; the tiles issued after it may stay in flight.
-    const int ahead = ktiles - 1 - kt;
-    if (ahead >= T::STAGES - 2) {
-      wait_vmcnt<(T::STAGES - 2) * T::LOADS_PER_TILE>();
-    } else if (T::STAGES > 3 && ahead == 1) {
-      wait_vmcnt<(T::STAGES > 3 ? T::LOADS_PER_TILE : 0)>();
-    } else {
-      wait_vmcnt<0>();
+    const uint8_t* stage = lds + (kt % T::STAGES) * T::STAGE_BYTES;
+    // k steps 0 .. KSTEPS-2: read the next step's fragments under this step's MFMAs.
+#pragma unroll
+    for (int s = 0; s + 1 < T::KSTEPS; ++s) {
+      HFrags<T>& cur = (s % 2 == 0) ? fa : fb;
+      HFrags<T>& nxt = (s % 2 == 0) ? fb : fa;
+      hload_frags<T>(nxt, stage, s + 1, wm, wn, lane);
+#pragma unroll
+      for (int x = 0; x < T::FM * T::FN; ++x) hmfma<T>(acc, cur, x);
+#pragma unroll
+      for (int x = 0; x < T::FM + 2 * T::FN; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, T::FM * T::FN - T::FM - 2 * T::FN, 0);
+      __builtin_amdgcn_sched_barrier(0);   // nothing below moves above this step's MFMAs
+    }
+    // Last k step: meet the other waves once tile kt + 1 has landed, read its first
+    // fragments, and issue the direct loads of tile kt + STAGES - 1 between MFMAs.
+    // After the last tile the wait, barrier and reads are harmless: the reads hit
+    // a stage that is no longer used and their values are dropped.
+    HFrags<T>& cur = ((T::KSTEPS - 1) % 2 == 0) ? fa : fb;
+    HFrags<T>& nxt = ((T::KSTEPS - 1) % 2 == 0) ? fb : fa;
+    {
+      const int left = ktiles - 2 - kt;    // tiles after kt + 1 that may stay in flight
+      wait_tiles_in_flight<T>(left < 0 ? 0 : (left < T::STAGES - 3 ? left : T::STAGES - 3));
     }
     lds_barrier();
-    if (kt + T::STAGES - 1 < ktiles)
-      hdma_issue<T>(p, m0, n0, (kt + T::STAGES - 1) * T::BK,
-                    lds + ((kt + T::STAGES - 1) % T::STAGES) * T::STAGE_BYTES, wave, lane);
-
-    const uint8_t* As = lds + (kt % T::STAGES) * T::STAGE_BYTES;
-    const uint8_t* Bs = As + T::A_BYTES;
+    hload_frags<T>(nxt, lds + ((kt + 1) % T::STAGES) * T::STAGE_BYTES, 0, wm, wn, lane);
+    const bool issue = kt + T::STAGES - 1 < ktiles;
+    const int k_issue = (kt + T::STAGES - 1) * T::BK;
+    const uint32_t st_issue = lds_base + ((kt + T::STAGES - 1) % T::STAGES) * T::STAGE_BYTES;
+    constexpr int kFirstDma = T::FM * T::FN - T::LOADS_PER_TILE;   // MFMA index of the first load
+    static_assert(kFirstDma + 1 >= (T::FM + 2 * T::FN + 1) / 2, "reads need MFMAs to hide under");
 #pragma unroll
-    for (int s = 0; s < T::KSTEPS; ++s) {
-      f16x8 af[T::FM], bf[T::FN];
+    for (int x = 0; x < T::FM * T::FN; ++x) {
+      hmfma<T>(acc, cur, x);
+      if (x == kFirstDma) {
+        // Before the first direct load: two fragment reads after each MFMA.
 #pragma unroll
-      for (int i = 0; i < T::FM; ++i)
-        af[i] = *reinterpret_cast<const f16x8*>(As + ((wm * T::FM + i) * T::KSTEPS + s) * 1024 +
-                                                16 * lane);
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
-        const int jb = wn * T::FN + j;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(Bs + ((s * 2 + 0) * (T::BN / 32) + jb) * 512 + 8 * lane));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(Bs + ((s * 2 + 1) * (T::BN / 32) + jb) * 512 + 8 * lane));
-        const s16x4 both[2] = {lo, hi};
-        bf[j] = __builtin_bit_cast(f16x8, both);
+        for (int y = 0; y < (T::FM + 2 * T::FN) / 2; ++y) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kFirstDma + 1 - (T::FM + 2 * T::FN) / 2, 1);
       }
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j)
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[j][i], 0, 0, 0);
+      const int v = x - kFirstDma;
+      if (v >= 0 && issue) {
+        uint32_t off;
+        const uint16_t* src = hdma_source<T>(p, m0, n0, k_issue, v, wave, lane, off);
+        dma16(src, st_issue + off);
+      }
     }
   }
 
@@ -510,12 +607,20 @@ static hipError_t launch_hdma(const HgemmCall& c, int group_m, hipStream_t s) {
   return hipGetLastError();
 }
 
+int hgemm_pick_tile(int M, int N, int K, int cus, bool dma_ok) {
+  // Whole 256x256 tiles take the direct-to-LDS kernel; other shapes the
+  // register-staged kernel with the largest tile that still fills the device.
+  const long t_large = (long)((M + 255) / 256) * ((N + 255) / 256);
+  const long t_med = (long)((M + 127) / 128) * ((N + 127) / 128);
+  if (M % 256 == 0 && N % 256 == 0 && K % 32 == 0 && dma_ok) return 3;
+  if (t_large >= cus) return 0;
+  if (t_med >= cus / 2) return 1;
+  return 2;
+}
+
 hipError_t launch_hgemm(const HgemmCall& c, int cus, int force_tile, hipStream_t s) {
   int tile = force_tile;
-  if (tile < 0) {
-    tile = sgemm_pick_tile(c.M, c.N, cus);
-    if (tile == 0) tile = 3;    // whole 256x256 tiles: the direct-to-LDS kernel
-  }
+  if (tile < 0) tile = hgemm_pick_tile(c.M, c.N, c.K, cus, dma_fits<HDmaLarge>(c));
   // The direct-to-LDS kernel needs whole tiles; otherwise fall back to the
   // register-staged kernel of the same tile size, which handles every shape.
   if (tile == 3 && !dma_fits<HDmaLarge>(c)) tile = 0;

@@ -283,12 +283,14 @@ static bool fits_fast_path(const SgemmCall& c) {
 }
 
 int sgemm_pick_tile(int M, int N, int cus) {
-  // Prefer the largest tile that still gives every CU at least one tile; the
-  // large tile runs one workgroup per CU, the others two or more.
-  const long t_large = (long)((M + 255) / 256) * ((N + 255) / 256);
+  // Measured on MI355X: 128x256 tiles at two workgroups per CU are fastest once
+  // they give every CU two tiles (4096^3: 133 vs 130 TFLOP/s for 256x256);
+  // below that, small 64x64 tiles beat 128x128 because they spread the work
+  // over more CUs (2048^3: 106 vs 104; 1000x3000x777: 51 vs 42).
+  const long t_tall = (long)((M + 127) / 128) * ((N + 255) / 256);
   const long t_med = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if (t_large >= cus) return 0;
-  if (t_med >= cus / 2) return 1;
+  if (t_tall >= 2L * cus) return 4;
+  if (t_med >= 2L * cus) return 1;
   return 2;
 }
 

@@ -106,10 +106,18 @@ def test_destroy_without_create(so):
 
 def test_tile_choice(so):
     # largest tile when it still fills the device, smaller tiles for small outputs
-    assert lib.gemm_debug_pick_tile(0, 4096, 4096, 256) == 0
-    assert lib.gemm_debug_pick_tile(0, 8192, 8192, 256) == 0
+    assert lib.gemm_debug_pick_tile(0, 4096, 4096, 256) == 4
+    assert lib.gemm_debug_pick_tile(0, 8192, 8192, 256) == 4
     assert lib.gemm_debug_pick_tile(0, 256, 256, 256) == 2
-    assert lib.gemm_debug_pick_tile(0, 1000, 3000, 256) in (1, 2)
+    assert lib.gemm_debug_pick_tile(0, 1000, 3000, 256) == 2
+    assert lib.gemm_debug_pick_tile(0, 2048, 2048, 256) == 2
+    assert lib.gemm_debug_pick_tile(0, 4096, 4096, 64) == 4
+    # the half product: whole 256-tiles take the direct-to-LDS kernel (3)
+    assert lib.gemm_debug_pick_tile(1, 4096, 14336, 256) == 3
+    assert lib.gemm_debug_pick_tile(1, 4096, 4000, 256) == 0
+    assert lib.gemm_debug_pick_tile(1, 2048, 2000, 256) == 1
+    assert lib.gemm_debug_pick_tile(1, 300, 500, 256) == 2
+    assert lib.gemm_debug_pick_tile(2, 300, 500, 256) == -1
     assert lib.gemm_debug_force_tile(0, 5) == lib.STATUS_INVALID_VALUE
     assert lib.gemm_debug_force_tile(1, 4) == lib.STATUS_INVALID_VALUE
     assert lib.gemm_debug_force_tile(1, 3) == lib.STATUS_SUCCESS
