@@ -26,7 +26,7 @@ int gemm_debug_force_tile(int op, int tile);
 
 /* The tile configuration the library would choose for an M x N output on a
  * device with `cus` compute units (op 0 = sgemm; op 1 = hgemm_bias_act with
- * 16-byte-aligned operands and K a multiple of 32).  Returns -1 for an unknown
+ * 16-byte-aligned operands and K a multiple of 64).  Returns -1 for an unknown
  * op.  Pure host computation. */
 int gemm_debug_pick_tile(int op, int M, int N, int cus);
 

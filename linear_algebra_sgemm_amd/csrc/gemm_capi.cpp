@@ -153,8 +153,8 @@ int gemm_debug_force_tile(int op, int tile) {
 
 int gemm_debug_pick_tile(int op, int M, int N, int cus) {
   if (op == 0) return lasg::sgemm_pick_tile(M, N, cus);
-  // half product: aligned operands assumed, K a multiple of 32
-  if (op == 1) return lasg::hgemm_pick_tile(M, N, 32, cus, true);
+  // half product: aligned operands assumed, K a multiple of 64
+  if (op == 1) return lasg::hgemm_pick_tile(M, N, 64, cus, true);
   return -1;
 }
 

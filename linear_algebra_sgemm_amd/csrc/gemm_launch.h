@@ -34,10 +34,11 @@ struct HgemmCall {
 // Tile configurations.  SGEMM: 0 = 256x256 (K step 16), 1 = 128x128, 2 = 64x64,
 // 3 = 256x256 with K step 32, 4 = 128x256 at two workgroups per CU.
 // HGEMM: 0 = 256x256, 1 = 128x128, 2 = 64x64 (register-staged, K step 64),
-// 3 = 256x256 direct-to-LDS, 4 stages of K step 32 (whole tiles only; other
-// shapes fall back to 0).
+// 3 = 256x256 direct-to-LDS, 4 stages of K step 32, 4 = 128x256 direct-to-LDS,
+// 3 stages, two workgroups per CU (3 and 4 need whole tiles and K a multiple of
+// 64; other shapes fall back to 0).
 constexpr int kSgemmTileCount = 5;
-constexpr int kHgemmTileCount = 4;
+constexpr int kHgemmTileCount = 5;
 
 // Tile configuration the shape selects on a device with `cus` compute units
 // (for the half product, `dma_ok` says whether operand alignment and leading

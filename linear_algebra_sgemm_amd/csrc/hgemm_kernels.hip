@@ -252,12 +252,13 @@ __global__ void __launch_bounds__(T::THREADS) hgemm_mfma_kernel(HgemmArgs p) {
 //
 // Loads go straight from global memory into LDS with global_load_lds_dwordx4
 // (lane l of one instruction writes its 16 bytes at base + 16 l), so no staging
-// registers are needed and STAGES - 1 K tiles can be in flight at once.  Since
-// each instruction picks the global chunk of every LDS slot, the stages are laid
-// out in the order the MFMA operands are read, which makes every fragment read
-// one contiguous, conflict-free block:
-//  * A, block (m-block ib, k-step s) = 1 KiB: slot l holds A[32 ib + l % 32]
-//    [16 s + 8 (l / 32) .. +7], read by lane l with one ds_read_b128.
+// registers are needed and STAGES - 1 K tiles can be in flight at once.  Each
+// instruction chooses the global chunk of every LDS slot, which sets the layout:
+//  * A is stored row-major (64-byte rows of one K tile) with the four 16-byte
+//    chunks of each row permuted by a_swizzle so that the fragment reads (one
+//    chunk from each of 32 rows) do not collide in the banks.  One load moves 16
+//    whole rows: the memory path serves about one cache line every two clocks
+//    per CU, so loads must use the lines they touch in full.
 //  * B, block (k-step s, half t, n-block jb) = 512 B: 32 chunks of 8 columns of
 //    one row, in the order (h, cg, q, c2) so that lane l reads bytes [8l, 8l+8)
 //    with ds_read_b64_tr_b16.  That instruction transposes inside groups of 16
@@ -272,9 +273,10 @@ __global__ void __launch_bounds__(T::THREADS) hgemm_mfma_kernel(HgemmArgs p) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-template <int BM_, int BN_, int BK_, int STAGES_>
+template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_PER_SIMD_ = 1>
 struct HDmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;   // workgroups sharing one CU
   static constexpr int WAVES_M = 2, WAVES_N = 2, WAVES = 4;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
@@ -288,14 +290,25 @@ struct HDmaTile {
   static constexpr int A_PER_WAVE = A_INSTR / WAVES;
   static constexpr int B_PER_WAVE = B_INSTR / WAVES;
   static constexpr int LOADS_PER_TILE = A_PER_WAVE + B_PER_WAVE;   // per lane, counted by vmcnt
+  static constexpr int A_CHUNKS_PER_ROW = BK / 8;                   // 16-byte chunks per A row
 
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(BK % 16 == 0 && BN % 64 == 0, "k steps of 16; B loads cover 64 columns");
+  static_assert(BK == 32, "the A chunk swizzle is laid out for rows of four 16-byte chunks");
   static_assert(A_INSTR % WAVES == 0 && B_INSTR % WAVES == 0, "loads split evenly over waves");
   static_assert(STAGES >= 2 && STAGES * STAGE_BYTES <= 160 * 1024, "stages must fit in LDS");
   static_assert((STAGES - 2) * LOADS_PER_TILE <= 63, "in-flight loads must fit vmcnt");
-  static_assert(FM * FN * 16 <= 256, "accumulators must fit in 256 registers per lane");
+  static_assert(FM * FN * 16 <= 256 / WAVES_PER_SIMD, "accumulators must leave room for operands");
 };
+
+// Chunk permutation of A row r in LDS.  A fragment read takes one chunk from 32
+// consecutive rows; rows are 64 bytes apart, so without the permutation rows r
+// and r + 4 would hit the same banks.  With it, any 8 (or 16) consecutive rows
+// land on distinct 16-byte bank groups of a 128-byte (or 256-byte) LDS cycle.
+template <class T>
+__device__ __forceinline__ int a_swizzle(int r) {
+  return ((r >> 1) ^ (r >> 3)) & (T::A_CHUNKS_PER_ROW - 1);
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -339,12 +352,15 @@ __device__ __forceinline__ const uint16_t* hdma_source(const HgemmArgs& p, int m
                                                        int v, int wave, int lane,
                                                        uint32_t& stage_offset) {
   if (v < T::A_PER_WAVE) {
-    const int ia = wave * T::A_PER_WAVE + v;      // = ib * KSTEPS + s
-    const int ib = ia / T::KSTEPS, s = ia % T::KSTEPS;
+    // A stage: row-major rows of BK halves with the 16-byte chunks of row r
+    // permuted by a_swizzle(r); one load = 1 KiB = whole rows, so every cache
+    // line it touches is read over its full width of the tile.
+    const int ia = wave * T::A_PER_WAVE + v;
+    const int r = ia * (1024 / (2 * T::BK)) + lane / T::A_CHUNKS_PER_ROW;
+    const int slot = lane % T::A_CHUNKS_PER_ROW;
     stage_offset = ia * 1024;
-    const int row = m0 + 32 * ib + lane % 32;
-    const int col = k0 + 16 * s + 8 * (lane / 32);
-    return p.A + (size_t)row * p.lda + col;
+    const int chunk = slot ^ a_swizzle<T>(r);
+    return p.A + (size_t)(m0 + r) * p.lda + k0 + 8 * chunk;
   }
   const int ibb = wave * T::B_PER_WAVE + (v - T::A_PER_WAVE);   // = (s * 2 + t) * (BN / 64) + jp
   const int jp = ibb % (T::BN / 64);
@@ -383,9 +399,12 @@ __device__ __forceinline__ void hload_frags(HFrags<T>& f, const uint8_t* stage, 
   const uint8_t* As = stage;
   const uint8_t* Bs = stage + T::A_BYTES;
 #pragma unroll
-  for (int i = 0; i < T::FM; ++i)
-    f.a[i] = *reinterpret_cast<const f16x8*>(As + ((wm * T::FM + i) * T::KSTEPS + s) * 1024 +
-                                             16 * lane);
+  for (int i = 0; i < T::FM; ++i) {
+    const int r = (wm * T::FM + i) * 32 + lane % 32;
+    const int chunk = 2 * s + lane / 32;
+    f.a[i] = *reinterpret_cast<const f16x8*>(As + r * (2 * T::BK) +
+                                             16 * (chunk ^ a_swizzle<T>(r)));
+  }
 #pragma unroll
   for (int j = 0; j < T::FN; ++j) {
     const int jb = wn * T::FN + j;
@@ -419,8 +438,73 @@ __device__ __forceinline__ void wait_tiles_in_flight(int ahead) {
   }
 }
 
+// One K tile of the direct-to-LDS kernel: MFMAs on the fragments of tile kt (x0:
+// k step 0, x1: k step 1, read during the previous tile), reads of tile kt + 1's
+// fragments into y0 / y1, the wait for tile kt + 1 and the barrier, and the direct
+// loads of tile kt + STAGES - 1.  After the last tile the wait is for nothing, and
+// the reads hit a stage that is no longer used; their values are dropped.
 template <class T>
-__global__ void __launch_bounds__(T::THREADS) hgemm_dma_kernel(HgemmArgs p) {
+__device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::FN][T::FM], int kt,
+                                          int ktiles, HFrags<T>& x0, HFrags<T>& x1,
+                                          HFrags<T>& y0, HFrags<T>& y1, const uint8_t* lds,
+                                          uint32_t lds_base, int m0, int n0, int wave, int wm,
+                                          int wn, int lane) {
+  static_assert(T::KSTEPS == 2, "two k steps per tile");
+  constexpr int NM = T::FM * T::FN;                  // MFMAs per k step
+  constexpr int NR = T::FM + 2 * T::FN;              // LDS reads per k step
+  constexpr int PRE = 2;                             // MFMAs issued before the barrier
+  constexpr int R0 = (NR + NM - PRE - 1) / (NM - PRE);          // reads per MFMA, step 0
+  constexpr int TAIL = NM - T::LOADS_PER_TILE;                  // MFMAs after the direct loads
+  static_assert(NM > PRE && TAIL >= 1 && T::LOADS_PER_TILE <= NM, "enough MFMAs to hide behind");
+  constexpr int R1 = (NR + TAIL - 1) / TAIL;                    // reads per MFMA, step 1 tail
+  // Two MFMAs first, so the matrix unit has work queued while the waves meet.
+  hmfma<T>(acc, x0, 0);
+  hmfma<T>(acc, x0, 1);
+  {
+    const int left = ktiles - 2 - kt;    // tiles after kt + 1 that may stay in flight
+    wait_tiles_in_flight<T>(left < 0 ? 0 : (left < T::STAGES - 3 ? left : T::STAGES - 3));
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  const uint8_t* next = lds + ((kt + 1) % T::STAGES) * T::STAGE_BYTES;
+  // Step 0: the remaining MFMAs with the reads of the next tile's first k step.
+  hload_frags<T>(y0, next, 0, wm, wn, lane);
+#pragma unroll
+  for (int x = PRE; x < NM; ++x) hmfma<T>(acc, x0, x);
+#pragma unroll
+  for (int x = 0; x < NM - PRE; ++x) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // Step 1: direct loads of tile kt + STAGES - 1 after the first MFMAs, then the
+  // reads of the next tile's second k step after the rest.
+  const bool issue = kt + T::STAGES - 1 < ktiles;
+  const int k_issue = (kt + T::STAGES - 1) * T::BK;
+  const uint32_t st_issue = lds_base + ((kt + T::STAGES - 1) % T::STAGES) * T::STAGE_BYTES;
+#pragma unroll
+  for (int x = 0; x < T::LOADS_PER_TILE; ++x) {
+    hmfma<T>(acc, x1, x);
+    if (issue) {
+      uint32_t off;
+      const uint16_t* src = hdma_source<T>(p, m0, n0, k_issue, x, wave, lane, off);
+      dma16(src, st_issue + off);
+    }
+  }
+  hload_frags<T>(y1, next, 1, wm, wn, lane);
+#pragma unroll
+  for (int x = T::LOADS_PER_TILE; x < NM; ++x) hmfma<T>(acc, x1, x);
+#pragma unroll
+  for (int x = 0; x < TAIL; ++x) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, R1, 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <class T>
+__global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(T::WAVES_PER_SIMD)))
+hgemm_dma_kernel(HgemmArgs p) {
   static_assert(T::KSTEPS % 2 == 0, "fragments ping-pong between two register sets");
   static_assert(T::LOADS_PER_TILE <= T::FM * T::FN, "one direct load per MFMA at most");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[T::STAGES * T::STAGE_BYTES];
@@ -444,79 +528,31 @@ __global__ void __launch_bounds__(T::THREADS) hgemm_dma_kernel(HgemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-  // Pipeline.  Tile kt lives in stage kt % STAGES.  Its direct loads are issued
-  // in the middle of tile kt - STAGES + 1; in the middle of every tile kt the
-  // waves wait for tile kt + 1 to land, meet at one barrier (which also frees
-  // stage (kt - 1) % STAGES), issue the loads of tile kt + STAGES - 1 into that
-  // stage between the MFMAs of kt's last k step, and read the first fragments
-  // of tile kt + 1.  Fragments of the next k step are always read while the
-  // MFMAs of the current one run.
+  // Pipeline.  Tile kt lives in stage kt % STAGES; its direct loads are issued
+  // during tile kt - STAGES + 1.  While the MFMAs of tile kt run, the waves read
+  // every fragment of tile kt + 1 (two register sets per tile, four in all, so a
+  // fragment is read a whole tile, about 1000 cycles, before its MFMA: LDS
+  // latency under this load is several hundred cycles).  Early in tile kt the
+  // waves wait for tile kt + 1 to land and meet at one barrier; past it, every
+  // wave has also finished with stage (kt - 1) % STAGES (its fragments were
+  // consumed in tile kt - 1), which the direct loads of tile kt + STAGES - 1
+  // then refill.  K is a multiple of 2 BK, so the loop body covers two tiles.
   const int ktiles = p.K / T::BK;
-  HFrags<T> fa, fb;
+  HFrags<T> f0, f1, f2, f3;
   if (ktiles > 0) {
 #pragma unroll
     for (int st = 0; st < T::STAGES - 1; ++st)
       if (st < ktiles) hdma_issue_all<T>(p, m0, n0, st * T::BK, lds_base + st * T::STAGE_BYTES,
                                          wave, lane);
     wait_tiles_in_flight<T>(ktiles - 1 < T::STAGES - 2 ? ktiles - 1 : T::STAGES - 2);
-    lds_barrier();
-    hload_frags<T>(fa, lds, 0, wm, wn, lane);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    hload_frags<T>(f0, lds, 0, wm, wn, lane);
+    hload_frags<T>(f1, lds, 1, wm, wn, lane);
   }
-
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const uint8_t* stage = lds + (kt % T::STAGES) * T::STAGE_BYTES;
-    // k steps 0 .. KSTEPS-2: read the next step's fragments under this step's MFMAs.
-#pragma unroll
-    for (int s = 0; s + 1 < T::KSTEPS; ++s) {
-      HFrags<T>& cur = (s % 2 == 0) ? fa : fb;
-      HFrags<T>& nxt = (s % 2 == 0) ? fb : fa;
-      hload_frags<T>(nxt, stage, s + 1, wm, wn, lane);
-#pragma unroll
-      for (int x = 0; x < T::FM * T::FN; ++x) hmfma<T>(acc, cur, x);
-#pragma unroll
-      for (int x = 0; x < T::FM + 2 * T::FN; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, T::FM * T::FN - T::FM - 2 * T::FN, 0);
-      __builtin_amdgcn_sched_barrier(0);   // nothing below moves above this step's MFMAs
-    }
-    // Last k step: meet the other waves once tile kt + 1 has landed, read its first
-    // fragments, and issue the direct loads of tile kt + STAGES - 1 between MFMAs.
-    // After the last tile the wait, barrier and reads are harmless: the reads hit
-    // a stage that is no longer used and their values are dropped.
-    HFrags<T>& cur = ((T::KSTEPS - 1) % 2 == 0) ? fa : fb;
-    HFrags<T>& nxt = ((T::KSTEPS - 1) % 2 == 0) ? fb : fa;
-    {
-      const int left = ktiles - 2 - kt;    // tiles after kt + 1 that may stay in flight
-      wait_tiles_in_flight<T>(left < 0 ? 0 : (left < T::STAGES - 3 ? left : T::STAGES - 3));
-    }
-    lds_barrier();
-    hload_frags<T>(nxt, lds + ((kt + 1) % T::STAGES) * T::STAGE_BYTES, 0, wm, wn, lane);
-    const bool issue = kt + T::STAGES - 1 < ktiles;
-    const int k_issue = (kt + T::STAGES - 1) * T::BK;
-    const uint32_t st_issue = lds_base + ((kt + T::STAGES - 1) % T::STAGES) * T::STAGE_BYTES;
-    constexpr int kFirstDma = T::FM * T::FN - T::LOADS_PER_TILE;   // MFMA index of the first load
-    static_assert(kFirstDma + 1 >= (T::FM + 2 * T::FN + 1) / 2, "reads need MFMAs to hide under");
-#pragma unroll
-    for (int x = 0; x < T::FM * T::FN; ++x) {
-      hmfma<T>(acc, cur, x);
-      if (x == kFirstDma) {
-        // Before the first direct load: two fragment reads after each MFMA.
-#pragma unroll
-        for (int y = 0; y < (T::FM + 2 * T::FN) / 2; ++y) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kFirstDma + 1 - (T::FM + 2 * T::FN) / 2, 1);
-      }
-      const int v = x - kFirstDma;
-      if (v >= 0 && issue) {
-        uint32_t off;
-        const uint16_t* src = hdma_source<T>(p, m0, n0, k_issue, v, wave, lane, off);
-        dma16(src, st_issue + off);
-      }
-    }
+  for (int kt = 0; kt < ktiles; kt += 2) {
+    hdma_tile<T>(p, acc, kt, ktiles, f0, f1, f2, f3, lds, lds_base, m0, n0, wave, wm, wn, lane);
+    hdma_tile<T>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, m0, n0, wave, wm, wn, lane);
   }
 
   // Epilogue.  Lane l holds, for n-block j, m-block i and q = 0..3, the four
@@ -559,7 +595,8 @@ __global__ void __launch_bounds__(T::THREADS) hgemm_dma_kernel(HgemmArgs p) {
 using HTileLarge = HgemmTile<256, 256, 64, 2, 2>;
 using HTileMedium = HgemmTile<128, 128, 64, 2, 2>;
 using HTileSmall = HgemmTile<64, 64, 64, 2, 2>;
-using HDmaLarge = HDmaTile<256, 256, 32, 4>;     // 4 stages x 32 KiB
+using HDmaLarge = HDmaTile<256, 256, 32, 4>;     // 4 stages x 32 KiB, one workgroup per CU
+using HDmaTall = HDmaTile<128, 256, 32, 3, 2>;   // 3 stages x 24 KiB, two workgroups per CU
 
 template <class T>
 static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s) {
@@ -586,7 +623,7 @@ static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s) {
 
 template <class T>
 static bool dma_fits(const HgemmCall& c) {
-  return c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % T::BK == 0 && c.lda % 8 == 0 &&
+  return c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % (2 * T::BK) == 0 && c.lda % 8 == 0 &&
          c.ldb % 8 == 0 && (reinterpret_cast<uintptr_t>(c.A) & 15u) == 0 &&
          (reinterpret_cast<uintptr_t>(c.B) & 15u) == 0;
 }
@@ -612,7 +649,7 @@ int hgemm_pick_tile(int M, int N, int K, int cus, bool dma_ok) {
   // register-staged kernel with the largest tile that still fills the device.
   const long t_large = (long)((M + 255) / 256) * ((N + 255) / 256);
   const long t_med = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if (M % 256 == 0 && N % 256 == 0 && K % 32 == 0 && dma_ok) return 3;
+  if (M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && dma_ok) return 3;
   if (t_large >= cus) return 0;
   if (t_med >= cus / 2) return 1;
   return 2;
@@ -629,6 +666,9 @@ hipError_t launch_hgemm(const HgemmCall& c, int cus, int force_tile, hipStream_t
     case 1: return launch_htile<HTileMedium>(c, 8, s);
     case 2: return launch_htile<HTileSmall>(c, 8, s);
     case 3: return launch_hdma<HDmaLarge>(c, 4, s);
+    case 4:
+      if (!dma_fits<HDmaTall>(c)) return launch_htile<HTileLarge>(c, 4, s);
+      return launch_hdma<HDmaTall>(c, 8, s);
     default: return hipErrorInvalidValue;
   }
 }

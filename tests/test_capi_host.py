@@ -119,7 +119,7 @@ def test_tile_choice(so):
     assert lib.gemm_debug_pick_tile(1, 300, 500, 256) == 2
     assert lib.gemm_debug_pick_tile(2, 300, 500, 256) == -1
     assert lib.gemm_debug_force_tile(0, 5) == lib.STATUS_INVALID_VALUE
-    assert lib.gemm_debug_force_tile(1, 4) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(1, 5) == lib.STATUS_INVALID_VALUE
     assert lib.gemm_debug_force_tile(1, 3) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(1, -1) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(0, 4) == lib.STATUS_SUCCESS
