@@ -31,6 +31,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "sgemm": os.path.join(ROOT, "linear_algebra_sgemm_amd", "csrc", "sgemm_kernels.hip"),
     "hgemm_bias_gelu": os.path.join(ROOT, "linear_algebra_sgemm_amd", "csrc", "hgemm_kernels.hip"),
+    "bgemm_bias_gelu": os.path.join(ROOT, "linear_algebra_sgemm_amd", "csrc", "hgemm_kernels.hip"),
 }
 
 
@@ -85,7 +86,8 @@ def cpu_baseline(w, A, B, C, target_seconds: float):
             a = A[:rows].contiguous().view(torch.int16).numpy().view("uint16")
             b = B.contiguous().view(torch.int16).numpy().view("uint16")
             oracle.hgemm_bias_act(rows, N, K, w.alpha, a, K, b, N, C.numpy(),
-                                  oracle.ACT_GELU_TANH, with_den=False)
+                                  oracle.ACT_GELU_TANH, with_den=False,
+                                  fmt="bf16" if w.op == "bgemm_bias_gelu" else "f16")
         return time.perf_counter() - t0
 
     probe = min(M, 16)
@@ -141,16 +143,17 @@ def main():
         dtype, flops_dtype = "f32", "f32"
         nbytes = cost.sgemm_bytes(M, N, K, w.beta)
     else:
+        bf16 = w.op == "bgemm_bias_gelu"
         dbias = C.to(dev)
-        dC = torch.empty((M, N), dtype=torch.float16, device=dev)
+        dC = torch.empty((M, N), dtype=torch.bfloat16 if bf16 else torch.float16, device=dev)
+        fn = lib.bgemm_bias_act if bf16 else lib.hgemm_bias_act
 
         def call():
-            lib.hgemm_bias_act(M, N, K, w.alpha, dA, K, dB, N, dbias, lib.ACT_GELU_TANH, dC, N,
-                               stream=stream)
+            fn(M, N, K, w.alpha, dA, K, dB, N, dbias, lib.ACT_GELU_TANH, dC, N, stream=stream)
 
         def reset():
             pass
-        dtype, flops_dtype = "f16", "f16"
+        dtype = flops_dtype = "bf16" if bf16 else "f16"
         nbytes = cost.hgemm_bias_act_bytes(M, N, K)
     flops = cost.gemm_flops(M, N, K)
 
@@ -180,7 +183,7 @@ def main():
         tile = lib.gemm_debug_pick_tile(0, M, N, torch.cuda.get_device_properties(0).multi_processor_count)
         kernel_name = "sgemm_mfma_kernel, tile config %d" % tile
     else:
-        kernel_name = "hgemm_dma_kernel (256x256, direct-to-LDS)"
+        kernel_name = "hgemm_dma_kernel (256x256, direct-to-LDS, %s)" % dtype
     line = {
         "metric": METRIC,
         "value": round(tflops, 3),

@@ -89,6 +89,17 @@ int hgemm_bias_act(int M, int N, int K, float alpha,
                    const float* bias, int act,
                    uint16_t* C, int ldc, hipStream_t stream);
 
+/*
+ * The same product with bfloat16 inputs and output (the upper 16 bits of an
+ * IEEE binary32, passed as uint16_t bit patterns): C = act(alpha * A x B +
+ * bias), FP32 accumulation, C rounded to nearest even.  Arguments, layout,
+ * conventions and errors are those of hgemm_bias_act.
+ */
+int bgemm_bias_act(int M, int N, int K, float alpha,
+                   const uint16_t* A, int lda, const uint16_t* B, int ldb,
+                   const float* bias, int act,
+                   uint16_t* C, int ldc, hipStream_t stream);
+
 /* Static text for a status code; for GEMM_STATUS_HIP_ERROR it also names the
  * last HIP error seen by the library on this host thread. */
 const char* gemm_status_string(int status);

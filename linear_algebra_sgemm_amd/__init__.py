@@ -14,7 +14,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["GemmError", "gemm_create", "gemm_destroy", "sgemm", "hgemm_bias_act",
+__all__ = ["GemmError", "gemm_create", "gemm_destroy", "sgemm", "hgemm_bias_act", "bgemm_bias_act",
            "gemm_status_string", "gemm_debug_force_tile", "gemm_debug_pick_tile", "library_path",
            "load_library", "EXPORTED_SYMBOLS", "ACT_NONE", "ACT_GELU_TANH"]
 
@@ -32,7 +32,7 @@ ACT_NONE = 0
 ACT_GELU_TANH = 1
 
 # Every symbol declared in include/gemm.h and include/gemm_debug.h.
-EXPORTED_SYMBOLS = ("gemm_create", "gemm_destroy", "sgemm", "hgemm_bias_act",
+EXPORTED_SYMBOLS = ("gemm_create", "gemm_destroy", "sgemm", "hgemm_bias_act", "bgemm_bias_act",
                     "gemm_status_string", "gemm_debug_force_tile", "gemm_debug_pick_tile")
 
 _lib = None
@@ -66,6 +66,8 @@ def load_library():
     lib.sgemm.restype = I
     lib.hgemm_bias_act.argtypes = [I, I, I, F, P, I, P, I, P, I, P, I, P]
     lib.hgemm_bias_act.restype = I
+    lib.bgemm_bias_act.argtypes = [I, I, I, F, P, I, P, I, P, I, P, I, P]
+    lib.bgemm_bias_act.restype = I
     lib.gemm_status_string.argtypes = [I]
     lib.gemm_status_string.restype = ctypes.c_char_p
     lib.gemm_debug_force_tile.argtypes = [I, I]
@@ -125,6 +127,15 @@ def hgemm_bias_act(M, N, K, alpha, A, lda, B, ldb, bias, act, C, ldc, stream=Non
                                        _ptr(B), int(ldb), _ptr(bias), int(act), _ptr(C), int(ldc),
                                        _stream(stream))
     return _check(st, "hgemm_bias_act", raise_on_error)
+
+
+def bgemm_bias_act(M, N, K, alpha, A, lda, B, ldb, bias, act, C, ldc, stream=None, *,
+                   raise_on_error=True):
+    """C = act(alpha * A x B + bias), bfloat16 A/B/C, fp32 bias and accumulation; see include/gemm.h."""
+    st = load_library().bgemm_bias_act(int(M), int(N), int(K), float(alpha), _ptr(A), int(lda),
+                                       _ptr(B), int(ldb), _ptr(bias), int(act), _ptr(C), int(ldc),
+                                       _stream(stream))
+    return _check(st, "bgemm_bias_act", raise_on_error)
 
 
 def gemm_status_string(status: int) -> str:

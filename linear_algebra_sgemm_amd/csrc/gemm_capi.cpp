@@ -106,9 +106,11 @@ int sgemm(int M, int N, int K, float alpha, const float* A, int lda, const float
   return e == hipSuccess ? GEMM_STATUS_SUCCESS : hip_failure(e);
 }
 
-int hgemm_bias_act(int M, int N, int K, float alpha, const uint16_t* A, int lda,
-                   const uint16_t* B, int ldb, const float* bias, int act, uint16_t* C, int ldc,
-                   hipStream_t stream) {
+namespace {
+
+int half_product(bool bf16, int M, int N, int K, float alpha, const uint16_t* A, int lda,
+                 const uint16_t* B, int ldb, const float* bias, int act, uint16_t* C, int ldc,
+                 hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0) return GEMM_STATUS_INVALID_VALUE;
   if (!ld_ok(lda, K) || !ld_ok(ldb, N) || !ld_ok(ldc, N)) return GEMM_STATUS_INVALID_VALUE;
   if (act != GEMM_ACT_NONE && act != GEMM_ACT_GELU_TANH) return GEMM_STATUS_INVALID_VALUE;
@@ -121,8 +123,24 @@ int hgemm_bias_act(int M, int N, int K, float alpha, const uint16_t* A, int lda,
   // alpha == 0 or K == 0: the product is zero and A, B stay unread; the kernel
   // skips its K loop and still applies bias and activation.
   lasg::HgemmCall c{M, N, reads_ab ? K : 0, alpha, A, lda, B, ldb, bias, act, C, ldc};
-  hipError_t e = lasg::launch_hgemm(c, g_cus.load(), g_force_hgemm_tile.load(), stream);
+  const int force = g_force_hgemm_tile.load();
+  hipError_t e = bf16 ? lasg::launch_bgemm(c, g_cus.load(), force, stream)
+                      : lasg::launch_hgemm(c, g_cus.load(), force, stream);
   return e == hipSuccess ? GEMM_STATUS_SUCCESS : hip_failure(e);
+}
+
+}  // namespace
+
+int hgemm_bias_act(int M, int N, int K, float alpha, const uint16_t* A, int lda,
+                   const uint16_t* B, int ldb, const float* bias, int act, uint16_t* C, int ldc,
+                   hipStream_t stream) {
+  return half_product(false, M, N, K, alpha, A, lda, B, ldb, bias, act, C, ldc, stream);
+}
+
+int bgemm_bias_act(int M, int N, int K, float alpha, const uint16_t* A, int lda,
+                   const uint16_t* B, int ldb, const float* bias, int act, uint16_t* C, int ldc,
+                   hipStream_t stream) {
+  return half_product(true, M, N, K, alpha, A, lda, B, ldb, bias, act, C, ldc, stream);
 }
 
 const char* gemm_status_string(int status) {

@@ -50,6 +50,9 @@ int hgemm_pick_tile(int M, int N, int K, int cus, bool dma_ok);
 hipError_t launch_sgemm(const SgemmCall& c, int cus, int force_tile, hipStream_t s);
 hipError_t launch_sgemm_scale(int M, int N, float beta, float* C, int ldc, hipStream_t s);
 
+// The half-precision product: binary16 (hgemm) or bfloat16 (bgemm) inputs and
+// output, FP32 accumulation; same kernels, tiles and tile choice.
 hipError_t launch_hgemm(const HgemmCall& c, int cus, int force_tile, hipStream_t s);
+hipError_t launch_bgemm(const HgemmCall& c, int cus, int force_tile, hipStream_t s);
 
 }  // namespace lasg

@@ -24,8 +24,33 @@
 
 namespace lasg {
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+// The 16-bit input formats: IEEE binary16 and bfloat16 share every load, LDS
+// layout and transposing read; they differ in the MFMA and the output rounding.
+struct EltF16 {
+  typedef _Float16 vec8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  // fp32 -> binary16, round to nearest even (v_cvt_f16_f32)
+  static __device__ __forceinline__ uint16_t bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+};
+
+struct EltBF16 {
+  typedef __bf16 vec8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // fp32 -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32)
+  static __device__ __forceinline__ uint16_t bits(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+};
+
+template <class E_, int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
 struct HgemmTile {
+  using E = E_;
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
@@ -205,18 +230,19 @@ __global__ void __launch_bounds__(T::THREADS) hgemm_mfma_kernel(HgemmArgs p) {
 
 #pragma unroll
     for (int s = 0; s < T::BK / 16; ++s) {
-      f16x8 af[T::FM], bf[T::FN];
+      typedef typename T::E::vec8 vec8;
+      vec8 af[T::FM], bf[T::FN];
 #pragma unroll
       for (int i = 0; i < T::FM; ++i)
-        af[i] = *reinterpret_cast<const f16x8*>(As + a_off + i * 32 * T::STRIDE + 16 * s);
+        af[i] = *reinterpret_cast<const vec8*>(As + a_off + i * 32 * T::STRIDE + 16 * s);
 #pragma unroll
       for (int j = 0; j < T::FN; ++j)
-        bf[j] = *reinterpret_cast<const f16x8*>(Bt + b_off + j * 32 * T::STRIDE + 16 * s);
+        bf[j] = *reinterpret_cast<const vec8*>(Bt + b_off + j * 32 * T::STRIDE + 16 * s);
 #pragma unroll
       for (int i = 0; i < T::FM; ++i)
 #pragma unroll
         for (int j = 0; j < T::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = T::E::mfma(af[i], bf[j], acc[i][j]);
     }
 
     if (more) st.store(odd ? As0 : As1, odd ? Bt0 : Bt1, tid);
@@ -239,8 +265,7 @@ __global__ void __launch_bounds__(T::THREADS) hgemm_mfma_kernel(HgemmArgs p) {
         if (EDGE && (row >= p.M || !col_ok)) continue;
         float x = __builtin_fmaf(alpha, acc[i][j][r], bj);
         if (gelu) x = gelu_tanh(x);
-        const _Float16 h = (_Float16)x;
-        p.C[(size_t)row * p.ldc + col] = __builtin_bit_cast(uint16_t, h);
+        p.C[(size_t)row * p.ldc + col] = T::E::bits(x);
       }
     }
   }
@@ -273,8 +298,9 @@ __global__ void __launch_bounds__(T::THREADS) hgemm_mfma_kernel(HgemmArgs p) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_PER_SIMD_ = 1>
+template <class E_, int BM_, int BN_, int BK_, int STAGES_, int WAVES_PER_SIMD_ = 1>
 struct HDmaTile {
+  using E = E_;
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;   // workgroups sharing one CU
   static constexpr int WAVES_M = 2, WAVES_N = 2, WAVES = 4;
@@ -389,8 +415,8 @@ __device__ __forceinline__ void hdma_issue_all(const HgemmArgs& p, int m0, int n
 // MFMA operand fragments of one k step of one wave.
 template <class T>
 struct HFrags {
-  f16x8 a[T::FM];
-  f16x8 b[T::FN];
+  typename T::E::vec8 a[T::FM];
+  typename T::E::vec8 b[T::FN];
 };
 
 template <class T>
@@ -402,7 +428,7 @@ __device__ __forceinline__ void hload_frags(HFrags<T>& f, const uint8_t* stage, 
   for (int i = 0; i < T::FM; ++i) {
     const int r = (wm * T::FM + i) * 32 + lane % 32;
     const int chunk = 2 * s + lane / 32;
-    f.a[i] = *reinterpret_cast<const f16x8*>(As + r * (2 * T::BK) +
+    f.a[i] = *reinterpret_cast<const typename T::E::vec8*>(As + r * (2 * T::BK) +
                                              16 * (chunk ^ a_swizzle<T>(r)));
   }
 #pragma unroll
@@ -413,14 +439,14 @@ __device__ __forceinline__ void hload_frags(HFrags<T>& f, const uint8_t* stage, 
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_s16x4_t*)(Bs + ((s * 2 + 1) * (T::BN / 32) + jb) * 512 + 8 * lane));
     const s16x4 both[2] = {lo, hi};
-    f.b[j] = __builtin_bit_cast(f16x8, both);
+    f.b[j] = __builtin_bit_cast(typename T::E::vec8, both);
   }
 }
 
 template <class T>
 __device__ __forceinline__ void hmfma(f32x16 (&acc)[T::FN][T::FM], const HFrags<T>& f, int idx) {
   const int j = idx / T::FM, i = idx % T::FM;
-  acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[j][i], 0, 0, 0);
+  acc[j][i] = T::E::mfma(f.b[j], f.a[i], acc[j][i]);
 }
 
 // Wait until at most `ahead` tiles of direct loads are still in flight.
@@ -573,30 +599,31 @@ hgemm_dma_kernel(HgemmArgs p) {
 #pragma unroll
       for (int i = 0; i < T::FM; ++i) {
         const int row = m0 + wm * T::WTM + 32 * i + lane % 32;
-        _Float16 h[4];
+        uint16_t h[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float x = __builtin_fmaf(alpha, acc[j][i][4 * q + e], bias4[e]);
           if (gelu) x = gelu_tanh(x);
-          h[e] = (_Float16)x;
+          h[e] = T::E::bits(x);
         }
         uint16_t* dst = p.C + (size_t)row * p.ldc + col;
         if (vec_store) {
           *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, h);
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dst[e] = __builtin_bit_cast(uint16_t, h[e]);
+          for (int e = 0; e < 4; ++e) dst[e] = h[e];
         }
       }
     }
   }
 }
 
-using HTileLarge = HgemmTile<256, 256, 64, 2, 2>;
-using HTileMedium = HgemmTile<128, 128, 64, 2, 2>;
-using HTileSmall = HgemmTile<64, 64, 64, 2, 2>;
-using HDmaLarge = HDmaTile<256, 256, 32, 4>;     // 4 stages x 32 KiB, one workgroup per CU
-using HDmaTall = HDmaTile<128, 256, 32, 3, 2>;   // 3 stages x 24 KiB, two workgroups per CU
+template <class E> using HTileLarge = HgemmTile<E, 256, 256, 64, 2, 2>;
+template <class E> using HTileMedium = HgemmTile<E, 128, 128, 64, 2, 2>;
+template <class E> using HTileSmall = HgemmTile<E, 64, 64, 64, 2, 2>;
+// direct-to-LDS: 4 stages x 32 KiB, one workgroup per CU / 3 stages x 24 KiB, two per CU
+template <class E> using HDmaLarge = HDmaTile<E, 256, 256, 32, 4>;
+template <class E> using HDmaTall = HDmaTile<E, 128, 256, 32, 3, 2>;
 
 template <class T>
 static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s) {
@@ -655,22 +682,31 @@ int hgemm_pick_tile(int M, int N, int K, int cus, bool dma_ok) {
   return 2;
 }
 
-hipError_t launch_hgemm(const HgemmCall& c, int cus, int force_tile, hipStream_t s) {
+template <class E>
+static hipError_t launch_half(const HgemmCall& c, int cus, int force_tile, hipStream_t s) {
   int tile = force_tile;
-  if (tile < 0) tile = hgemm_pick_tile(c.M, c.N, c.K, cus, dma_fits<HDmaLarge>(c));
-  // The direct-to-LDS kernel needs whole tiles; otherwise fall back to the
+  if (tile < 0) tile = hgemm_pick_tile(c.M, c.N, c.K, cus, dma_fits<HDmaLarge<E>>(c));
+  // The direct-to-LDS kernels need whole tiles; otherwise fall back to the
   // register-staged kernel of the same tile size, which handles every shape.
-  if (tile == 3 && !dma_fits<HDmaLarge>(c)) tile = 0;
+  if (tile == 3 && !dma_fits<HDmaLarge<E>>(c)) tile = 0;
   switch (tile) {
-    case 0: return launch_htile<HTileLarge>(c, 4, s);
-    case 1: return launch_htile<HTileMedium>(c, 8, s);
-    case 2: return launch_htile<HTileSmall>(c, 8, s);
-    case 3: return launch_hdma<HDmaLarge>(c, 4, s);
+    case 0: return launch_htile<HTileLarge<E>>(c, 4, s);
+    case 1: return launch_htile<HTileMedium<E>>(c, 8, s);
+    case 2: return launch_htile<HTileSmall<E>>(c, 8, s);
+    case 3: return launch_hdma<HDmaLarge<E>>(c, 4, s);
     case 4:
-      if (!dma_fits<HDmaTall>(c)) return launch_htile<HTileLarge>(c, 4, s);
-      return launch_hdma<HDmaTall>(c, 8, s);
+      if (!dma_fits<HDmaTall<E>>(c)) return launch_htile<HTileLarge<E>>(c, 4, s);
+      return launch_hdma<HDmaTall<E>>(c, 8, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_hgemm(const HgemmCall& c, int cus, int force_tile, hipStream_t s) {
+  return launch_half<EltF16>(c, cus, force_tile, s);
+}
+
+hipError_t launch_bgemm(const HgemmCall& c, int cus, int force_tile, hipStream_t s) {
+  return launch_half<EltBF16>(c, cus, force_tile, s);
 }
 
 }  // namespace lasg

@@ -12,7 +12,8 @@ product with a fused bias + GELU epilogue on the DeepGEMM page):
 * draws in the order A, B, C (or A, B, bias for the half-precision product);
 * U[-1, 1] is ``rand * 2 - 1`` in float32 (covers [-1, 1));
 * N(0, 1) is ``randn`` in float32;
-* the fp16 operands are ``(randn * 0.02)`` rounded to float16 (round to nearest even);
+* the 16-bit operands are ``(randn * 0.02)`` rounded to float16 or bfloat16 (round to
+  nearest even);
 * matrices are packed row-major (leading dimension = column count) unless a
   caller asks for padding, which is filled with NaN so that any read of it
   shows up in the result.
@@ -28,14 +29,14 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    op: str            # "sgemm" or "hgemm_bias_gelu"
+    op: str            # "sgemm", "hgemm_bias_gelu" or "bgemm_bias_gelu"
     M: int
     N: int
     K: int
     seed: int
     alpha: float
     beta: float = 0.0
-    dist_ab: str = "uniform"     # "uniform" U[-1,1], "normal" N(0,1), "normal002_f16"
+    dist_ab: str = "uniform"     # "uniform" U[-1,1], "normal" N(0,1), "normal002_f16"/"_bf16"
     dist_c: str = "uniform"      # distribution of C (sgemm) -- bias is always N(0,1)
     note: str = field(default="", compare=False)
 
@@ -54,6 +55,9 @@ WORKLOADS = {
                           dist_ab="normal002_f16"),
     "sgemm_8192": Workload("sgemm_8192", "sgemm", 8192, 8192, 8192, seed=4, alpha=1.0, beta=1.0,
                            dist_ab="normal", dist_c="uniform"),
+    # the FFN product again with bfloat16 operands and output
+    "bgemm_ffn": Workload("bgemm_ffn", "bgemm_bias_gelu", 4096, 14336, 4096, seed=5, alpha=1.0,
+                          dist_ab="normal002_bf16"),
 }
 
 
@@ -64,6 +68,8 @@ def _draw(gen: torch.Generator, rows: int, cols: int, dist: str) -> torch.Tensor
         return torch.randn((rows, cols), generator=gen, dtype=torch.float32)
     if dist == "normal002_f16":
         return (torch.randn((rows, cols), generator=gen, dtype=torch.float32) * 0.02).to(torch.float16)
+    if dist == "normal002_bf16":
+        return (torch.randn((rows, cols), generator=gen, dtype=torch.float32) * 0.02).to(torch.bfloat16)
     raise ValueError("unknown distribution %r" % dist)
 
 
@@ -92,12 +98,14 @@ def sgemm_inputs(M: int, N: int, K: int, seed: int, dist_ab: str = "uniform",
 
 
 def hgemm_inputs(M: int, N: int, K: int, seed: int, lda: int | None = None,
-                 ldb: int | None = None):
-    """Host tensors A (M x lda fp16), B (K x ldb fp16), bias (N fp32 ~ N(0,1)), drawn A, B, bias."""
+                 ldb: int | None = None, fmt: str = "f16"):
+    """Host tensors A (M x lda), B (K x ldb) in fp16 (fmt "f16") or bfloat16 ("bf16") and
+    bias (N fp32 ~ N(0,1)), drawn in the order A, B, bias."""
     gen = torch.Generator(device="cpu")
     gen.manual_seed(seed)
-    A = _draw(gen, M, K, "normal002_f16")
-    B = _draw(gen, K, N, "normal002_f16")
+    dist = {"f16": "normal002_f16", "bf16": "normal002_bf16"}[fmt]
+    A = _draw(gen, M, K, dist)
+    B = _draw(gen, K, N, dist)
     bias = torch.randn((N,), generator=gen, dtype=torch.float32)
     return _pad(A, lda or max(K, 1)), _pad(B, ldb or max(N, 1)), bias
 
@@ -105,7 +113,7 @@ def hgemm_inputs(M: int, N: int, K: int, seed: int, lda: int | None = None,
 def workload_inputs(w: Workload):
     if w.op == "sgemm":
         return sgemm_inputs(w.M, w.N, w.K, w.seed, w.dist_ab, w.dist_c)
-    return hgemm_inputs(w.M, w.N, w.K, w.seed)
+    return hgemm_inputs(w.M, w.N, w.K, w.seed, fmt="bf16" if w.op == "bgemm_bias_gelu" else "f16")
 
 
 def sha256(*tensors: torch.Tensor) -> str:

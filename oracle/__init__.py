@@ -8,7 +8,7 @@ The arithmetic lives in ``oracle.c`` (plain C, IEEE double, no FMA contraction,
 ascending-k sums, OpenMP over rows); this module builds it with gcc and
 marshals numpy arrays through ctypes.  The definition it follows is the problem
 statement of "SGEMM优化，从naive到warptiling" (section 问题与估算) and, for the
-half-precision variant, the fused bias/activation epilogue of the DeepGEMM page
+half-precision variants (binary16 and bfloat16 inputs), the fused bias/activation epilogue of the DeepGEMM page
 (sections 1.1 and 3.2); the header of ``oracle.c`` states each reading.
 
 Every function here is pinned by tests that do not reuse its own formula:
@@ -58,8 +58,14 @@ def _bind(lib):
     lib.oracle_hgemm_bias_act.restype = None
     lib.oracle_hgemm_entries.argtypes = [i32, f64, P, i32, P, i32, P, i32, P, P, i64, P, P, i32]
     lib.oracle_hgemm_entries.restype = None
+    lib.oracle_bgemm_bias_act.argtypes = [i32, i32, i32, f64, P, i32, P, i32, P, i32, P, P, i32]
+    lib.oracle_bgemm_bias_act.restype = None
+    lib.oracle_bgemm_entries.argtypes = [i32, f64, P, i32, P, i32, P, i32, P, P, i64, P, P, i32]
+    lib.oracle_bgemm_entries.restype = None
     lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_half_to_double.restype = f64
+    lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_double.restype = f64
     lib.oracle_gelu_tanh.argtypes = [f64]
     lib.oracle_gelu_tanh.restype = f64
     lib.oracle_max_threads.argtypes = []
@@ -79,11 +85,12 @@ def _as_f32(a):
 
 
 def _as_f16_bits(a):
+    """numpy float16 or a uint16 / int16 array of 16-bit patterns (binary16 or bfloat16)."""
     a = np.asarray(a)
-    if a.dtype == np.float16:
+    if a.dtype == np.float16 or a.dtype == np.int16:
         a = a.view(np.uint16)
     if a.dtype != np.uint16:
-        raise TypeError("expected float16 (or uint16 bit pattern) array, got %s" % a.dtype)
+        raise TypeError("expected float16 (or 16-bit pattern) array, got %s" % a.dtype)
     return np.ascontiguousarray(a).ravel()
 
 
@@ -156,8 +163,9 @@ class Oracle:
         return ref, den
 
     def hgemm_bias_act(self, M, N, K, alpha, A, lda, B, ldb, bias, act, *, with_den=True,
-                       threads=0):
-        """(ref, den) of act(alpha*A*B + bias) for fp16 A, B and an fp32 bias of length N."""
+                       threads=0, fmt="f16"):
+        """(ref, den) of act(alpha*A*B + bias) for 16-bit A, B (fmt "f16" = binary16,
+        "bf16" = bfloat16 bit patterns) and an fp32 bias of length N."""
         A = _as_f16_bits(A)
         B = _as_f16_bits(B)
         bias = None if bias is None else _as_f32(bias)
@@ -168,11 +176,13 @@ class Oracle:
             raise ValueError("bias shorter than N")
         ref = np.empty((M, N), np.float64)
         den = np.empty((M, N), np.float64) if with_den else None
-        self.lib.oracle_hgemm_bias_act(M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
-                                       _ptr(bias), int(act), _ptr(ref), _ptr(den), int(threads))
+        fn = {"f16": self.lib.oracle_hgemm_bias_act, "bf16": self.lib.oracle_bgemm_bias_act}[fmt]
+        fn(M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb, _ptr(bias), int(act), _ptr(ref),
+           _ptr(den), int(threads))
         return ref, den
 
-    def hgemm_entries(self, K, alpha, A, lda, B, ldb, bias, act, rows, cols, *, threads=0):
+    def hgemm_entries(self, K, alpha, A, lda, B, ldb, bias, act, rows, cols, *, threads=0,
+                      fmt="f16"):
         """(ref, den) of the entries (rows[t], cols[t]) of act(alpha*A*B + bias)."""
         A = _as_f16_bits(A)
         B = _as_f16_bits(B)
@@ -181,13 +191,16 @@ class Oracle:
         cols = np.ascontiguousarray(cols, dtype=np.int64)
         ref = np.empty(rows.size, np.float64)
         den = np.empty(rows.size, np.float64)
-        self.lib.oracle_hgemm_entries(K, float(alpha), _ptr(A), lda, _ptr(B), ldb, _ptr(bias),
-                                      int(act), _ptr(rows), _ptr(cols), rows.size, _ptr(ref),
-                                      _ptr(den), int(threads))
+        fn = {"f16": self.lib.oracle_hgemm_entries, "bf16": self.lib.oracle_bgemm_entries}[fmt]
+        fn(K, float(alpha), _ptr(A), lda, _ptr(B), ldb, _ptr(bias), int(act), _ptr(rows),
+           _ptr(cols), rows.size, _ptr(ref), _ptr(den), int(threads))
         return ref, den
 
     def half_to_double(self, bits: int) -> float:
         return float(self.lib.oracle_half_to_double(int(bits) & 0xFFFF))
+
+    def bf16_to_double(self, bits: int) -> float:
+        return float(self.lib.oracle_bf16_to_double(int(bits) & 0xFFFF))
 
     def gelu_tanh(self, x: float) -> float:
         return float(self.lib.oracle_gelu_tanh(float(x)))
@@ -201,6 +214,7 @@ sgemm_entries = _default.sgemm_entries
 hgemm_bias_act = _default.hgemm_bias_act
 hgemm_entries = _default.hgemm_entries
 half_to_double = _default.half_to_double
+bf16_to_double = _default.bf16_to_double
 gelu_tanh = _default.gelu_tanh
 
 

@@ -16,7 +16,7 @@
  *  - Lecture 24 "CUDA GEMM 分块（Tiling）与 Tensor Core 思维", its opening
  *    triple-loop definition of the product: every output element is the sum
  *    over k of A[i][k] * B[k][j].
- *  - The half-precision variant with bias and activation fused into the
+ *  - The half-precision variant (binary16 or bfloat16 inputs) with bias and activation fused into the
  *    write-back is the one described on the DeepGEMM page (sections 1.1 and
  *    3.2: bias, scaling and GELU done in registers before one store).  Its
  *    activation is read as the tanh form of GELU (Hendrycks & Gimpel 2016):
@@ -71,6 +71,15 @@ double oracle_half_to_double(uint16_t h) {
     v = ldexp((double)(frac + 1024), expo - 25);
   }
   return sign ? -v : v;
+}
+
+/* bfloat16 -> double: a bfloat16 value is the upper 16 bits of an IEEE binary32,
+ * so it is widened by appending 16 zero bits and converted exactly. */
+double oracle_bf16_to_double(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
 }
 
 /* The tanh form of GELU, evaluated in double with the C library's tanh. */
@@ -174,17 +183,19 @@ void oracle_sgemm_entries(int K, double alpha, const float *A, int lda,
   }
 }
 
+typedef double (*decode16_fn)(uint16_t);
+
 /*
- * Half-precision inputs (IEEE binary16 bit patterns), product summed in double:
+ * 16-bit inputs (binary16 or bfloat16 bit patterns, decoded exactly to double),
+ * product summed in double:
  *   x = alpha * sum_k a_ik b_kj + bias[j]      (bias may be NULL: 0)
  *   ref = act(x), act 0 = identity, act 1 = GELU(tanh)
  *   den = |alpha| sum_k |a||b| + |bias[j]|
- * The fp16 values are exact in double.  alpha == 0 or K == 0 leaves only bias.
+ * alpha == 0 or K == 0 leaves only bias.
  */
-void oracle_hgemm_bias_act(int M, int N, int K, double alpha, const uint16_t *A,
-                           int lda, const uint16_t *B, int ldb,
-                           const float *bias, int act, double *ref, double *den,
-                           int threads) {
+static void half_gemm(decode16_fn dec, int M, int N, int K, double alpha, const uint16_t *A,
+                      int lda, const uint16_t *B, int ldb, const float *bias, int act,
+                      double *ref, double *den, int threads) {
   int nt = oracle_threads(threads);
   int skip_product = (alpha == 0.0) || (K == 0);
 #pragma omp parallel num_threads(nt)
@@ -200,9 +211,9 @@ void oracle_hgemm_bias_act(int M, int N, int K, double alpha, const uint16_t *A,
       }
       if (!skip_product) {
         for (int k = 0; k < K; ++k) {
-          double a = oracle_half_to_double(A[(size_t)i * lda + k]);
+          double a = dec(A[(size_t)i * lda + k]);
           const uint16_t *bsrc = B + (size_t)k * ldb;
-          for (int j = 0; j < N; ++j) brow[j] = oracle_half_to_double(bsrc[j]);
+          for (int j = 0; j < N; ++j) brow[j] = dec(bsrc[j]);
           for (int j = 0; j < N; ++j) acc[j] += a * brow[j];
           if (den) {
             double aa = fabs(a);
@@ -223,11 +234,11 @@ void oracle_hgemm_bias_act(int M, int N, int K, double alpha, const uint16_t *A,
   }
 }
 
-/* Sampled entries of the half-precision product, as oracle_sgemm_entries. */
-void oracle_hgemm_entries(int K, double alpha, const uint16_t *A, int lda,
-                          const uint16_t *B, int ldb, const float *bias, int act,
-                          const int64_t *rows, const int64_t *cols,
-                          int64_t count, double *ref, double *den, int threads) {
+/* Sampled entries of the 16-bit product, one ascending-k dot product each. */
+static void half_entries(decode16_fn dec, int K, double alpha, const uint16_t *A, int lda,
+                         const uint16_t *B, int ldb, const float *bias, int act,
+                         const int64_t *rows, const int64_t *cols, int64_t count, double *ref,
+                         double *den, int threads) {
   int nt = oracle_threads(threads);
   int skip_product = (alpha == 0.0) || (K == 0);
 #pragma omp parallel for num_threads(nt) schedule(static)
@@ -236,8 +247,8 @@ void oracle_hgemm_entries(int K, double alpha, const uint16_t *A, int lda,
     double s = 0.0, m = 0.0;
     if (!skip_product) {
       for (int k = 0; k < K; ++k) {
-        double a = oracle_half_to_double(A[i * lda + k]);
-        double b = oracle_half_to_double(B[(int64_t)k * ldb + j]);
+        double a = dec(A[i * lda + k]);
+        double b = dec(B[(int64_t)k * ldb + j]);
         s += a * b;
         m += fabs(a) * fabs(b);
       }
@@ -247,6 +258,36 @@ void oracle_hgemm_entries(int K, double alpha, const uint16_t *A, int lda,
     ref[t] = act == 1 ? oracle_gelu_tanh(x) : x;
     if (den) den[t] = (skip_product ? 0.0 : fabs(alpha) * m) + fabs(bb);
   }
+}
+
+/* binary16 inputs */
+void oracle_hgemm_bias_act(int M, int N, int K, double alpha, const uint16_t *A, int lda,
+                           const uint16_t *B, int ldb, const float *bias, int act, double *ref,
+                           double *den, int threads) {
+  half_gemm(oracle_half_to_double, M, N, K, alpha, A, lda, B, ldb, bias, act, ref, den, threads);
+}
+
+void oracle_hgemm_entries(int K, double alpha, const uint16_t *A, int lda, const uint16_t *B,
+                          int ldb, const float *bias, int act, const int64_t *rows,
+                          const int64_t *cols, int64_t count, double *ref, double *den,
+                          int threads) {
+  half_entries(oracle_half_to_double, K, alpha, A, lda, B, ldb, bias, act, rows, cols, count, ref,
+               den, threads);
+}
+
+/* bfloat16 inputs */
+void oracle_bgemm_bias_act(int M, int N, int K, double alpha, const uint16_t *A, int lda,
+                           const uint16_t *B, int ldb, const float *bias, int act, double *ref,
+                           double *den, int threads) {
+  half_gemm(oracle_bf16_to_double, M, N, K, alpha, A, lda, B, ldb, bias, act, ref, den, threads);
+}
+
+void oracle_bgemm_entries(int K, double alpha, const uint16_t *A, int lda, const uint16_t *B,
+                          int ldb, const float *bias, int act, const int64_t *rows,
+                          const int64_t *cols, int64_t count, double *ref, double *den,
+                          int threads) {
+  half_entries(oracle_bf16_to_double, K, alpha, A, lda, B, ldb, bias, act, rows, cols, count, ref,
+               den, threads);
 }
 
 int oracle_max_threads(void) { return oracle_threads(0); }

@@ -33,9 +33,11 @@ def run_sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None, sync=Tr
 
 
 def run_hgemm(M, N, K, alpha, A, lda, B, ldb, bias, act, C, ldc, stream=None, sync=True):
+    """The half product; binary16 or bfloat16 by the dtype of A."""
     dA, dB, dC = device_copy(A), device_copy(B), device_copy(C)
     dbias = None if bias is None else device_copy(bias)
-    lib.hgemm_bias_act(M, N, K, alpha, dA, lda, dB, ldb, dbias, act, dC, ldc, stream=stream)
+    fn = lib.bgemm_bias_act if A.dtype == torch.bfloat16 else lib.hgemm_bias_act
+    fn(M, N, K, alpha, dA, lda, dB, ldb, dbias, act, dC, ldc, stream=stream)
     if sync:
         torch.cuda.synchronize()
     return dC
@@ -51,9 +53,10 @@ def sgemm_error(M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, got):
 
 
 def hgemm_error(M, N, K, alpha, A, lda, B, ldb, bias, act, got, ldc):
+    fmt = "bf16" if A.dtype == torch.bfloat16 else "f16"
     ref, den = oracle.hgemm_bias_act(M, N, K, alpha, A.view(torch.int16).numpy().view(np.uint16),
                                      lda, B.view(torch.int16).numpy().view(np.uint16), ldb,
-                                     None if bias is None else bias.numpy(), act)
+                                     None if bias is None else bias.numpy(), act, fmt=fmt)
     g = got.cpu().float().numpy().reshape(-1, ldc)[:M, :N]
     e = oracle.normalized_error(g, ref, den)
     return float(e.max()) if e.size else 0.0, np.unravel_index(int(e.argmax()), e.shape) if e.size else None

@@ -15,10 +15,11 @@ What pins what:
   dimensions: the whole sum, within the double-precision rounding bound, and the
   error scale ``den`` it returns;
 * small-integer operands (exact): the product against Python integer arithmetic;
-* binary16 decoding against numpy over all 65536 bit patterns;
+* binary16 decoding against numpy, bfloat16 decoding against torch, both over all
+  65536 bit patterns;
 * GELU(tanh) against its odd-part identity gelu(x) - gelu(-x) = x, its limits and
   torch's float64 ``gelu(approximate='tanh')``;
-* the half-precision product against torch.matmul in float64 and torch's GELU.
+* the binary16 and bfloat16 products against torch.matmul in float64 and torch's GELU.
 """
 from __future__ import annotations
 
@@ -209,6 +210,16 @@ def pin_half_decoder(o: _oracle.Oracle):
     assert np.array_equal(np.signbit(got[~nan_w]), np.signbit(want[~nan_w])), "signed zeros"
 
 
+def pin_bf16_decoder(o: _oracle.Oracle):
+    bits = np.arange(65536, dtype=np.int64).astype(np.int32)
+    t = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([o.bf16_to_double(int(b)) for b in range(65536)], dtype=np.float64)
+    nan_w = np.isnan(t)
+    assert np.array_equal(nan_w, np.isnan(got)), "bfloat16 NaN patterns"
+    assert np.array_equal(got[~nan_w], t[~nan_w]), "bfloat16 decoding"
+    assert np.array_equal(np.signbit(got[~nan_w]), np.signbit(t[~nan_w])), "bfloat16 signed zeros"
+
+
 def pin_gelu(o: _oracle.Oracle):
     assert o.gelu_tanh(0.0) == 0.0
     xs = np.concatenate([np.linspace(-8, 8, 401), [1e-6, 3.0, 0.5, 12.0, 30.0]])
@@ -253,6 +264,32 @@ def pin_half_product_vs_torch(o: _oracle.Oracle):
         assert np.array_equal(er, ref2[rows, cols])
 
 
+def pin_bf16_product_vs_torch(o: _oracle.Oracle):
+    rng = _rng(9)
+    for (M, N, K, alpha) in [(9, 7, 11, 1.0), (24, 40, 200, -0.5)]:
+        A = torch.from_numpy(rng.standard_normal((M, K)) * 0.5).to(torch.bfloat16)
+        B = torch.from_numpy(rng.standard_normal((K, N)) * 0.5).to(torch.bfloat16)
+        bias = rng.standard_normal(N).astype(np.float32)
+        a64, b64 = A.to(torch.float64), B.to(torch.float64)
+        x = alpha * (a64 @ b64) + torch.from_numpy(bias.astype(np.float64))
+        mag = abs(alpha) * (a64.abs() @ b64.abs()) + torch.from_numpy(np.abs(bias.astype(np.float64)))
+        tol = (K + 4) * U53 * mag.numpy() + 1e-300
+        bits = lambda t: t.view(torch.int16).numpy()  # noqa: E731
+        ref0, den0 = o.hgemm_bias_act(M, N, K, alpha, bits(A), K, bits(B), N, bias, _oracle.ACT_NONE,
+                                      fmt="bf16")
+        assert np.all(np.abs(ref0 - x.numpy()) <= tol), "bfloat16 product + bias"
+        assert np.allclose(den0, mag.numpy(), rtol=(K + 4) * U53)
+        ref1, _ = o.hgemm_bias_act(M, N, K, alpha, bits(A), K, bits(B), N, bias,
+                                   _oracle.ACT_GELU_TANH, fmt="bf16")
+        g = torch.nn.functional.gelu(x, approximate="tanh").numpy()
+        assert np.all(np.abs(ref1 - g) <= 2 * tol + 1e-14 * np.abs(g)), "bfloat16 gelu(x + bias)"
+        rows = rng.integers(0, M, 30)
+        cols = rng.integers(0, N, 30)
+        er, _ = o.hgemm_entries(K, alpha, bits(A), K, bits(B), N, bias, _oracle.ACT_GELU_TANH,
+                                rows, cols, fmt="bf16")
+        assert np.array_equal(er, ref1[rows, cols])
+
+
 def pin_half_unread(o: _oracle.Oracle):
     M, N, K = 4, 6, 5
     A = np.full((M, K), np.nan, np.float16)
@@ -266,7 +303,8 @@ def pin_half_unread(o: _oracle.Oracle):
 
 PINS = [pin_identity, pin_permutation, pin_all_ones, pin_alpha_zero_and_unread,
         pin_brute_force_rational, pin_small_integers_exact, pin_entries_match_full,
-        pin_half_decoder, pin_gelu, pin_half_product_vs_torch, pin_half_unread]
+        pin_half_decoder, pin_bf16_decoder, pin_gelu, pin_half_product_vs_torch,
+        pin_bf16_product_vs_torch, pin_half_unread]
 
 
 def failing_pins(o: _oracle.Oracle):

@@ -1,0 +1,124 @@
+"""The bfloat16 variant of the half product (bgemm_bias_act) on the GPU through the
+C ABI, against the CPU oracle with bfloat16 decoding.
+
+Bar: max |C - ref| / (|alpha| sum_k |a||b| + |bias_j|) <= 1e-2 (C is stored in
+bfloat16; its rounding alone is at most 2^-9 of |C|).  Identity and permutation
+operands without activation must match bit for bit.
+"""
+import itertools
+
+import pytest
+import torch
+
+import linear_algebra_sgemm_amd as lib
+import oracle
+from linear_algebra_sgemm_amd import inputs
+from tests.gpu_helpers import FP16_TOL, f16_bits, hgemm_error, note, run_hgemm
+
+pytestmark = pytest.mark.gpu
+
+TILES = (0, 1, 2, 3, 4)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def library():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lib.gemm_create()
+    yield
+    lib.gemm_debug_force_tile(1, -1)
+    torch.cuda.synchronize()
+    lib.gemm_destroy()
+
+
+@pytest.fixture
+def tile_forced():
+    yield
+    lib.gemm_debug_force_tile(1, -1)
+
+
+def check_full(M, N, K, alpha, act, seed, with_bias=True, lda=None, ldb=None, ldc=None, label=""):
+    A, B, bias = inputs.hgemm_inputs(M, N, K, seed, lda, ldb, fmt="bf16")
+    lda, ldb = A.shape[1], B.shape[1]
+    ldc = ldc or max(N, 1)
+    C = torch.full((M, ldc), float("nan"), dtype=torch.bfloat16)
+    b = bias if with_bias else None
+    note("bgemm %s M=%d N=%d K=%d lda=%d ldb=%d ldc=%d alpha=%g act=%d seed=%d"
+         % (label, M, N, K, lda, ldb, ldc, alpha, act, seed))
+    got = run_hgemm(M, N, K, alpha, A, lda, B, ldb, b, act, C, ldc)
+    err, where = hgemm_error(M, N, K, alpha, A, lda, B, ldb, b, act, got, ldc)
+    assert err <= FP16_TOL, "max normalised error %.3g at %s (%s)" % (err, where, label)
+    out = got.cpu()
+    if ldc > N:
+        assert torch.isnan(out[:, N:].float()).all(), "wrote outside the N columns"
+    return out
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("shape", [(512, 512, 128), (256, 768, 320), (300, 520, 100)])
+def test_every_tile(tile, shape, tile_forced):
+    lib.gemm_debug_force_tile(1, tile)
+    M, N, K = shape
+    check_full(M, N, K, 1.0, lib.ACT_GELU_TANH, seed=201 + tile, label="tile %d" % tile)
+
+
+@pytest.mark.parametrize("act", [lib.ACT_NONE, lib.ACT_GELU_TANH])
+def test_activation_options(act):
+    check_full(384, 640, 192, 0.5, act, seed=9, label="options")
+
+
+EDGE_SIZES = (1, 17, 64, 129)
+
+
+@pytest.mark.parametrize("M,N,K", list(itertools.product(EDGE_SIZES, repeat=3))[::5])
+def test_edge_grid(M, N, K):
+    check_full(M, N, K, 1.5, lib.ACT_GELU_TANH, seed=M * 7 + N * 5 + K, label="edge grid")
+
+
+def test_padded_leading_dimensions():
+    check_full(200, 136, 88, 1.0, lib.ACT_GELU_TANH, seed=13, lda=96, ldb=141, ldc=139,
+               label="padded ld")
+
+
+@pytest.mark.parametrize("tile", [0, 3])
+def test_exact_identity_and_permutation(tile, tile_forced):
+    lib.gemm_debug_force_tile(1, tile)
+    g = torch.Generator().manual_seed(19)
+    M, N = 256, 512
+    B = torch.randn((M, N), generator=g).bfloat16()
+    C = torch.zeros((M, N), dtype=torch.bfloat16)
+    note("bgemm identity tile=%d" % tile)
+    got = run_hgemm(M, N, M, 1.0, torch.eye(M).bfloat16(), M, B, N, None, lib.ACT_NONE, C, N).cpu()
+    assert torch.equal(got, B), "I x B must equal B bit for bit"
+    p = torch.randperm(M, generator=g)
+    P = torch.zeros((M, M))
+    P[torch.arange(M), p] = 1.0
+    got = run_hgemm(M, N, M, 1.0, P.bfloat16(), M, B, N, None, lib.ACT_NONE, C, N).cpu()
+    assert torch.equal(got, B[p]), "P x B must permute rows exactly"
+
+
+def test_alpha_zero():
+    M, N, K = 70, 90, 40
+    A, B, bias = inputs.hgemm_inputs(M, N, K, 29, fmt="bf16")
+    nanA = torch.full_like(A, float("nan"))
+    nanB = torch.full_like(B, float("nan"))
+    C = torch.zeros((M, N), dtype=torch.bfloat16)
+    want = torch.nn.functional.gelu(bias.double(), approximate="tanh")
+    note("bgemm alpha=0")
+    got = run_hgemm(M, N, K, 0.0, nanA, K, nanB, N, bias, lib.ACT_GELU_TANH, C, N).cpu()
+    e = (got.double() - want).abs() / bias.double().abs().clamp_min(1e-30)
+    assert torch.isfinite(got.float()).all() and float(e.max()) <= FP16_TOL
+
+
+def test_workload_ffn_full_size_sampled():
+    w = inputs.WORKLOADS["bgemm_ffn"]
+    A, B, bias = inputs.workload_inputs(w)
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16)
+    note("bgemm full-size ffn 4096x14336x4096")
+    got = run_hgemm(w.M, w.N, w.K, w.alpha, A, w.K, B, w.N, bias, lib.ACT_GELU_TANH, C, w.N).cpu()
+    assert torch.isfinite(got.float()).all()
+    rows, cols = inputs.sample_indices(w.M, w.N, 4096, w.seed)
+    ref, den = oracle.hgemm_entries(w.K, w.alpha, f16_bits(A), w.K, f16_bits(B), w.N, bias.numpy(),
+                                    oracle.ACT_GELU_TANH, rows, cols, fmt="bf16")
+    e = oracle.normalized_error(got.float().numpy()[rows, cols], ref, den)
+    assert float(e.max()) <= FP16_TOL, "max normalised error %.3g" % e.max()

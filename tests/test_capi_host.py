@@ -30,7 +30,8 @@ def so():
 
 def test_headers_declare_the_boundary():
     names = set(_declared_functions())
-    assert {"gemm_create", "gemm_destroy", "sgemm", "hgemm_bias_act", "gemm_status_string"} <= names
+    assert {"gemm_create", "gemm_destroy", "sgemm", "hgemm_bias_act", "bgemm_bias_act",
+            "gemm_status_string"} <= names
     assert names == set(lib.EXPORTED_SYMBOLS)
 
 
@@ -91,6 +92,15 @@ def test_hgemm_rejects_bad_arguments_without_gpu(so):
                                   raise_on_error=False)
 
     assert call(act=2) == lib.STATUS_INVALID_VALUE
+    b = dict(ok)
+    b["act"] = 7
+    assert lib.bgemm_bias_act(b["M"], b["N"], b["K"], b["alpha"], b["A"], b["lda"], b["B"],
+                              b["ldb"], b["bias"], b["act"], b["C"], b["ldc"], stream=0,
+                              raise_on_error=False) == lib.STATUS_INVALID_VALUE
+    b["act"] = 1
+    assert lib.bgemm_bias_act(b["M"], b["N"], b["K"], b["alpha"], b["A"], b["lda"], b["B"],
+                              b["ldb"], b["bias"], b["act"], b["C"], b["ldc"], stream=0,
+                              raise_on_error=False) == lib.STATUS_NOT_INITIALIZED
     assert call(act=-1) == lib.STATUS_INVALID_VALUE
     assert call(lda=7) == lib.STATUS_INVALID_VALUE
     assert call(ldc=15) == lib.STATUS_INVALID_VALUE

@@ -33,6 +33,7 @@ MUTATIONS = {
     "half_exponent_bias": ("v = ldexp((double)(frac + 1024), expo - 25);",
                            "v = ldexp((double)(frac + 1024), expo - 24);"),
     "half_subnormal_scale": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
+    "bf16_shift": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
     "hgemm_bias_row_index": ("double b = bias ? (double)bias[j] : 0.0;",
                              "double b = bias ? (double)bias[i % N] : 0.0;"),
     "den_missing_beta": ("cmag = fabs(beta) * fabs(c);\n        }\n        ref[",
