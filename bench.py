@@ -180,8 +180,11 @@ def main():
 
     traffic = profiled_traffic(w.name, w.op)
     if w.op == "sgemm":
-        tile = lib.gemm_debug_pick_tile(0, M, N, torch.cuda.get_device_properties(0).multi_processor_count)
+        tile, splits = lib.gemm_debug_pick_config(
+            0, M, N, K, torch.cuda.get_device_properties(0).multi_processor_count)
         kernel_name = "sgemm_mfma_kernel, tile config %d" % tile
+        if splits > 1:
+            kernel_name += ", split-K x%d + sgemm_splitk_reduce_kernel (timed together)" % splits
     else:
         kernel_name = "hgemm_dma_kernel (256x256, direct-to-LDS, %s)" % dtype
     line = {

@@ -26,11 +26,34 @@ extern "C" {
  */
 int gemm_debug_force_tile(int op, int tile);
 
-/* The tile configuration the library would choose for an M x N output on a
- * device with `cus` compute units (op 0 = sgemm; op 1 = hgemm_bias_act with
- * 16-byte-aligned operands and K a multiple of 64).  Returns -1 for an unknown
- * op.  Pure host computation. */
-int gemm_debug_pick_tile(int op, int M, int N, int cus);
+/*
+ * Force the number of K chunks (split-K) of later sgemm calls: op 0 only;
+ * splits -1 = choose by shape (the default), 1 = never split, 2 .. 32 = that
+ * many chunks (still reduced to what K and the workspace allow).  Returns
+ * GEMM_STATUS_INVALID_VALUE for another op or count.  Pure host state, not
+ * synchronised with calls in flight on other threads.
+ */
+int gemm_debug_force_splits(int op, int splits);
+
+/*
+ * Whether the shape -> configuration choice consults the offline-tuned table
+ * (on = 1, the default) or only the built-in rule (on = 0).  Forced tiles and
+ * split counts win either way.  Returns GEMM_STATUS_INVALID_VALUE for another
+ * value.  Pure host state.
+ */
+int gemm_debug_use_tuned_table(int on);
+
+/*
+ * The configuration the library would run for an M x N x K product on a device
+ * with `cus` compute units, forced values included: *tile receives the tile
+ * configuration, *splits the number of K chunks (1 = no split).  op 0 = sgemm
+ * with 16-byte-aligned operands; op 1 = the half products with 16-byte-aligned
+ * operands and lda, ldb multiples of 8 (always *splits = 1; a direct-to-LDS
+ * tile the shape does not suit is reported as the tile that runs instead).  Returns GEMM_STATUS_INVALID_VALUE for an
+ * unknown op, negative sizes, cus <= 0 or a null output pointer.  Pure host
+ * computation: no HIP call, no library state needed.
+ */
+int gemm_debug_pick_config(int op, int M, int N, int K, int cus, int* tile, int* splits);
 
 #ifdef __cplusplus
 }

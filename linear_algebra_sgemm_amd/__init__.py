@@ -15,7 +15,8 @@ import ctypes
 import os
 
 __all__ = ["GemmError", "gemm_create", "gemm_destroy", "sgemm", "hgemm_bias_act", "bgemm_bias_act",
-           "gemm_status_string", "gemm_debug_force_tile", "gemm_debug_pick_tile", "library_path",
+           "gemm_status_string", "gemm_debug_force_tile", "gemm_debug_force_splits",
+           "gemm_debug_pick_config", "gemm_debug_use_tuned_table", "library_path",
            "load_library", "EXPORTED_SYMBOLS", "ACT_NONE", "ACT_GELU_TANH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +34,8 @@ ACT_GELU_TANH = 1
 
 # Every symbol declared in include/gemm.h and include/gemm_debug.h.
 EXPORTED_SYMBOLS = ("gemm_create", "gemm_destroy", "sgemm", "hgemm_bias_act", "bgemm_bias_act",
-                    "gemm_status_string", "gemm_debug_force_tile", "gemm_debug_pick_tile")
+                    "gemm_status_string", "gemm_debug_force_tile", "gemm_debug_force_splits",
+                    "gemm_debug_pick_config", "gemm_debug_use_tuned_table")
 
 _lib = None
 
@@ -72,8 +74,13 @@ def load_library():
     lib.gemm_status_string.restype = ctypes.c_char_p
     lib.gemm_debug_force_tile.argtypes = [I, I]
     lib.gemm_debug_force_tile.restype = I
-    lib.gemm_debug_pick_tile.argtypes = [I, I, I, I]
-    lib.gemm_debug_pick_tile.restype = I
+    lib.gemm_debug_force_splits.argtypes = [I, I]
+    lib.gemm_debug_force_splits.restype = I
+    IP = ctypes.POINTER(ctypes.c_int)
+    lib.gemm_debug_pick_config.argtypes = [I, I, I, I, I, IP, IP]
+    lib.gemm_debug_pick_config.restype = I
+    lib.gemm_debug_use_tuned_table.argtypes = [I]
+    lib.gemm_debug_use_tuned_table.restype = I
     _lib = lib
     return lib
 
@@ -149,5 +156,18 @@ def gemm_debug_force_tile(op: int, tile: int) -> int:
     return load_library().gemm_debug_force_tile(int(op), int(tile))
 
 
-def gemm_debug_pick_tile(op: int, M: int, N: int, cus: int) -> int:
-    return load_library().gemm_debug_pick_tile(int(op), int(M), int(N), int(cus))
+def gemm_debug_force_splits(op: int, splits: int) -> int:
+    return load_library().gemm_debug_force_splits(int(op), int(splits))
+
+
+def gemm_debug_use_tuned_table(on: bool) -> int:
+    return load_library().gemm_debug_use_tuned_table(1 if on else 0)
+
+
+def gemm_debug_pick_config(op: int, M: int, N: int, K: int, cus: int):
+    """(tile, splits) the library would run for this shape, or raise GemmError."""
+    tile, splits = ctypes.c_int(-1), ctypes.c_int(-1)
+    st = load_library().gemm_debug_pick_config(int(op), int(M), int(N), int(K), int(cus),
+                                                ctypes.byref(tile), ctypes.byref(splits))
+    _check(st, "gemm_debug_pick_config", True)
+    return tile.value, splits.value

@@ -28,11 +28,26 @@ struct LibraryState {
   int cus = 256;
 };
 
+// Split-K workspace: FP32 partials, allocated by gemm_create and shared by all
+// calls.  Calls on different streams take turns: each split-K call first
+// waits for the event recorded after the previous one (when that ran on
+// another stream), then records the event after its own reduction.
+struct Workspace {
+  std::mutex mu;
+  float* ptr = nullptr;
+  size_t floats = 0;
+  hipEvent_t done = nullptr;
+  hipStream_t last = nullptr;
+  bool used = false;
+};
+
 LibraryState g_state;
+Workspace g_ws;
 std::atomic<int> g_ready{0};
 std::atomic<int> g_cus{256};
 std::atomic<int> g_force_sgemm_tile{-1};
 std::atomic<int> g_force_hgemm_tile{-1};
+std::atomic<int> g_force_sgemm_splits{-1};
 
 thread_local char t_last_error[256] = "";
 
@@ -65,6 +80,23 @@ int gemm_create(void) {
                   prop.gcnArchName);
     return GEMM_STATUS_ARCH_MISMATCH;
   }
+  {
+    std::lock_guard<std::mutex> wl(g_ws.mu);
+    void* ptr = nullptr;
+    e = hipMalloc(&ptr, lasg::kWorkspaceBytes);
+    if (e != hipSuccess) return hip_failure(e);
+    hipEvent_t ev = nullptr;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      (void)hipFree(ptr);
+      return hip_failure(e);
+    }
+    g_ws.ptr = static_cast<float*>(ptr);
+    g_ws.floats = lasg::kWorkspaceBytes / sizeof(float);
+    g_ws.done = ev;
+    g_ws.last = nullptr;
+    g_ws.used = false;
+  }
   g_state.device = dev;
   g_state.cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   g_cus.store(g_state.cus);
@@ -79,6 +111,16 @@ int gemm_destroy(void) {
   if (--g_state.refcount == 0) {
     g_ready.store(0);
     g_state.device = -1;
+    std::lock_guard<std::mutex> wl(g_ws.mu);
+    // Work still queued may use the workspace: let the device finish first.
+    hipError_t e = hipDeviceSynchronize();
+    if (g_ws.done) (void)hipEventDestroy(g_ws.done);
+    if (g_ws.ptr) (void)hipFree(g_ws.ptr);
+    g_ws.ptr = nullptr;
+    g_ws.floats = 0;
+    g_ws.done = nullptr;
+    g_ws.used = false;
+    if (e != hipSuccess) return hip_failure(e);
   }
   return GEMM_STATUS_SUCCESS;
 }
@@ -101,7 +143,24 @@ int sgemm(int M, int N, int K, float alpha, const float* A, int lda, const float
     e = lasg::launch_sgemm_scale(M, N, beta, C, ldc, stream);
   } else {
     lasg::SgemmCall c{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
-    e = lasg::launch_sgemm(c, g_cus.load(), g_force_sgemm_tile.load(), stream);
+    const lasg::SgemmPlan plan =
+        lasg::plan_sgemm(M, N, K, g_cus.load(), g_force_sgemm_tile.load(),
+                         g_force_sgemm_splits.load(), g_ws.floats);
+    if (plan.splits > 1) {
+      std::lock_guard<std::mutex> wl(g_ws.mu);
+      if (g_ws.ptr == nullptr) return GEMM_STATUS_NOT_INITIALIZED;
+      if (g_ws.used && g_ws.last != stream) {
+        e = hipStreamWaitEvent(stream, g_ws.done, 0);
+        if (e != hipSuccess) return hip_failure(e);
+      }
+      e = lasg::launch_sgemm(c, plan, g_ws.ptr, stream);
+      if (e != hipSuccess) return hip_failure(e);
+      e = hipEventRecord(g_ws.done, stream);
+      g_ws.last = stream;
+      g_ws.used = true;
+    } else {
+      e = lasg::launch_sgemm(c, plan, nullptr, stream);
+    }
   }
   return e == hipSuccess ? GEMM_STATUS_SUCCESS : hip_failure(e);
 }
@@ -157,23 +216,45 @@ const char* gemm_status_string(int status) {
 }
 
 int gemm_debug_force_tile(int op, int tile) {
+  if (op != 0 && op != 1) return GEMM_STATUS_INVALID_VALUE;
   const int count = op == 0 ? lasg::kSgemmTileCount : lasg::kHgemmTileCount;
   if (tile < -1 || tile >= count) return GEMM_STATUS_INVALID_VALUE;
-  if (op == 0) {
-    g_force_sgemm_tile.store(tile);
-  } else if (op == 1) {
-    g_force_hgemm_tile.store(tile);
-  } else {
-    return GEMM_STATUS_INVALID_VALUE;
-  }
+  (op == 0 ? g_force_sgemm_tile : g_force_hgemm_tile).store(tile);
   return GEMM_STATUS_SUCCESS;
 }
 
-int gemm_debug_pick_tile(int op, int M, int N, int cus) {
-  if (op == 0) return lasg::sgemm_pick_tile(M, N, cus);
-  // half product: aligned operands assumed, K a multiple of 64
-  if (op == 1) return lasg::hgemm_pick_tile(M, N, 64, cus, true);
-  return -1;
+int gemm_debug_force_splits(int op, int splits) {
+  if (op != 0) return GEMM_STATUS_INVALID_VALUE;
+  if (splits != -1 && (splits < 1 || splits > lasg::kMaxSplits)) return GEMM_STATUS_INVALID_VALUE;
+  g_force_sgemm_splits.store(splits);
+  return GEMM_STATUS_SUCCESS;
+}
+
+int gemm_debug_use_tuned_table(int on) {
+  if (on != 0 && on != 1) return GEMM_STATUS_INVALID_VALUE;
+  lasg::set_use_tuned(on == 1);
+  return GEMM_STATUS_SUCCESS;
+}
+
+int gemm_debug_pick_config(int op, int M, int N, int K, int cus, int* tile, int* splits) {
+  if (M < 0 || N < 0 || K < 0 || cus <= 0 || tile == nullptr || splits == nullptr)
+    return GEMM_STATUS_INVALID_VALUE;
+  if (op == 0) {
+    const lasg::SgemmPlan p =
+        lasg::plan_sgemm(M, N, K, cus, g_force_sgemm_tile.load(), g_force_sgemm_splits.load(),
+                         lasg::kWorkspaceBytes / sizeof(float));
+    *tile = p.tile;
+    *splits = p.splits;
+    return GEMM_STATUS_SUCCESS;
+  }
+  if (op == 1) {
+    const int forced = g_force_hgemm_tile.load();
+    *tile = lasg::hgemm_resolve_tile(forced >= 0 ? forced : lasg::hgemm_pick_tile(M, N, K, cus, true),
+                                     M, N, K, true);
+    *splits = 1;
+    return GEMM_STATUS_SUCCESS;
+  }
+  return GEMM_STATUS_INVALID_VALUE;
 }
 
 }  // extern "C"

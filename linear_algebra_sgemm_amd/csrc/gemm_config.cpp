@@ -1,0 +1,136 @@
+// Shape -> configuration: which tile configuration and how many K chunks a
+// call uses.  Host code only.
+//
+// Two sources, in order:
+//  1. an offline-tuned table (gemm_tuned.inc, written by tune.py beside the
+//     package from timings of every legal configuration on MI355X), keyed by
+//     the size class of M, N and K (log2 rounded to the nearest integer,
+//     clamped to 7..14, i.e. 128 .. 16384); it only lists classes where a
+//     configuration beat the built-in rule;
+//  2. the built-in rule below.
+// Either way the result then passes the legality filter: the split count is
+// clamped to the K tiles there are and to the workspace.  This follows the
+// parameter search of the SGEMM page (kernel k9, section "k7、k8、k9": many
+// tile-parameter combinations timed on the target GPU, the best one kept) and
+// the DeepGEMM page's offline tuning of block shapes and split-K with a table
+// lookup at run time (section 5.3).
+#include <atomic>
+#include <cmath>
+#include <cstddef>
+
+#include "gemm_launch.h"
+
+namespace lasg {
+
+namespace {
+
+struct TunedEntry {
+  signed char op, lm, ln, lk, tile, splits;
+};
+
+const TunedEntry kTuned[] = {
+#include "gemm_tuned.inc"
+    {-1, 0, 0, 0, 0, 0},  // end marker
+};
+
+std::atomic<bool> g_use_tuned{true};
+
+int size_class(int x) {
+  if (x <= 1) return 7;
+  const long c = std::lround(std::log2((double)x));
+  return c < 7 ? 7 : c > 14 ? 14 : (int)c;
+}
+
+long ceil_div(long a, long b) { return (a + b - 1) / b; }
+
+// Built-in tile rule, measured on MI355X: 128x256 tiles at two workgroups per
+// CU are fastest once they give every CU two tiles (4096^3: 133 vs 130
+// TFLOP/s for 256x256); below that, 128x128 if it still gives two tiles per
+// CU, else 64x64 tiles, which spread small outputs over more CUs (2048^3: 106
+// vs 104; 1000x3000x777: 51 vs 42).
+int sgemm_rule_tile(int M, int N, int cus) {
+  const long t_tall = ceil_div(M, 128) * ceil_div(N, 256);
+  const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
+  if (t_tall >= 2L * cus) return 4;
+  if (t_med >= 2L * cus) return 1;
+  return 2;
+}
+
+// Built-in split rule: when the output has fewer tiles than there are CUs,
+// split K so that tiles x splits reaches the CU count, keeping at least four
+// K tiles per chunk.
+int sgemm_rule_splits(int M, int N, int K, int tile, int cus) {
+  const long tiles = ceil_div(M, sgemm_tile_bm(tile)) * ceil_div(N, sgemm_tile_bn(tile));
+  if (tiles >= cus) return 1;
+  const long by_cus = ceil_div(cus, tiles);
+  const long by_k = ceil_div(K, sgemm_tile_bk(tile)) / 4;
+  long s = by_cus < by_k ? by_cus : by_k;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : (int)s;
+}
+
+}  // namespace
+
+void set_use_tuned(bool on) { g_use_tuned.store(on); }
+
+bool tuned_config(int op, int M, int N, int K, int* tile, int* splits) {
+  if (!g_use_tuned.load()) return false;
+  const int lm = size_class(M), ln = size_class(N), lk = size_class(K);
+  for (const TunedEntry* e = kTuned; e->op >= 0; ++e) {
+    if (e->op == op && e->lm == lm && e->ln == ln && e->lk == lk) {
+      *tile = e->tile;
+      *splits = e->splits;
+      return true;
+    }
+  }
+  return false;
+}
+
+SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_splits,
+                     size_t ws_floats) {
+  int tuned_tile = -1, tuned_splits = -1;
+  const bool tuned = tuned_config(0, M, N, K, &tuned_tile, &tuned_splits) &&
+                     tuned_tile >= 0 && tuned_tile < kSgemmTileCount && tuned_splits >= 1;
+  SgemmPlan p;
+  p.tile = force_tile >= 0 ? force_tile : tuned ? tuned_tile : sgemm_rule_tile(M, N, cus);
+  long s = force_splits > 0 ? force_splits
+           : (tuned && force_tile < 0) ? tuned_splits
+                                       : sgemm_rule_splits(M, N, K, p.tile, cus);
+  // Legality: whole K tiles per chunk, no empty chunk, partials fit the workspace.
+  const long bk = sgemm_tile_bk(p.tile);
+  const long ktiles = ceil_div(K, bk);
+  const long mn = (long)M * N;
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s > ktiles) s = ktiles;
+  if (mn > 0 && s > (long)(ws_floats / (size_t)mn)) s = (long)(ws_floats / (size_t)mn);
+  long chunk = K;
+  if (s > 1) {
+    chunk = ceil_div(ktiles, s) * bk;
+    s = ceil_div(K, chunk);  // no chunk is empty
+  }
+  if (s <= 1) {
+    s = 1;
+    chunk = K;
+  }
+  p.splits = (int)s;
+  p.k_chunk = (int)chunk;
+  return p;
+}
+
+int hgemm_pick_tile(int M, int N, int K, int cus, bool operands_ok) {
+  int tuned_tile = -1, tuned_splits = 1;
+  if (tuned_config(1, M, N, K, &tuned_tile, &tuned_splits) && tuned_tile >= 0 &&
+      tuned_tile < kHgemmTileCount)
+    return tuned_tile;
+  // Built-in rule: whole 256x256 tiles take the direct-to-LDS kernel; other
+  // shapes the register-staged kernel with the largest tile that still fills
+  // the device.
+  const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
+  const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
+  if (M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && operands_ok) return 3;
+  if (t_large >= cus) return 0;
+  if (t_med >= cus / 2) return 1;
+  return 2;
+}
+
+}  // namespace lasg

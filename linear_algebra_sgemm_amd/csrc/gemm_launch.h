@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace lasg {
@@ -40,14 +41,51 @@ struct HgemmCall {
 constexpr int kSgemmTileCount = 5;
 constexpr int kHgemmTileCount = 5;
 
-// Tile configuration the shape selects on a device with `cus` compute units
-// (for the half product, `dma_ok` says whether operand alignment and leading
-// dimensions allow the direct-to-LDS kernel).
-int sgemm_pick_tile(int M, int N, int cus);
-int hgemm_pick_tile(int M, int N, int K, int cus, bool dma_ok);
+// K step of each SGEMM tile configuration (checked against the kernels).
+constexpr int sgemm_tile_bk(int tile) { return tile == 3 ? 32 : 16; }
+// Output tile of each SGEMM configuration.
+constexpr int sgemm_tile_bm(int tile) { return tile == 0 || tile == 3 ? 256 : tile == 2 ? 64 : 128; }
+constexpr int sgemm_tile_bn(int tile) { return tile == 0 || tile == 3 || tile == 4 ? 256 : tile == 2 ? 64 : 128; }
 
-// force_tile < 0 lets the shape decide; otherwise it names the tile configuration.
-hipError_t launch_sgemm(const SgemmCall& c, int cus, int force_tile, hipStream_t s);
+// Split-K: at most this many K chunks per output tile.
+constexpr int kMaxSplits = 32;
+// Library-owned FP32 workspace for split-K partials (per device, allocated by
+// gemm_create): splits * M * N floats must fit.
+constexpr size_t kWorkspaceBytes = size_t(64) << 20;
+
+// How one SGEMM call runs: tile configuration, number of K chunks (1 = no
+// split) and the chunk length in elements (a multiple of the tile's K step).
+struct SgemmPlan {
+  int tile;
+  int splits;
+  int k_chunk;
+};
+
+// The plan for an M x N x K product on `cus` compute units.  force_tile /
+// force_splits < 0 let the shape decide (offline-tuned table, else the
+// built-in rule); the split count is then clamped to the K tiles there are and
+// to `ws_floats` of workspace.
+SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_splits,
+                     size_t ws_floats);
+
+// Offline-tuned choice for (op, M, N, K) if the table has one for the shape's
+// size class: op 0 = sgemm, op 1 = the half products.
+bool tuned_config(int op, int M, int N, int K, int* tile, int* splits);
+
+// Tile configuration of the half products (`operands_ok`: lda and ldb are
+// multiples of 8 and A, B 16-byte aligned, as the direct-to-LDS kernels need).
+int hgemm_pick_tile(int M, int N, int K, int cus, bool operands_ok);
+// The configuration that actually runs for `tile`: the direct-to-LDS ones (3,
+// 4) become the register-staged 256x256 one (0) when the shape or operands do
+// not suit them.
+int hgemm_resolve_tile(int tile, int M, int N, int K, bool operands_ok);
+
+// Whether the offline-tuned table is consulted (default on; a test hook turns
+// it off to see the built-in rule).
+void set_use_tuned(bool on);
+
+// `ws` holds at least plan.splits * M * N floats when plan.splits > 1.
+hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hipStream_t s);
 hipError_t launch_sgemm_scale(int M, int N, float beta, float* C, int ldc, hipStream_t s);
 
 // The half-precision product: binary16 (hgemm) or bfloat16 (bgemm) inputs and

@@ -671,31 +671,35 @@ static hipError_t launch_hdma(const HgemmCall& c, int group_m, hipStream_t s) {
   return hipGetLastError();
 }
 
-int hgemm_pick_tile(int M, int N, int K, int cus, bool dma_ok) {
-  // Whole 256x256 tiles take the direct-to-LDS kernel; other shapes the
-  // register-staged kernel with the largest tile that still fills the device.
-  const long t_large = (long)((M + 255) / 256) * ((N + 255) / 256);
-  const long t_med = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if (M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && dma_ok) return 3;
-  if (t_large >= cus) return 0;
-  if (t_med >= cus / 2) return 1;
-  return 2;
+static_assert(HDmaLarge<EltF16>::BM == 256 && HDmaLarge<EltF16>::BN == 256 &&
+                  HDmaTall<EltF16>::BM == 128 && HDmaTall<EltF16>::BN == 256 &&
+                  2 * HDmaLarge<EltF16>::BK == 64 && 2 * HDmaTall<EltF16>::BK == 64,
+              "hgemm_resolve_tile's shape conditions must match the direct-to-LDS tiles");
+
+int hgemm_resolve_tile(int tile, int M, int N, int K, bool operands_ok) {
+  // The direct-to-LDS kernels need whole tiles and K a multiple of 64;
+  // otherwise the register-staged 256x256 kernel, which handles every shape, runs.
+  if (tile == 3 && !(operands_ok && M % 256 == 0 && N % 256 == 0 && K % 64 == 0)) return 0;
+  if (tile == 4 && !(operands_ok && M % 128 == 0 && N % 256 == 0 && K % 64 == 0)) return 0;
+  return tile;
 }
 
 template <class E>
 static hipError_t launch_half(const HgemmCall& c, int cus, int force_tile, hipStream_t s) {
-  int tile = force_tile;
-  if (tile < 0) tile = hgemm_pick_tile(c.M, c.N, c.K, cus, dma_fits<HDmaLarge<E>>(c));
-  // The direct-to-LDS kernels need whole tiles; otherwise fall back to the
-  // register-staged kernel of the same tile size, which handles every shape.
-  if (tile == 3 && !dma_fits<HDmaLarge<E>>(c)) tile = 0;
+  const bool operands_ok = c.lda % 8 == 0 && c.ldb % 8 == 0 &&
+                           (reinterpret_cast<uintptr_t>(c.A) & 15u) == 0 &&
+                           (reinterpret_cast<uintptr_t>(c.B) & 15u) == 0;
+  int tile = force_tile >= 0 ? force_tile : hgemm_pick_tile(c.M, c.N, c.K, cus, operands_ok);
+  tile = hgemm_resolve_tile(tile, c.M, c.N, c.K, operands_ok);
   switch (tile) {
     case 0: return launch_htile<HTileLarge<E>>(c, 4, s);
     case 1: return launch_htile<HTileMedium<E>>(c, 8, s);
     case 2: return launch_htile<HTileSmall<E>>(c, 8, s);
-    case 3: return launch_hdma<HDmaLarge<E>>(c, 4, s);
+    case 3:
+      if (!dma_fits<HDmaLarge<E>>(c)) return hipErrorInvalidValue;
+      return launch_hdma<HDmaLarge<E>>(c, 4, s);
     case 4:
-      if (!dma_fits<HDmaTall<E>>(c)) return launch_htile<HTileLarge<E>>(c, 4, s);
+      if (!dma_fits<HDmaTall<E>>(c)) return hipErrorInvalidValue;
       return launch_hdma<HDmaTall<E>>(c, 8, s);
     default: return hipErrorInvalidValue;
   }

@@ -14,7 +14,13 @@
 //  * LDS rows are padded so the 16-byte fragment reads and the B row reads are
 //    free of bank conflicts (Tiled-GEMM 11.5; lecture 24, 4.2);
 //  * ragged M, N, K and unaligned leading dimensions are handled by zero-filling
-//    out-of-range loads and predicating stores (Tiled-GEMM 11.3).
+//    out-of-range loads and predicating stores (Tiled-GEMM 11.3);
+//  * shapes with too few output tiles to occupy the GPU split K over several
+//    workgroups per tile (the split-K of lecture 24, section 8.3, exercise 2,
+//    and of the DeepGEMM page, section 5.3).  Those pages merge the partials
+//    with atomic adds; here each workgroup writes its FP32 partial to a
+//    workspace and a second kernel adds the partials in a fixed order and
+//    applies alpha and beta, so results do not change from run to run.
 //
 // The MFMA consumes, per lane, one A value (row l % 32, k-slot l / 32) and one
 // B value (column l % 32, k-slot l / 32).  Which physical k feeds which k-slot
@@ -67,6 +73,10 @@ struct SgemmArgs {
   float* C;
   int ldc;
   int tiles_m, tiles_n, group_m;
+  // Split-K: workgroup row blockIdx.y covers K range [y * k_chunk, min(K, (y + 1) * k_chunk))
+  // and writes its raw partial to ws + y * M * N (M x N, row stride N).
+  int k_chunk;
+  float* ws;
 };
 
 // Global -> register staging of one K tile.  EDGE selects bounds-checked scalar
@@ -130,9 +140,18 @@ struct Stage {
   }
 };
 
-template <class T, bool EDGE>
+template <class T, bool EDGE, bool SPLIT>
 __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(T::WAVES_PER_SIMD)))
 sgemm_mfma_kernel(SgemmArgs p) {
+  if constexpr (SPLIT) {
+    // This workgroup's K chunk: shift A and B to its start and shorten K.  The
+    // chunk length is a multiple of BK, so the fast path's alignment holds.
+    const int kbeg = blockIdx.y * p.k_chunk;
+    const int klen = p.K - kbeg < p.k_chunk ? p.K - kbeg : p.k_chunk;
+    p.A += kbeg;
+    p.B += (size_t)kbeg * p.ldb;
+    p.K = klen;
+  }
   __shared__ __attribute__((aligned(16))) float lds[T::LDS_FLOATS];
   float* const As0 = lds;
   float* const Bs0 = lds + T::A_STAGE;
@@ -202,6 +221,24 @@ sgemm_mfma_kernel(SgemmArgs p) {
     __syncthreads();
   }
 
+  if constexpr (SPLIT) {
+    // Raw partial sums into this K chunk's slice of the workspace.
+    float* W = p.ws + (size_t)blockIdx.y * p.M * p.N;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) {
+        const int col = n0 + wn * T::WTN + j * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * T::WTM + i * 32 + mfma32_row(r, lane);
+          if (EDGE && (row >= p.M || col >= p.N)) continue;
+          W[(size_t)row * p.N + col] = acc[i][j][r];
+        }
+      }
+    return;
+  }
+
   // Epilogue: C = alpha * acc + beta * C, C read only when beta != 0.  For each
   // row of blocks, all C loads are issued before the first one is consumed, so
   // their latencies overlap instead of adding up.
@@ -248,6 +285,23 @@ __global__ void __launch_bounds__(256) sgemm_scale_kernel(int M, int N, float be
   }
 }
 
+// Second half of split-K: C = alpha * (sum of the `splits` partials, added in
+// order 0, 1, ...) + beta * C, C read only when beta != 0.
+__global__ void __launch_bounds__(256) sgemm_splitk_reduce_kernel(int M, int N, int splits,
+                                                                  const float* ws, float alpha,
+                                                                  float beta, float* C, int ldc) {
+  const int64_t total = (int64_t)M * N;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    float sum = ws[t];
+    for (int q = 1; q < splits; ++q) sum += ws[q * total + t];
+    const int64_t i = t / N, j = t % N;
+    float* dst = C + i * ldc + j;
+    const float v = alpha * sum;
+    *dst = (beta != 0.0f) ? __builtin_fmaf(beta, *dst, v) : v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launchers.
 // ---------------------------------------------------------------------------
@@ -257,8 +311,25 @@ using TileSmall = SgemmTile<64, 64, 16, 2, 2>;       // 4 waves, 32 x 32 each
 using TileLargeK32 = SgemmTile<256, 256, 32, 2, 2>;  // as TileLarge, half the barriers
 using TileTall = SgemmTile<128, 256, 16, 2, 2, 2>;   // 4 waves, 64 x 128 each, 2 workgroups/CU
 
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static_assert(TileLarge::BK == sgemm_tile_bk(0) && TileMedium::BK == sgemm_tile_bk(1) &&
+                  TileSmall::BK == sgemm_tile_bk(2) && TileLargeK32::BK == sgemm_tile_bk(3) &&
+                  TileTall::BK == sgemm_tile_bk(4),
+              "the host-side planner's K steps must match the tiles");
+
+static hipError_t launch_reduce(const SgemmCall& c, int splits, const float* ws, hipStream_t s) {
+  const int64_t total = (int64_t)c.M * c.N;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(sgemm_splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, c.M,
+                     c.N, splits, ws, c.alpha, c.beta, c.C, c.ldc);
+  return hipGetLastError();
+}
+
 template <class T>
-static hipError_t launch_tile(const SgemmCall& c, bool edge, int group_m, hipStream_t s) {
+static hipError_t launch_tile(const SgemmCall& c, const SgemmPlan& plan, int group_m, float* ws,
+                              hipStream_t s) {
   SgemmArgs p;
   p.M = c.M; p.N = c.N; p.K = c.K;
   p.alpha = c.alpha; p.beta = c.beta;
@@ -266,42 +337,36 @@ static hipError_t launch_tile(const SgemmCall& c, bool edge, int group_m, hipStr
   p.tiles_m = (c.M + T::BM - 1) / T::BM;
   p.tiles_n = (c.N + T::BN - 1) / T::BN;
   p.group_m = group_m;
-  const dim3 grid(p.tiles_m * p.tiles_n), block(T::THREADS);
+  p.k_chunk = plan.k_chunk;
+  p.ws = ws;
+  const bool edge = !(c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % T::BK == 0 &&
+                      c.lda % 4 == 0 && c.ldb % 4 == 0 && aligned16(c.A) && aligned16(c.B));
+  const bool split = plan.splits > 1;
+  const dim3 grid(p.tiles_m * p.tiles_n, split ? plan.splits : 1), block(T::THREADS);
+  if (split) {
+    if (edge)
+      hipLaunchKernelGGL((sgemm_mfma_kernel<T, true, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((sgemm_mfma_kernel<T, false, true>), grid, block, 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_reduce(c, plan.splits, ws, s);
+  }
   if (edge)
-    hipLaunchKernelGGL((sgemm_mfma_kernel<T, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((sgemm_mfma_kernel<T, true, false>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((sgemm_mfma_kernel<T, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((sgemm_mfma_kernel<T, false, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
-static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-template <class T>
-static bool fits_fast_path(const SgemmCall& c) {
-  return c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % T::BK == 0 && c.lda % 4 == 0 &&
-         c.ldb % 4 == 0 && aligned16(c.A) && aligned16(c.B);
-}
-
-int sgemm_pick_tile(int M, int N, int cus) {
-  // Measured on MI355X: 128x256 tiles at two workgroups per CU are fastest once
-  // they give every CU two tiles (4096^3: 133 vs 130 TFLOP/s for 256x256);
-  // below that, small 64x64 tiles beat 128x128 because they spread the work
-  // over more CUs (2048^3: 106 vs 104; 1000x3000x777: 51 vs 42).
-  const long t_tall = (long)((M + 127) / 128) * ((N + 255) / 256);
-  const long t_med = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if (t_tall >= 2L * cus) return 4;
-  if (t_med >= 2L * cus) return 1;
-  return 2;
-}
-
-hipError_t launch_sgemm(const SgemmCall& c, int cus, int force_tile, hipStream_t s) {
-  const int tile = force_tile >= 0 ? force_tile : sgemm_pick_tile(c.M, c.N, cus);
-  switch (tile) {
-    case 0: return launch_tile<TileLarge>(c, !fits_fast_path<TileLarge>(c), 4, s);
-    case 1: return launch_tile<TileMedium>(c, !fits_fast_path<TileMedium>(c), 8, s);
-    case 2: return launch_tile<TileSmall>(c, !fits_fast_path<TileSmall>(c), 8, s);
-    case 3: return launch_tile<TileLargeK32>(c, !fits_fast_path<TileLargeK32>(c), 4, s);
-    case 4: return launch_tile<TileTall>(c, !fits_fast_path<TileTall>(c), 8, s);
+hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hipStream_t s) {
+  if (plan.splits > 1 && ws == nullptr) return hipErrorInvalidValue;
+  switch (plan.tile) {
+    case 0: return launch_tile<TileLarge>(c, plan, 4, ws, s);
+    case 1: return launch_tile<TileMedium>(c, plan, 8, ws, s);
+    case 2: return launch_tile<TileSmall>(c, plan, 8, ws, s);
+    case 3: return launch_tile<TileLargeK32>(c, plan, 4, ws, s);
+    case 4: return launch_tile<TileTall>(c, plan, 8, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

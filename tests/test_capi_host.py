@@ -1,7 +1,9 @@
 """The C-ABI library on the CPU: it loads, exports every declared symbol, and its
 host-side argument checks answer without touching a GPU."""
 import ctypes
+import math
 import os
+import random
 import re
 
 import pytest
@@ -114,20 +116,155 @@ def test_destroy_without_create(so):
     assert lib.gemm_destroy(raise_on_error=False) == lib.STATUS_NOT_INITIALIZED
 
 
-def test_tile_choice(so):
-    # largest tile when it still fills the device, smaller tiles for small outputs
-    assert lib.gemm_debug_pick_tile(0, 4096, 4096, 256) == 4
-    assert lib.gemm_debug_pick_tile(0, 8192, 8192, 256) == 4
-    assert lib.gemm_debug_pick_tile(0, 256, 256, 256) == 2
-    assert lib.gemm_debug_pick_tile(0, 1000, 3000, 256) == 2
-    assert lib.gemm_debug_pick_tile(0, 2048, 2048, 256) == 2
-    assert lib.gemm_debug_pick_tile(0, 4096, 4096, 64) == 4
-    # the half product: whole 256-tiles take the direct-to-LDS kernel (3)
-    assert lib.gemm_debug_pick_tile(1, 4096, 14336, 256) == 3
-    assert lib.gemm_debug_pick_tile(1, 4096, 4000, 256) == 0
-    assert lib.gemm_debug_pick_tile(1, 2048, 2000, 256) == 1
-    assert lib.gemm_debug_pick_tile(1, 300, 500, 256) == 2
-    assert lib.gemm_debug_pick_tile(2, 300, 500, 256) == -1
+TUNED_TABLE = os.path.join(ROOT, "linear_algebra_sgemm_amd", "csrc", "gemm_tuned.inc")
+
+
+def tuned_classes():
+    """(op, class M, class N, class K) of every entry of the offline-tuned table."""
+    out = set()
+    for line in open(TUNED_TABLE):
+        m = re.match(r"\s*\{\s*(-?\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*,", line)
+        if m:
+            out.add(tuple(int(g) for g in m.groups()))
+    return out
+
+
+def size_class(x):
+    c = round(math.log2(x)) if x > 1 else 7
+    return min(max(c, 7), 14)
+
+
+def load_raw():
+    return lib.load_library()
+
+
+def pick(op, M, N, K, cus=256):
+    return lib.gemm_debug_pick_config(op, M, N, K, cus)
+
+
+def test_config_rule(so):
+    """The built-in rule (tuned table off): the largest tile that still gives every
+    CU two tiles, split-K only when the tiles do not cover the CUs."""
+    cases = [
+        (0, 4096, 4096, 4096, 256, (4, 1)),
+        (0, 8192, 8192, 8192, 256, (4, 1)),
+        (0, 256, 256, 256, 256, (2, 4)),      # 16 tiles; >= 4 K tiles per chunk
+        (0, 512, 512, 512, 256, (2, 4)),      # 64 tiles; 256 / 64 = 4 chunks
+        (0, 1000, 3000, 777, 256, (2, 1)),    # 752 tiles
+        (0, 2048, 2048, 2048, 256, (2, 1)),
+        (0, 4096, 4096, 4096, 64, (4, 1)),
+        (0, 128, 128, 16384, 256, (2, 32)),   # 4 tiles; 64 chunks by CUs, capped at 32
+        (1, 4096, 14336, 4096, 256, (3, 1)),  # whole 256-tiles: direct-to-LDS kernel
+        (1, 4096, 4000, 4096, 256, (0, 1)),
+        (1, 2048, 2000, 4096, 256, (1, 1)),
+        (1, 300, 500, 4096, 256, (2, 1)),
+    ]
+    assert lib.gemm_debug_use_tuned_table(False) == lib.STATUS_SUCCESS
+    try:
+        for op, M, N, K, cus, want in cases:
+            assert pick(op, M, N, K, cus) == want, (op, M, N, K, cus)
+    finally:
+        assert lib.gemm_debug_use_tuned_table(True) == lib.STATUS_SUCCESS
+    assert load_raw().gemm_debug_use_tuned_table(2) == lib.STATUS_INVALID_VALUE
+    # with the table on, the shapes the table does not list still follow the rule
+    table = tuned_classes()
+    for op, M, N, K, cus, want in cases:
+        if (op, size_class(M), size_class(N), size_class(K)) not in table:
+            assert pick(op, M, N, K, cus) == want, (op, M, N, K, cus)
+
+
+def test_half_tile_resolution(so):
+    """A forced direct-to-LDS tile that the shape does not suit is reported (and run)
+    as the register-staged 256x256 configuration."""
+    try:
+        assert lib.gemm_debug_force_tile(1, 3) == lib.STATUS_SUCCESS
+        assert pick(1, 4096, 4096, 4096) == (3, 1)
+        assert pick(1, 300, 512, 4096) == (0, 1)
+        assert pick(1, 512, 512, 96) == (0, 1)
+        assert lib.gemm_debug_force_tile(1, 4) == lib.STATUS_SUCCESS
+        assert pick(1, 128, 256, 64) == (4, 1)
+        assert pick(1, 128, 128, 64) == (0, 1)
+        assert lib.gemm_debug_force_tile(1, 1) == lib.STATUS_SUCCESS
+        assert pick(1, 128, 128, 64) == (1, 1)
+    finally:
+        lib.gemm_debug_force_tile(1, -1)
+
+
+def test_config_tuned_entries_are_used(so):
+    """Every tuned entry is what the library runs for a shape of that size class
+    (before the legality clamps, which cannot bind at these aligned sizes)."""
+    for line in open(TUNED_TABLE):
+        m = re.match(r"\s*\{\s*(-?\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*,\s*(\d+)\s*,"
+                     r"\s*(\d+)\s*,\s*(\d+)\s*\}", line)
+        if not m:
+            continue
+        op, lm, ln, lk, tile, splits = (int(g) for g in m.groups())
+        M, N, K = 1 << lm, 1 << ln, 1 << lk
+        got = pick(op, M, N, K)
+        assert got[0] == tile, (op, M, N, K, got, tile)
+        if op == 0 and splits * M * N <= (64 << 20) // 4 and splits <= -(-K // 32):
+            assert got[1] == splits, (op, M, N, K, got, splits)
+
+
+def bk_of(tile):
+    return 32 if tile == 3 else 16
+
+
+def test_split_legality(so):
+    """Forced split counts are reduced to what K and the 64 MiB workspace allow,
+    with no empty K chunk."""
+    rng = random.Random(7)
+    try:
+        for _ in range(400):
+            M, N = rng.randint(1, 3000), rng.randint(1, 3000)
+            K = rng.choice([1, 15, 16, 17, 100, 777, 4096, 20000])
+            want = rng.choice([1, 2, 3, 5, 8, 16, 32])
+            tile = rng.choice([-1, 0, 1, 2, 3, 4])
+            assert lib.gemm_debug_force_tile(0, tile) == lib.STATUS_SUCCESS
+            assert lib.gemm_debug_force_splits(0, want) == lib.STATUS_SUCCESS
+            t, s = pick(0, M, N, K)
+            if tile >= 0:
+                assert t == tile
+            bk = bk_of(t)
+            ktiles = -(-K // bk)
+            assert 1 <= s <= max(1, min(want, ktiles))
+            assert s * M * N <= (64 << 20) // 4 or s == 1
+            if s > 1:
+                chunk = -(-ktiles // min(want, ktiles, (64 << 20) // 4 // (M * N))) * bk
+                assert s == -(-K // chunk) and (s - 1) * chunk < K
+    finally:
+        lib.gemm_debug_force_tile(0, -1)
+        lib.gemm_debug_force_splits(0, -1)
+
+
+def test_forced_splits(so):
+    try:
+        assert lib.gemm_debug_force_tile(0, 2) == lib.STATUS_SUCCESS
+        assert lib.gemm_debug_force_splits(0, 8) == lib.STATUS_SUCCESS
+        assert pick(0, 256, 256, 256) == (2, 8)        # 16 K tiles, 2 per chunk
+        assert pick(0, 256, 256, 100) == (2, 7)        # only 7 K tiles
+        assert pick(0, 8192, 8192, 8192) == (2, 1)     # 8 x 256 MiB exceeds the workspace
+        assert pick(0, 2048, 2048, 4096) == (2, 4)     # 4 x 16 MiB fits exactly
+        assert lib.gemm_debug_force_splits(0, 3) == lib.STATUS_SUCCESS
+        assert pick(0, 64, 64, 160) == (2, 3)          # 10 K tiles -> chunks of 4, 4, 2
+        assert lib.gemm_debug_force_splits(0, 1) == lib.STATUS_SUCCESS
+        assert pick(0, 64, 64, 16384) == (2, 1)
+    finally:
+        lib.gemm_debug_force_tile(0, -1)
+        lib.gemm_debug_force_splits(0, -1)
+    assert lib.gemm_debug_force_splits(0, 0) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_splits(0, 33) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_splits(1, 2) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_splits(0, -1) == lib.STATUS_SUCCESS
+    with pytest.raises(lib.GemmError):
+        pick(2, 300, 500, 64)
+    with pytest.raises(lib.GemmError):
+        pick(0, -1, 500, 64)
+    with pytest.raises(lib.GemmError):
+        pick(0, 300, 500, 64, cus=0)
+
+
+def test_force_tile_values(so):
     assert lib.gemm_debug_force_tile(0, 5) == lib.STATUS_INVALID_VALUE
     assert lib.gemm_debug_force_tile(1, 5) == lib.STATUS_INVALID_VALUE
     assert lib.gemm_debug_force_tile(1, 3) == lib.STATUS_SUCCESS
