@@ -56,14 +56,14 @@ int sgemm_rule_tile(int M, int N, int cus) {
   return 2;
 }
 
-// Built-in split rule: when the output has fewer tiles than there are CUs,
-// split K so that tiles x splits reaches the CU count, keeping at least four
-// K tiles per chunk.
+// Built-in split rule (from the size sweep): when the output has fewer tiles
+// than there are CUs and K is at least 512, split K until there are about four
+// workgroups per CU (small tiles share a CU), keeping chunks of at least 128.
 int sgemm_rule_splits(int M, int N, int K, int tile, int cus) {
   const long tiles = ceil_div(M, sgemm_tile_bm(tile)) * ceil_div(N, sgemm_tile_bn(tile));
-  if (tiles >= cus) return 1;
-  const long by_cus = ceil_div(cus, tiles);
-  const long by_k = ceil_div(K, sgemm_tile_bk(tile)) / 4;
+  if (tiles >= cus || K < 512) return 1;
+  const long by_cus = ceil_div(4L * cus, tiles);
+  const long by_k = ceil_div(K, sgemm_tile_bk(tile)) * sgemm_tile_bk(tile) / 128;
   long s = by_cus < by_k ? by_cus : by_k;
   if (s > kMaxSplits) s = kMaxSplits;
   return s < 1 ? 1 : (int)s;
@@ -122,14 +122,15 @@ int hgemm_pick_tile(int M, int N, int K, int cus, bool operands_ok) {
   if (tuned_config(1, M, N, K, &tuned_tile, &tuned_splits) && tuned_tile >= 0 &&
       tuned_tile < kHgemmTileCount)
     return tuned_tile;
-  // Built-in rule: whole 256x256 tiles take the direct-to-LDS kernel; other
-  // shapes the register-staged kernel with the largest tile that still fills
-  // the device.
+  // Built-in rule (from the size sweep): 256x256 tiles once they give every CU
+  // one and K is at least 512 (the direct-to-LDS kernel when the shape and
+  // operands allow it); 128x128 tiles once they give every CU two; else 64x64
+  // tiles, which spread small outputs over the most CUs.
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
-  if (M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && operands_ok) return 3;
-  if (t_large >= cus) return 0;
-  if (t_med >= cus / 2) return 1;
+  if (t_large >= cus && K >= 512)
+    return (M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && operands_ok) ? 3 : 0;
+  if (t_med >= 2L * cus) return 1;
   return 2;
 }
 

@@ -327,13 +327,17 @@ struct HDmaTile {
   static_assert(FM * FN * 16 <= 256 / WAVES_PER_SIMD, "accumulators must leave room for operands");
 };
 
-// Chunk permutation of A row r in LDS.  A fragment read takes one chunk from 32
-// consecutive rows; rows are 64 bytes apart, so without the permutation rows r
-// and r + 4 would hit the same banks.  With it, any 8 (or 16) consecutive rows
-// land on distinct 16-byte bank groups of a 128-byte (or 256-byte) LDS cycle.
+// Chunk permutation of A row r in LDS.  A fragment read takes the same chunk
+// from 32 consecutive rows; rows are 64 bytes apart, so four rows fill one
+// 256-byte line of the 64 banks, and without a permutation rows r, r + 4, r + 8
+// ... would all hit the same 16-byte bank group (a 4-way conflict).  Permuting
+// the chunks by (r / 4) % 4 gives the rows of four consecutive lines four
+// different groups.  Measured on gfx950 with SQ_LDS_BANK_CONFLICT: this form is
+// conflict-free (4 LDS cycles per 16-byte read of a wave), while a permutation
+// by ((r / 2) ^ (r / 8)) % 4 still costs 8 cycles.
 template <class T>
 __device__ __forceinline__ int a_swizzle(int r) {
-  return ((r >> 1) ^ (r >> 3)) & (T::A_CHUNKS_PER_ROW - 1);
+  return (r >> 2) & (T::A_CHUNKS_PER_ROW - 1);
 }
 
 template <int N>
@@ -621,9 +625,11 @@ hgemm_dma_kernel(HgemmArgs p) {
 template <class E> using HTileLarge = HgemmTile<E, 256, 256, 64, 2, 2>;
 template <class E> using HTileMedium = HgemmTile<E, 128, 128, 64, 2, 2>;
 template <class E> using HTileSmall = HgemmTile<E, 64, 64, 64, 2, 2>;
-// direct-to-LDS: 4 stages x 32 KiB, one workgroup per CU / 3 stages x 24 KiB, two per CU
+// direct-to-LDS: 4 stages x 32 KiB, one workgroup per CU / 3 stages x 24 KiB, two per CU /
+// 5 stages x 32 KiB (all 160 KiB of LDS, three K tiles in flight while one is consumed)
 template <class E> using HDmaLarge = HDmaTile<E, 256, 256, 32, 4>;
 template <class E> using HDmaTall = HDmaTile<E, 128, 256, 32, 3, 2>;
+template <class E> using HDmaDeep = HDmaTile<E, 256, 256, 32, 5>;
 
 template <class T>
 static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s) {
@@ -673,13 +679,16 @@ static hipError_t launch_hdma(const HgemmCall& c, int group_m, hipStream_t s) {
 
 static_assert(HDmaLarge<EltF16>::BM == 256 && HDmaLarge<EltF16>::BN == 256 &&
                   HDmaTall<EltF16>::BM == 128 && HDmaTall<EltF16>::BN == 256 &&
-                  2 * HDmaLarge<EltF16>::BK == 64 && 2 * HDmaTall<EltF16>::BK == 64,
+                  HDmaDeep<EltF16>::BM == 256 && HDmaDeep<EltF16>::BN == 256 &&
+                  2 * HDmaLarge<EltF16>::BK == 64 && 2 * HDmaTall<EltF16>::BK == 64 &&
+                  2 * HDmaDeep<EltF16>::BK == 64,
               "hgemm_resolve_tile's shape conditions must match the direct-to-LDS tiles");
 
 int hgemm_resolve_tile(int tile, int M, int N, int K, bool operands_ok) {
   // The direct-to-LDS kernels need whole tiles and K a multiple of 64;
   // otherwise the register-staged 256x256 kernel, which handles every shape, runs.
-  if (tile == 3 && !(operands_ok && M % 256 == 0 && N % 256 == 0 && K % 64 == 0)) return 0;
+  if ((tile == 3 || tile == 5) && !(operands_ok && M % 256 == 0 && N % 256 == 0 && K % 64 == 0))
+    return 0;
   if (tile == 4 && !(operands_ok && M % 128 == 0 && N % 256 == 0 && K % 64 == 0)) return 0;
   return tile;
 }
@@ -701,6 +710,9 @@ static hipError_t launch_half(const HgemmCall& c, int cus, int force_tile, hipSt
     case 4:
       if (!dma_fits<HDmaTall<E>>(c)) return hipErrorInvalidValue;
       return launch_hdma<HDmaTall<E>>(c, 8, s);
+    case 5:
+      if (!dma_fits<HDmaDeep<E>>(c)) return hipErrorInvalidValue;
+      return launch_hdma<HDmaDeep<E>>(c, 4, s);
     default: return hipErrorInvalidValue;
   }
 }

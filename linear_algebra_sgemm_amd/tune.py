@@ -31,6 +31,7 @@ from __future__ import annotations
 
 import argparse
 import datetime
+import json
 import os
 import statistics
 import sys
@@ -48,12 +49,12 @@ DEFAULT_REPORT = os.path.join(ROOT, "profiles", "size_sweep.md")
 
 OPS = {"sgemm": 0, "half": 1}
 SGEMM_TILES = (0, 1, 2, 3, 4)
-HALF_TILES = (0, 1, 2, 3, 4)
+HALF_TILES = (0, 1, 2, 3, 4, 5)
 SPLITS = (1, 2, 4, 8, 16, 32)
 TILE_NAMES = {
     0: {0: "256x256", 1: "128x128", 2: "64x64", 3: "256x256 (BK 32)", 4: "128x256 (2 WG/CU)"},
     1: {0: "256x256 reg", 1: "128x128 reg", 2: "64x64 reg", 3: "256x256 direct",
-        4: "128x256 direct"},
+        4: "128x256 direct", 5: "256x256 direct, 5 stages"},
 }
 
 
@@ -255,6 +256,7 @@ def main(argv=None):
     ap.add_argument("--margin", type=float, default=0.03)
     ap.add_argument("--table", default=DEFAULT_TABLE)
     ap.add_argument("--report", default=DEFAULT_REPORT)
+    ap.add_argument("--dump", default=None, help="also write every timing as JSON here")
     args = ap.parse_args(argv)
     if not torch.cuda.is_available():
         sys.exit("the tuner times kernels and needs a GPU")
@@ -285,6 +287,13 @@ def main(argv=None):
     for p in (args.table, args.report):
         d = os.path.dirname(os.path.abspath(p))
         os.makedirs(d, exist_ok=True)
+    if args.dump:
+        dump = {str(op): {"%d,%d,%d" % k: {"rule": list(rule[k]),
+                                            "ms": {"%d,%d" % cfg: ms for cfg, ms in times.items()}}
+                          for k, times in results.items()}
+                for op, (results, rule, _) in all_results.items()}
+        with open(args.dump, "w") as f:
+            json.dump(dump, f)
     write_table(args.table, entries, header)
     write_report(args.report, all_results, header, command, args.margin)
     log("wrote %s (%d entries) and %s" % (args.table, len(entries), args.report))

@@ -148,15 +148,19 @@ def test_config_rule(so):
     cases = [
         (0, 4096, 4096, 4096, 256, (4, 1)),
         (0, 8192, 8192, 8192, 256, (4, 1)),
-        (0, 256, 256, 256, 256, (2, 4)),      # 16 tiles; >= 4 K tiles per chunk
-        (0, 512, 512, 512, 256, (2, 4)),      # 64 tiles; 256 / 64 = 4 chunks
+        (0, 256, 256, 256, 256, (2, 1)),      # K < 512: no split
+        (0, 256, 256, 1024, 256, (2, 8)),     # 16 tiles; chunks of 128
+        (0, 512, 512, 512, 256, (2, 4)),      # 64 tiles; chunks of 128
         (0, 1000, 3000, 777, 256, (2, 1)),    # 752 tiles
         (0, 2048, 2048, 2048, 256, (2, 1)),
         (0, 4096, 4096, 4096, 64, (4, 1)),
-        (0, 128, 128, 16384, 256, (2, 32)),   # 4 tiles; 64 chunks by CUs, capped at 32
+        (0, 128, 128, 16384, 256, (2, 32)),   # 4 tiles; 256 chunks by CUs, capped at 32
+        (0, 1024, 1024, 4096, 256, (2, 1)),   # 256 tiles of 64x64 cover the CUs
         (1, 4096, 14336, 4096, 256, (3, 1)),  # whole 256-tiles: direct-to-LDS kernel
         (1, 4096, 4000, 4096, 256, (0, 1)),
-        (1, 2048, 2000, 4096, 256, (1, 1)),
+        (1, 2048, 2000, 4096, 256, (2, 1)),
+        (1, 4096, 2048, 4096, 256, (1, 1)),   # 512 tiles of 128x128
+        (1, 4096, 4096, 256, 256, (1, 1)),    # K < 512: not the 256x256 tiles
         (1, 300, 500, 4096, 256, (2, 1)),
     ]
     assert lib.gemm_debug_use_tuned_table(False) == lib.STATUS_SUCCESS
@@ -266,7 +270,8 @@ def test_forced_splits(so):
 
 def test_force_tile_values(so):
     assert lib.gemm_debug_force_tile(0, 5) == lib.STATUS_INVALID_VALUE
-    assert lib.gemm_debug_force_tile(1, 5) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(1, 6) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(1, 5) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(1, 3) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(1, -1) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(0, 4) == lib.STATUS_SUCCESS
