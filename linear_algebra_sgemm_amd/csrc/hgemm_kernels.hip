@@ -358,15 +358,18 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// One direct global -> LDS copy of 16 bytes per lane: lane l writes LDS bytes
-// [lds_base + 16 l, +16).  Written as inline assembly so that the compiler does
-// not add its own "wait for every LDS-bound load" before later LDS reads; the
-// kernel orders these copies itself with wait_vmcnt and lds_barrier.
+// One direct global -> LDS copy of 16 bytes per lane from address base + offset
+// (a wave-uniform 64-bit base in scalar registers and a per-lane 32-bit byte
+// offset: the instruction's saddr form, so the K loop only advances the scalar
+// base); lane l writes LDS bytes [lds_base + 16 l, +16).  Written as inline
+// assembly so that the compiler does not add its own "wait for every LDS-bound
+// load" before later LDS reads; the kernel orders these copies itself with
+// wait_vmcnt and the barriers.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // m0 is listed as clobbered on purpose
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds_base), "v"(src) : "memory", "m0");
+__device__ __forceinline__ void dma16_sbase(const void* base, uint32_t offset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_base), "v"(offset), "s"(base) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -405,15 +408,41 @@ __device__ __forceinline__ const uint16_t* hdma_source(const HgemmArgs& p, int m
   return p.B + (size_t)row * p.ldb + col;
 }
 
+// The direct loads of one K tile as (wave-uniform base, per-lane offset) pairs:
+// load v reads A at a_base(k0) + off[v] (v < A_PER_WAVE) or B at b_base(k0) +
+// off[v], with a_base(k0) = A + m0 lda + k0 and b_base(k0) = B + k0 ldb + n0
+// (elements).  The offsets do not depend on k0; they are the addresses of
+// hdma_source minus the base, in bytes.
 template <class T>
-__device__ __forceinline__ void hdma_issue_all(const HgemmArgs& p, int m0, int n0, int k0,
-                                               uint32_t stage_base, int wave, int lane) {
+struct HDmaOffsets {
+  uint32_t off[T::LOADS_PER_TILE];
+  __device__ __forceinline__ HDmaOffsets(const HgemmArgs& p, int wave, int lane) {
 #pragma unroll
-  for (int v = 0; v < T::LOADS_PER_TILE; ++v) {
-    uint32_t off;
-    const uint16_t* src = hdma_source<T>(p, m0, n0, k0, v, wave, lane, off);
-    dma16(src, stage_base + off);
+    for (int v = 0; v < T::LOADS_PER_TILE; ++v) {
+      uint32_t unused;
+      const uint16_t* src = hdma_source<T>(p, 0, 0, 0, v, wave, lane, unused);
+      const uint16_t* base = v < T::A_PER_WAVE ? p.A : p.B;
+      off[v] = (uint32_t)((src - base) * sizeof(uint16_t));
+    }
   }
+};
+
+template <class T>
+__device__ __forceinline__ uint32_t hdma_lds_slot(int v, int wave) {
+  if (v < T::A_PER_WAVE) return (wave * T::A_PER_WAVE + v) * 1024;
+  return T::A_BYTES + (wave * T::B_PER_WAVE + (v - T::A_PER_WAVE)) * 1024;
+}
+
+// Issue the direct loads of K tile `kt` into the stage at LDS byte address `stage`.
+template <class T>
+__device__ __forceinline__ void hdma_issue_tile(const HgemmArgs& p, const HDmaOffsets<T>& o,
+                                                const uint16_t* a_tile, const uint16_t* b_tile,
+                                                int kt, uint32_t stage, int wave) {
+  const uint16_t* a = a_tile + kt * T::BK;
+  const uint16_t* b = b_tile + (size_t)kt * T::BK * p.ldb;
+#pragma unroll
+  for (int v = 0; v < T::LOADS_PER_TILE; ++v)
+    dma16_sbase(v < T::A_PER_WAVE ? a : b, o.off[v], stage + hdma_lds_slot<T>(v, wave));
 }
 
 // MFMA operand fragments of one k step of one wave.
@@ -473,24 +502,29 @@ __device__ __forceinline__ void wait_tiles_in_flight(int ahead) {
 // fragments into y0 / y1, the wait for tile kt + 1 and the barrier, and the direct
 // loads of tile kt + STAGES - 1.  After the last tile the wait is for nothing, and
 // the reads hit a stage that is no longer used; their values are dropped.
-template <class T>
+// STEADY: the caller guarantees kt + STAGES - 1 < ktiles (the look-ahead tile
+// exists), so the wait depth is fixed and the loads are issued unconditionally.
+template <class T, bool STEADY>
 __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::FN][T::FM], int kt,
                                           int ktiles, HFrags<T>& x0, HFrags<T>& x1,
                                           HFrags<T>& y0, HFrags<T>& y1, const uint8_t* lds,
-                                          uint32_t lds_base, int m0, int n0, int wave, int wm,
-                                          int wn, int lane) {
+                                          uint32_t lds_base, const HDmaOffsets<T>& dma,
+                                          const uint16_t* a_tile, const uint16_t* b_tile,
+                                          int wave, int wm, int wn, int lane) {
   static_assert(T::KSTEPS == 2, "two k steps per tile");
   constexpr int NM = T::FM * T::FN;                  // MFMAs per k step
   constexpr int NR = T::FM + 2 * T::FN;              // LDS reads per k step
   constexpr int PRE = 2;                             // MFMAs issued before the barrier
   constexpr int R0 = (NR + NM - PRE - 1) / (NM - PRE);          // reads per MFMA, step 0
-  constexpr int TAIL = NM - T::LOADS_PER_TILE;                  // MFMAs after the direct loads
+  constexpr int TAIL = NM - T::LOADS_PER_TILE;                  // MFMAs before the direct loads
   static_assert(NM > PRE && TAIL >= 1 && T::LOADS_PER_TILE <= NM, "enough MFMAs to hide behind");
-  constexpr int R1 = (NR + TAIL - 1) / TAIL;                    // reads per MFMA, step 1 tail
+  constexpr int R1 = (NR + TAIL - 1) / TAIL;                    // reads per MFMA, step 1
   // Two MFMAs first, so the matrix unit has work queued while the waves meet.
   hmfma<T>(acc, x0, 0);
   hmfma<T>(acc, x0, 1);
-  {
+  if constexpr (STEADY) {
+    wait_vmcnt<(T::STAGES - 3) * T::LOADS_PER_TILE>();
+  } else {
     const int left = ktiles - 2 - kt;    // tiles after kt + 1 that may stay in flight
     wait_tiles_in_flight<T>(left < 0 ? 0 : (left < T::STAGES - 3 ? left : T::STAGES - 3));
   }
@@ -507,27 +541,51 @@ __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::F
     __builtin_amdgcn_sched_group_barrier(0x100, R0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // Step 1: direct loads of tile kt + STAGES - 1 after the first MFMAs, then the
-  // reads of the next tile's second k step after the rest.
-  const bool issue = kt + T::STAGES - 1 < ktiles;
-  const int k_issue = (kt + T::STAGES - 1) * T::BK;
-  const uint32_t st_issue = lds_base + ((kt + T::STAGES - 1) % T::STAGES) * T::STAGE_BYTES;
+  // Step 1: the reads of the next tile's second k step with the first MFMAs, then
+  // the direct loads of tile kt + STAGES - 1 with the rest.  Reading first leaves
+  // the last LDS reads of the tile several MFMAs before its end, so they have
+  // landed when the next tile waits for its fragments (the compiler's wait at the
+  // top of the K loop is for all of them).
+  const int kt_issue = kt + T::STAGES - 1;
+  const bool issue = STEADY || kt_issue < ktiles;
+  const uint32_t st_issue = lds_base + (kt_issue % T::STAGES) * T::STAGE_BYTES;
+  const uint16_t* a_issue = a_tile + kt_issue * T::BK;
+  const uint16_t* b_issue = b_tile + (size_t)kt_issue * T::BK * p.ldb;
+  if constexpr (2 * TAIL >= NR) {
+    hload_frags<T>(y1, next, 1, wm, wn, lane);
 #pragma unroll
-  for (int x = 0; x < T::LOADS_PER_TILE; ++x) {
-    hmfma<T>(acc, x1, x);
-    if (issue) {
-      uint32_t off;
-      const uint16_t* src = hdma_source<T>(p, m0, n0, k_issue, x, wave, lane, off);
-      dma16(src, st_issue + off);
+    for (int x = 0; x < TAIL; ++x) hmfma<T>(acc, x1, x);
+#pragma unroll
+    for (int x = 0; x < TAIL; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, R1, 1);
     }
-  }
-  hload_frags<T>(y1, next, 1, wm, wn, lane);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int x = T::LOADS_PER_TILE; x < NM; ++x) hmfma<T>(acc, x1, x);
+    for (int x = 0; x < T::LOADS_PER_TILE; ++x) {
+      hmfma<T>(acc, x1, TAIL + x);
+      if (issue)
+        dma16_sbase(x < T::A_PER_WAVE ? a_issue : b_issue, dma.off[x],
+                    st_issue + hdma_lds_slot<T>(x, wave));
+    }
+  } else {
+    // Few MFMAs per k step (the 128 x 256 tile): loads first, so the reads are
+    // not crowded into the last MFMAs' registers.
 #pragma unroll
-  for (int x = 0; x < TAIL; ++x) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, R1, 1);
+    for (int x = 0; x < T::LOADS_PER_TILE; ++x) {
+      hmfma<T>(acc, x1, x);
+      if (issue)
+        dma16_sbase(x < T::A_PER_WAVE ? a_issue : b_issue, dma.off[x],
+                    st_issue + hdma_lds_slot<T>(x, wave));
+    }
+    hload_frags<T>(y1, next, 1, wm, wn, lane);
+#pragma unroll
+    for (int x = T::LOADS_PER_TILE; x < NM; ++x) hmfma<T>(acc, x1, x);
+#pragma unroll
+    for (int x = 0; x < TAIL; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, R1, 1);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -568,21 +626,36 @@ hgemm_dma_kernel(HgemmArgs p) {
   // consumed in tile kt - 1), which the direct loads of tile kt + STAGES - 1
   // then refill.  K is a multiple of 2 BK, so the loop body covers two tiles.
   const int ktiles = p.K / T::BK;
+  // Wave-uniform tile bases (k = 0) and the per-lane offsets of the direct loads.
+  const uint16_t* a_tile = p.A + (size_t)m0 * p.lda;
+  const uint16_t* b_tile = p.B + n0;
+  const HDmaOffsets<T> dma(p, wave, lane);
   HFrags<T> f0, f1, f2, f3;
   if (ktiles > 0) {
 #pragma unroll
     for (int st = 0; st < T::STAGES - 1; ++st)
-      if (st < ktiles) hdma_issue_all<T>(p, m0, n0, st * T::BK, lds_base + st * T::STAGE_BYTES,
-                                         wave, lane);
+      if (st < ktiles) hdma_issue_tile<T>(p, dma, a_tile, b_tile, st, lds_base + st * T::STAGE_BYTES,
+                                          wave);
     wait_tiles_in_flight<T>(ktiles - 1 < T::STAGES - 2 ? ktiles - 1 : T::STAGES - 2);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     hload_frags<T>(f0, lds, 0, wm, wn, lane);
     hload_frags<T>(f1, lds, 1, wm, wn, lane);
   }
-  for (int kt = 0; kt < ktiles; kt += 2) {
-    hdma_tile<T>(p, acc, kt, ktiles, f0, f1, f2, f3, lds, lds_base, m0, n0, wave, wm, wn, lane);
-    hdma_tile<T>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, m0, n0, wave, wm, wn, lane);
+  int kt = 0;
+  // Steady state: both tiles of the pair have their look-ahead tile to load.
+  for (; kt + T::STAGES < ktiles; kt += 2) {
+    hdma_tile<T, true>(p, acc, kt, ktiles, f0, f1, f2, f3, lds, lds_base, dma, a_tile, b_tile,
+                       wave, wm, wn, lane);
+    hdma_tile<T, true>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, dma, a_tile, b_tile,
+                       wave, wm, wn, lane);
+  }
+  // Drain: the last STAGES (or fewer) tiles, loads and waits decided per tile.
+  for (; kt < ktiles; kt += 2) {
+    hdma_tile<T, false>(p, acc, kt, ktiles, f0, f1, f2, f3, lds, lds_base, dma, a_tile, b_tile,
+                        wave, wm, wn, lane);
+    hdma_tile<T, false>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, dma, a_tile,
+                        b_tile, wave, wm, wn, lane);
   }
 
   // Epilogue.  Lane l holds, for n-block j, m-block i and q = 0..3, the four
@@ -658,7 +731,9 @@ template <class T>
 static bool dma_fits(const HgemmCall& c) {
   return c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % (2 * T::BK) == 0 && c.lda % 8 == 0 &&
          c.ldb % 8 == 0 && (reinterpret_cast<uintptr_t>(c.A) & 15u) == 0 &&
-         (reinterpret_cast<uintptr_t>(c.B) & 15u) == 0;
+         (reinterpret_cast<uintptr_t>(c.B) & 15u) == 0 &&
+         (int64_t)c.lda * T::BM * 2 < (int64_t(1) << 31) &&
+         (int64_t)c.ldb * T::BK * 2 < (int64_t(1) << 31);
 }
 
 template <class T>
@@ -695,9 +770,13 @@ int hgemm_resolve_tile(int tile, int M, int N, int K, bool operands_ok) {
 
 template <class E>
 static hipError_t launch_half(const HgemmCall& c, int cus, int force_tile, hipStream_t s) {
+  // The direct loads address A and B as a tile base plus a 32-bit byte offset
+  // of at most 256 rows of A or 32 rows of B.
   const bool operands_ok = c.lda % 8 == 0 && c.ldb % 8 == 0 &&
                            (reinterpret_cast<uintptr_t>(c.A) & 15u) == 0 &&
-                           (reinterpret_cast<uintptr_t>(c.B) & 15u) == 0;
+                           (reinterpret_cast<uintptr_t>(c.B) & 15u) == 0 &&
+                           (int64_t)c.lda * 256 * 2 < (int64_t(1) << 31) &&
+                           (int64_t)c.ldb * 32 * 2 < (int64_t(1) << 31);
   int tile = force_tile >= 0 ? force_tile : hgemm_pick_tile(c.M, c.N, c.K, cus, operands_ok);
   tile = hgemm_resolve_tile(tile, c.M, c.N, c.K, operands_ok);
   switch (tile) {
