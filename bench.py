@@ -186,7 +186,10 @@ def main():
         if splits > 1:
             kernel_name += ", split-K x%d + sgemm_splitk_reduce_kernel (timed together)" % splits
     else:
-        kernel_name = "hgemm_dma_kernel (256x256, direct-to-LDS, %s)" % dtype
+        tile, _ = lib.gemm_debug_pick_config(
+            1, M, N, K, torch.cuda.get_device_properties(0).multi_processor_count)
+        kernel_name = "%s, %s, tile config %d" % (
+            "hgemm_dma_kernel" if tile >= 3 else "hgemm_mfma_kernel", dtype, tile)
     line = {
         "metric": METRIC,
         "value": round(tflops, 3),

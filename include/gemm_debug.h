@@ -18,8 +18,9 @@ extern "C" {
  * largest tile, 1 = medium, 2 = small; sgemm also has 3 = largest tile with a
  * K step of 32 and 4 = 128 x 256 tiles at two workgroups per compute unit; the
  * half products also have 3 = 256 x 256 and 4 = 128 x 256 direct-to-LDS kernels
- * and 5 = the 256 x 256 one with a five-stage pipeline (whole tiles only, else
- * the 256 x 256 register-staged kernel).
+ * 5 = the 256 x 256 one with a five-stage pipeline and 6 = the 256 x 256 one
+ * with eight waves (whole tiles only, else the 256 x 256 register-staged
+ * kernel).
  * Whether the aligned fast path or the
  * bounds-checked path runs still follows the shape and alignment.  Returns
  * GEMM_STATUS_INVALID_VALUE for an unknown op or tile.  Pure host state: no

@@ -36,10 +36,11 @@ struct HgemmCall {
 // 3 = 256x256 with K step 32, 4 = 128x256 at two workgroups per CU.
 // HGEMM: 0 = 256x256, 1 = 128x128, 2 = 64x64 (register-staged, K step 64),
 // 3 = 256x256 direct-to-LDS, 4 stages of K step 32, 4 = 128x256 direct-to-LDS,
-// 3 stages, two workgroups per CU, 5 = 256x256 direct-to-LDS, 5 stages (3, 4 and 5
-// need whole tiles and K a multiple of 64; other shapes fall back to 0).
+// 3 stages, two workgroups per CU, 5 = 256x256 direct-to-LDS, 5 stages, 6 = 256x256
+// direct-to-LDS with eight waves (3 to 6 need whole tiles and K a multiple of 64;
+// other shapes fall back to 0).
 constexpr int kSgemmTileCount = 5;
-constexpr int kHgemmTileCount = 6;
+constexpr int kHgemmTileCount = 7;
 
 // K step of each SGEMM tile configuration (checked against the kernels).
 constexpr int sgemm_tile_bk(int tile) { return tile == 3 ? 32 : 16; }

@@ -298,12 +298,13 @@ __global__ void __launch_bounds__(T::THREADS) hgemm_mfma_kernel(HgemmArgs p) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-template <class E_, int BM_, int BN_, int BK_, int STAGES_, int WAVES_PER_SIMD_ = 1>
+template <class E_, int BM_, int BN_, int BK_, int STAGES_, int WAVES_PER_SIMD_ = 1,
+          int WAVES_M_ = 2, int WAVES_N_ = 2>
 struct HDmaTile {
   using E = E_;
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
-  static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;   // workgroups sharing one CU
-  static constexpr int WAVES_M = 2, WAVES_N = 2, WAVES = 4;
+  static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;   // waves sharing one SIMD
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -703,6 +704,9 @@ template <class E> using HTileSmall = HgemmTile<E, 64, 64, 64, 2, 2>;
 template <class E> using HDmaLarge = HDmaTile<E, 256, 256, 32, 4>;
 template <class E> using HDmaTall = HDmaTile<E, 128, 256, 32, 3, 2>;
 template <class E> using HDmaDeep = HDmaTile<E, 256, 256, 32, 5>;
+// 256 x 256 with eight waves (2 x 4, each 128 x 64), two per SIMD: while one
+// wave waits on its LDS reads or the barrier, the other can issue MFMAs.
+template <class E> using HDmaEight = HDmaTile<E, 256, 256, 32, 4, 2, 2, 4>;
 
 template <class T>
 static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s) {
@@ -755,6 +759,8 @@ static hipError_t launch_hdma(const HgemmCall& c, int group_m, hipStream_t s) {
 static_assert(HDmaLarge<EltF16>::BM == 256 && HDmaLarge<EltF16>::BN == 256 &&
                   HDmaTall<EltF16>::BM == 128 && HDmaTall<EltF16>::BN == 256 &&
                   HDmaDeep<EltF16>::BM == 256 && HDmaDeep<EltF16>::BN == 256 &&
+                  HDmaEight<EltF16>::BM == 256 && HDmaEight<EltF16>::BN == 256 &&
+                  2 * HDmaEight<EltF16>::BK == 64 &&
                   2 * HDmaLarge<EltF16>::BK == 64 && 2 * HDmaTall<EltF16>::BK == 64 &&
                   2 * HDmaDeep<EltF16>::BK == 64,
               "hgemm_resolve_tile's shape conditions must match the direct-to-LDS tiles");
@@ -762,7 +768,8 @@ static_assert(HDmaLarge<EltF16>::BM == 256 && HDmaLarge<EltF16>::BN == 256 &&
 int hgemm_resolve_tile(int tile, int M, int N, int K, bool operands_ok) {
   // The direct-to-LDS kernels need whole tiles and K a multiple of 64;
   // otherwise the register-staged 256x256 kernel, which handles every shape, runs.
-  if ((tile == 3 || tile == 5) && !(operands_ok && M % 256 == 0 && N % 256 == 0 && K % 64 == 0))
+  if ((tile == 3 || tile == 5 || tile == 6) &&
+      !(operands_ok && M % 256 == 0 && N % 256 == 0 && K % 64 == 0))
     return 0;
   if (tile == 4 && !(operands_ok && M % 128 == 0 && N % 256 == 0 && K % 64 == 0)) return 0;
   return tile;
@@ -792,6 +799,9 @@ static hipError_t launch_half(const HgemmCall& c, int cus, int force_tile, hipSt
     case 5:
       if (!dma_fits<HDmaDeep<E>>(c)) return hipErrorInvalidValue;
       return launch_hdma<HDmaDeep<E>>(c, 4, s);
+    case 6:
+      if (!dma_fits<HDmaEight<E>>(c)) return hipErrorInvalidValue;
+      return launch_hdma<HDmaEight<E>>(c, 4, s);
     default: return hipErrorInvalidValue;
   }
 }

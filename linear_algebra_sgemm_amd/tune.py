@@ -4,7 +4,8 @@
         [--max-class 13] [--table PATH] [--report PATH] [--margin 0.03]
 
 For every size class (M, N, K) = (2^a, 2^b, 2^c), a, b, c in [min, max], and
-each op, every legal configuration is timed: each (tile, split count) pair is
+each op (plus the --extra shapes whose class lies outside that cube, timed at
+their own sizes), every legal configuration is timed: each (tile, split count) pair is
 forced through the test hooks, the library reports what it would actually run
 for the shape (split counts reduced to what K and the workspace allow, direct-
 to-LDS tiles replaced where the shape does not suit them) and each distinct
@@ -49,12 +50,12 @@ DEFAULT_REPORT = os.path.join(ROOT, "profiles", "size_sweep.md")
 
 OPS = {"sgemm": 0, "half": 1}
 SGEMM_TILES = (0, 1, 2, 3, 4)
-HALF_TILES = (0, 1, 2, 3, 4, 5)
+HALF_TILES = (0, 1, 2, 3, 4, 5, 6)
 SPLITS = (1, 2, 4, 8, 16, 32)
 TILE_NAMES = {
     0: {0: "256x256", 1: "128x128", 2: "64x64", 3: "256x256 (BK 32)", 4: "128x256 (2 WG/CU)"},
     1: {0: "256x256 reg", 1: "128x128 reg", 2: "64x64 reg", 3: "256x256 direct",
-        4: "128x256 direct", 5: "256x256 direct, 5 stages"},
+        4: "128x256 direct", 5: "256x256 direct, 5 stages", 6: "256x256 direct, 8 waves"},
 }
 
 
@@ -152,37 +153,55 @@ def unforce(op):
         lib.gemm_debug_force_splits(0, -1)
 
 
-def tune_op(op, lo, hi, margin, cus, dev, log, busy):
+def size_class(x):
+    """The library's size class of a dimension: log2 rounded, clamped to 7..14."""
+    import math
+    c = round(math.log2(x)) if x > 1 else 7
+    return min(max(c, 7), 14)
+
+
+def tune_op(op, lo, hi, margin, cus, dev, log, busy, extra=()):
+    """Time every class of the cube [lo, hi]^3 (aligned power-of-two shapes) and the
+    extra shapes whose class lies outside it (timed at their own sizes)."""
     buf = Buffers(op, 1 << hi, dev)
-    results = {}      # (a, b, c) -> {cfg: ms}
-    rule = {}         # (a, b, c) -> cfg
+    results = {}      # class (a, b, c) -> {cfg: ms}
+    rule = {}         # class -> cfg
+    dims = {}         # class -> (M, N, K) that was timed
     entries = []
-    for a in range(lo, hi + 1):
-        for b in range(lo, hi + 1):
-            for c in range(lo, hi + 1):
-                M, N, K = 1 << a, 1 << b, 1 << c
-                fn = call_for(op, buf, M, N, K)
-                lib.gemm_debug_use_tuned_table(False)
-                base = lib.gemm_debug_pick_config(op, M, N, K, cus)
-                times = {}
-                for cfg in candidates(op, M, N, K, cus):
-                    force(op, cfg)
-                    try:
-                        times[cfg] = timed(fn, busy)
-                    finally:
-                        unforce(op)
-                lib.gemm_debug_use_tuned_table(True)
-                results[(a, b, c)] = times
-                rule[(a, b, c)] = base
-                best = min(times, key=times.get)
-                gain = times[base] / times[best] - 1.0
-                if best != base and times[best] < times[base] * (1.0 - margin):
-                    entries.append((op, a, b, c, best[0], best[1], times[base], times[best]))
-                log("op %d %5d x %5d x %5d  rule %s %.4f ms  best %s %.4f ms  (%+.1f%%)"
-                    % (op, M, N, K, base, times[base], best, times[best], 100 * gain))
+    shapes = [(1 << a, 1 << b, 1 << c) for a in range(lo, hi + 1) for b in range(lo, hi + 1)
+              for c in range(lo, hi + 1)]
+    for (M, N, K) in extra:
+        key = (size_class(M), size_class(N), size_class(K))
+        if all(lo <= k <= hi for k in key):
+            continue
+        if (M * K > buf.A.numel()) or (K * N > buf.B.numel()) or (M * N > buf.C.numel()):
+            raise ValueError("extra shape %dx%dx%d does not fit the %d^2 buffers" % (M, N, K, 1 << hi))
+        shapes.append((M, N, K))
+    for (M, N, K) in shapes:
+        key = (size_class(M), size_class(N), size_class(K))
+        fn = call_for(op, buf, M, N, K)
+        lib.gemm_debug_use_tuned_table(False)
+        base = lib.gemm_debug_pick_config(op, M, N, K, cus)
+        times = {}
+        for cfg in candidates(op, M, N, K, cus):
+            force(op, cfg)
+            try:
+                times[cfg] = timed(fn, busy)
+            finally:
+                unforce(op)
+        lib.gemm_debug_use_tuned_table(True)
+        results[key] = times
+        rule[key] = base
+        dims[key] = (M, N, K)
+        best = min(times, key=times.get)
+        gain = times[base] / times[best] - 1.0
+        if best != base and times[best] < times[base] * (1.0 - margin):
+            entries.append((op,) + key + (best[0], best[1], times[base], times[best]))
+        log("op %d %5d x %5d x %5d  rule %s %.4f ms  best %s %.4f ms  (%+.1f%%)"
+            % (op, M, N, K, base, times[base], best, times[best], 100 * gain))
     del buf
     torch.cuda.empty_cache()
-    return results, rule, entries
+    return results, rule, entries, dims
 
 
 def write_table(path, entries, header):
@@ -197,8 +216,9 @@ def write_table(path, entries, header):
         f.write("\n".join(lines) + "\n")
 
 
-def flops(a, b, c):
-    return 2.0 * (1 << a) * (1 << b) * (1 << c)
+def flops(dims):
+    M, N, K = dims
+    return 2.0 * M * N * K
 
 
 def write_report(path, all_results, header, command, margin):
@@ -210,7 +230,7 @@ def write_report(path, all_results, header, command, margin):
            "batches). FP32: α = 1, β = 0.5. Half: fp16, bias + GELU(tanh). "
            "A class enters the tuned table when its best configuration beats the built-in rule "
            "by more than %.0f %%." % (100 * margin), ""]
-    for op, (results, rule, entries) in all_results.items():
+    for op, (results, rule, entries, dims) in all_results.items():
         name = "FP32 sgemm" if op == 0 else "FP16 bias + GELU (the BF16 product runs the same kernels)"
         squares = sorted(k for k in results if k[0] == k[1] == k[2])
         out += ["## %s: square sizes" % name, ""]
@@ -223,22 +243,32 @@ def write_report(path, all_results, header, command, margin):
             row = []
             for k in squares:
                 ms = results[k].get(cfg)
-                row.append("%.1f" % (flops(*k) / ms / 1e9) if ms else "—")
+                row.append("%.1f" % (flops(dims[k]) / ms / 1e9) if ms else "—")
             out.append("| tile %d %s | " % (cfg[0], TILE_NAMES[op][cfg[0]]) + " | ".join(row) + " |")
         for label, choose in (("built-in rule", lambda k: rule[k]),
                               ("best (any split)", lambda k: min(results[k], key=results[k].get))):
             row = []
             for k in squares:
                 cfg = choose(k)
-                row.append("%.1f %s" % (flops(*k) / results[k][cfg] / 1e9, _cfg_str(cfg)))
+                row.append("%.1f %s" % (flops(dims[k]) / results[k][cfg] / 1e9, _cfg_str(cfg)))
             out.append("| %s | " % label + " | ".join(row) + " |")
         out += ["", "## %s: tuned entries (%d of %d classes)" % (name, len(entries), len(results)),
                 "", "| M | N | K | rule | rule TFLOP/s | tuned | tuned TFLOP/s | gain |",
                 "|---|---|---|---|---|---|---|---|"]
         for (o, a, b, c, t, s, tb, tt) in sorted(entries, key=lambda e: e[6] / e[7], reverse=True):
+            d = dims[(a, b, c)]
             out.append("| %d | %d | %d | %s | %.1f | %s | %.1f | %+.1f %% |" % (
-                1 << a, 1 << b, 1 << c, _cfg_str(rule[(a, b, c)]), flops(a, b, c) / tb / 1e9,
-                _cfg_str((t, s)), flops(a, b, c) / tt / 1e9, 100 * (tb / tt - 1)))
+                d[0], d[1], d[2], _cfg_str(rule[(a, b, c)]), flops(d) / tb / 1e9,
+                _cfg_str((t, s)), flops(d) / tt / 1e9, 100 * (tb / tt - 1)))
+        extra_keys = [k for k in results if max(k) > max(squares)[0] or min(k) < min(squares)[0]]
+        if extra_keys:
+            out += ["", "## %s: extra shapes (size classes outside the cube)" % name, "",
+                    "| M | N | K | TFLOP/s per configuration | rule |", "|---|---|---|---|---|"]
+            for k in extra_keys:
+                d = dims[k]
+                cells = ", ".join("%s %.1f" % (_cfg_str(c), flops(d) / results[k][c] / 1e9)
+                                  for c in sorted(results[k]))
+                out.append("| %d | %d | %d | %s | %s |" % (d + (cells, _cfg_str(rule[k]))))
         out.append("")
     with open(path, "w") as f:
         f.write("\n".join(out) + "\n")
@@ -257,6 +287,9 @@ def main(argv=None):
     ap.add_argument("--table", default=DEFAULT_TABLE)
     ap.add_argument("--report", default=DEFAULT_REPORT)
     ap.add_argument("--dump", default=None, help="also write every timing as JSON here")
+    ap.add_argument("--extra", default="half:4096x14336x4096",
+                    help="comma-separated op:MxNxK shapes tuned at their own sizes when their "
+                         "size class lies outside the cube")
     args = ap.parse_args(argv)
     if not torch.cuda.is_available():
         sys.exit("the tuner times kernels and needs a GPU")
@@ -279,7 +312,10 @@ def main(argv=None):
         busy = make_busy(dev)
         for name in args.ops.split(","):
             op = OPS[name]
-            res = tune_op(op, args.min_class, args.max_class, args.margin, cus, dev, log, busy)
+            extra = [tuple(int(x) for x in e.split(":")[1].split("x"))
+                     for e in args.extra.split(",") if e and e.split(":")[0] == name]
+            res = tune_op(op, args.min_class, args.max_class, args.margin, cus, dev, log, busy,
+                          extra)
             all_results[op] = res
             entries += res[2]
     finally:
@@ -291,7 +327,7 @@ def main(argv=None):
         dump = {str(op): {"%d,%d,%d" % k: {"rule": list(rule[k]),
                                             "ms": {"%d,%d" % cfg: ms for cfg, ms in times.items()}}
                           for k, times in results.items()}
-                for op, (results, rule, _) in all_results.items()}
+                for op, (results, rule, _, _) in all_results.items()}
         with open(args.dump, "w") as f:
             json.dump(dump, f)
     write_table(args.table, entries, header)

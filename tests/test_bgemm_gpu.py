@@ -17,7 +17,7 @@ from tests.gpu_helpers import FP16_TOL, f16_bits, hgemm_error, note, run_hgemm
 
 pytestmark = pytest.mark.gpu
 
-TILES = (0, 1, 2, 3, 4, 5)
+TILES = (0, 1, 2, 3, 4, 5, 6)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -80,7 +80,7 @@ def test_padded_leading_dimensions():
                label="padded ld")
 
 
-@pytest.mark.parametrize("tile", [0, 3, 5])
+@pytest.mark.parametrize("tile", [0, 3, 5, 6])
 def test_exact_identity_and_permutation(tile, tile_forced):
     lib.gemm_debug_force_tile(1, tile)
     g = torch.Generator().manual_seed(19)

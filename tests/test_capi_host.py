@@ -270,7 +270,8 @@ def test_forced_splits(so):
 
 def test_force_tile_values(so):
     assert lib.gemm_debug_force_tile(0, 5) == lib.STATUS_INVALID_VALUE
-    assert lib.gemm_debug_force_tile(1, 6) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(1, 7) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(1, 6) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(1, 5) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(1, 3) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(1, -1) == lib.STATUS_SUCCESS
