@@ -43,14 +43,17 @@ int size_class(int x) {
 
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
-// Built-in tile rule, measured on MI355X: 128x256 tiles at two workgroups per
-// CU are fastest once they give every CU two tiles (4096^3: 133 vs 130
-// TFLOP/s for 256x256); below that, 128x128 if it still gives two tiles per
-// CU, else 64x64 tiles, which spread small outputs over more CUs (2048^3: 106
-// vs 104; 1000x3000x777: 51 vs 42).
-int sgemm_rule_tile(int M, int N, int cus) {
+// Built-in tile rule, measured on MI355X: the 256x256 direct-to-LDS tile once
+// whole tiles give every CU one (4096^3: 143 TFLOP/s, 8192^3: 145); 128x256
+// register-staged tiles at two workgroups per CU once they give every CU two
+// (4096^3: 134 vs 130 for 256x256); below that, 128x128 if it still gives two
+// tiles per CU, else 64x64 tiles, which spread small outputs over more CUs
+// (2048^3: 106 vs 104; 1000x3000x777: 51 vs 42).
+int sgemm_rule_tile(int M, int N, int K, int cus) {
+  const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_tall = ceil_div(M, 128) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
+  if (t_large >= cus && M % 256 == 0 && N % 256 == 0 && K % 32 == 0) return 7;
   if (t_tall >= 2L * cus) return 4;
   if (t_med >= 2L * cus) return 1;
   return 2;
@@ -92,7 +95,7 @@ SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_spl
   const bool tuned = tuned_config(0, M, N, K, &tuned_tile, &tuned_splits) &&
                      tuned_tile >= 0 && tuned_tile < kSgemmTileCount && tuned_splits >= 1;
   SgemmPlan p;
-  p.tile = force_tile >= 0 ? force_tile : tuned ? tuned_tile : sgemm_rule_tile(M, N, cus);
+  p.tile = force_tile >= 0 ? force_tile : tuned ? tuned_tile : sgemm_rule_tile(M, N, K, cus);
   long s = force_splits > 0 ? force_splits
            : (tuned && force_tile < 0) ? tuned_splits
                                        : sgemm_rule_splits(M, N, K, p.tile, cus);
@@ -114,6 +117,9 @@ SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_spl
   }
   p.splits = (int)s;
   p.k_chunk = (int)chunk;
+  // Report what runs for 16-byte-aligned operands (the launch resolves again
+  // with the actual operands).
+  p.tile = sgemm_resolve_tile(p.tile, M, N, K, p.splits, true);
   return p;
 }
 

@@ -29,13 +29,39 @@
 // (0..3) gives k-slot h the index 4h + s; a lane then finds its four A values
 // for steps 0..3 side by side in an LDS row and reads them with one 16-byte
 // load.
+#include "dma_common.h"
 #include "gemm_common.h"
 #include "gemm_launch.h"
 
 namespace lasg {
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int WAVES_PER_SIMD_ = 1>
+// The FP32 MFMA block shapes.  BLK x BLK outputs per instruction, KSLOTS k-slots
+// (lane / BLK selects the slot) of one k each; ACC accumulator registers per lane.
+// A group of 4 * KSLOTS consecutive k is consumed by four MFMA steps; step s and
+// slot h take k = 4 h + s of the group, so a lane's four A values of one group
+// are contiguous.
+struct MfmaF32x32 {   // v_mfma_f32_32x32x2_f32: 64 cycles, 16 accumulators per lane
+  static constexpr int BLK = 32, KSLOTS = 2, ACC = 16;
+  typedef f32x16 acc_t;
+  static __device__ __forceinline__ acc_t mfma(float a, float b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  // Row (within the block) of accumulator register r of lane `lane`; the column is lane % 32.
+  static __device__ __forceinline__ int row(int r, int lane) { return mfma32_row(r, lane); }
+};
+struct MfmaF16x16 {   // v_mfma_f32_16x16x4_f32: 32 cycles, 4 accumulators per lane
+  static constexpr int BLK = 16, KSLOTS = 4, ACC = 4;
+  typedef f32x4 acc_t;
+  static __device__ __forceinline__ acc_t mfma(float a, float b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int row(int r, int lane) { return 4 * (lane >> 4) + r; }
+};
+
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int WAVES_PER_SIMD_ = 1,
+          class MF_ = MfmaF32x32>
 struct SgemmTile {
+  using MF = MF_;
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   // Waves of this kernel that must fit on one SIMD at once (register budget:
@@ -44,23 +70,28 @@ struct SgemmTile {
   static constexpr int THREADS = WAVES_M * WAVES_N * kWave;
   static constexpr int WTM = BM / WAVES_M;     // wave sub-tile rows
   static constexpr int WTN = BN / WAVES_N;     // wave sub-tile columns
-  static constexpr int FM = WTM / 32;          // 32x32 MFMA blocks per wave, along M
-  static constexpr int FN = WTN / 32;          // ... along N
+  static constexpr int BLK = MF::BLK;
+  static constexpr int G = 4 * MF::KSLOTS;     // k per group of four MFMA steps
+  static constexpr int FM = WTM / BLK;         // MFMA blocks per wave, along M
+  static constexpr int FN = WTN / BLK;         // ... along N
   static constexpr int A_STRIDE = BK + 4;      // floats per LDS row of the A tile (one row = one m)
-  static constexpr int B_STRIDE = BN + 8;      // floats per LDS row of the B tile (one row = one k)
+  // floats per LDS row of the B tile (one row = one k): the k-slots of one B read
+  // are 4 rows apart, so 4 B_STRIDE must spread them over the 64 banks.
+  static constexpr int B_STRIDE = BN + (MF::KSLOTS == 4 ? 4 : 8);
   static constexpr int A_STAGE = BM * A_STRIDE;
   static constexpr int B_STAGE = BK * B_STRIDE;
   static constexpr int LDS_FLOATS = 2 * (A_STAGE + B_STAGE);
   static constexpr int A_VECS = BM * BK / 4 / THREADS;   // float4 loads per thread per K tile
   static constexpr int B_VECS = BK * BN / 4 / THREADS;
 
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 MFMA blocks");
-  static_assert(BK % 8 == 0, "K tile is consumed in groups of 8");
+  static_assert(WTM % BLK == 0 && WTN % BLK == 0, "wave tile must be whole MFMA blocks");
+  static_assert(BK % G == 0, "K tile is consumed in whole groups");
   static_assert((BM * BK / 4) % THREADS == 0, "A tile must split evenly into float4 loads");
   static_assert((BK * BN / 4) % THREADS == 0, "B tile must split evenly into float4 loads");
   static_assert(THREADS % (BK / 4) == 0 && THREADS % (BN / 4) == 0, "load rows must not wrap");
   static_assert(LDS_FLOATS * 4 <= 160 * 1024, "two stages must fit gfx950's 160 KiB of LDS");
-  static_assert(FM * FN * 16 <= 256 / WAVES_PER_SIMD, "accumulators must leave room for operands");
+  static_assert(FM * FN * MF::ACC <= 256 / WAVES_PER_SIMD,
+                "accumulators must leave room for operands");
 };
 
 struct SgemmArgs {
@@ -140,6 +171,46 @@ struct Stage {
   }
 };
 
+// Epilogue of one wave: C = alpha * acc + beta * C over the wave's WTM x WTN
+// sub-tile at (r0, c0), C read only when beta != 0.  For each row of blocks, all
+// C loads are issued before the first one is consumed, so their latencies
+// overlap instead of adding up.
+template <class T, bool EDGE, class ACC>
+__device__ __forceinline__ void sgemm_store(const SgemmArgs& p, const ACC& acc, int r0, int c0,
+                                            int lane) {
+  using MF = typename T::MF;
+  const int lb = lane % T::BLK;
+  const float alpha = p.alpha, beta = p.beta;
+  const bool read_c = beta != 0.0f;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    float cv[T::FN][MF::ACC];
+    if (read_c) {
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) {
+        const int col = c0 + j * T::BLK + lb;
+#pragma unroll
+        for (int r = 0; r < MF::ACC; ++r) {
+          const int row = r0 + i * T::BLK + MF::row(r, lane);
+          const bool ok = !EDGE || (row < p.M && col < p.N);
+          cv[j][r] = ok ? p.C[(size_t)row * p.ldc + col] : 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+      const int col = c0 + j * T::BLK + lb;
+#pragma unroll
+      for (int r = 0; r < MF::ACC; ++r) {
+        const int row = r0 + i * T::BLK + MF::row(r, lane);
+        if (EDGE && (row >= p.M || col >= p.N)) continue;
+        const float v = alpha * acc[i][j][r];
+        p.C[(size_t)row * p.ldc + col] = read_c ? __builtin_fmaf(beta, cv[j][r], v) : v;
+      }
+    }
+  }
+}
+
 template <class T, bool EDGE, bool SPLIT>
 __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(T::WAVES_PER_SIMD)))
 sgemm_mfma_kernel(SgemmArgs p) {
@@ -168,16 +239,17 @@ sgemm_mfma_kernel(SgemmArgs p) {
   const int wave = tid / kWave;
   const int wm = wave / T::WAVES_N;
   const int wn = wave % T::WAVES_N;
-  const int l32 = lane % 32;
-  const int half = lane / 32;
+  using MF = typename T::MF;
+  const int lb = lane % T::BLK;       // row of A / column of B within a block
+  const int slot = lane / T::BLK;     // k-slot
 
-  f32x16 acc[T::FM][T::FN];
+  typename MF::acc_t acc[T::FM][T::FN];
 #pragma unroll
   for (int i = 0; i < T::FM; ++i)
 #pragma unroll
     for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < MF::ACC; ++r) acc[i][j][r] = 0.0f;
 
   const int ktiles = (p.K + T::BK - 1) / T::BK;
   Stage<T, EDGE> st;
@@ -188,8 +260,8 @@ sgemm_mfma_kernel(SgemmArgs p) {
   __syncthreads();
 
   // Per-lane fragment origins inside one LDS stage.
-  const int a_off = (wm * T::WTM + l32) * T::A_STRIDE + 4 * half;
-  const int b_off = (4 * half) * T::B_STRIDE + wn * T::WTN + l32;
+  const int a_off = (wm * T::WTM + lb) * T::A_STRIDE + 4 * slot;
+  const int b_off = (4 * slot) * T::B_STRIDE + wn * T::WTN + lb;
 
   for (int kt = 0; kt < ktiles; ++kt) {
     const bool odd = kt & 1;
@@ -199,21 +271,21 @@ sgemm_mfma_kernel(SgemmArgs p) {
     if (more) st.load(p, m0, n0, (kt + 1) * T::BK, tid);
 
 #pragma unroll
-    for (int g = 0; g < T::BK / 8; ++g) {
+    for (int g = 0; g < T::BK / T::G; ++g) {
       f32x4 af[T::FM];
 #pragma unroll
       for (int i = 0; i < T::FM; ++i)
-        af[i] = *reinterpret_cast<const f32x4*>(As + a_off + i * 32 * T::A_STRIDE + 8 * g);
+        af[i] = *reinterpret_cast<const f32x4*>(As + a_off + i * T::BLK * T::A_STRIDE + T::G * g);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         float bf[T::FN];
 #pragma unroll
-        for (int j = 0; j < T::FN; ++j) bf[j] = Bs[b_off + (8 * g + s) * T::B_STRIDE + j * 32];
+        for (int j = 0; j < T::FN; ++j)
+          bf[j] = Bs[b_off + (T::G * g + s) * T::B_STRIDE + j * T::BLK];
 #pragma unroll
         for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-          for (int j = 0; j < T::FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][s], bf[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < T::FN; ++j) acc[i][j] = MF::mfma(af[i][s], bf[j], acc[i][j]);
       }
     }
 
@@ -228,10 +300,10 @@ sgemm_mfma_kernel(SgemmArgs p) {
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
       for (int j = 0; j < T::FN; ++j) {
-        const int col = n0 + wn * T::WTN + j * 32 + l32;
+        const int col = n0 + wn * T::WTN + j * T::BLK + lb;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * T::WTM + i * 32 + mfma32_row(r, lane);
+        for (int r = 0; r < MF::ACC; ++r) {
+          const int row = m0 + wm * T::WTM + i * T::BLK + MF::row(r, lane);
           if (EDGE && (row >= p.M || col >= p.N)) continue;
           W[(size_t)row * p.N + col] = acc[i][j][r];
         }
@@ -239,38 +311,7 @@ sgemm_mfma_kernel(SgemmArgs p) {
     return;
   }
 
-  // Epilogue: C = alpha * acc + beta * C, C read only when beta != 0.  For each
-  // row of blocks, all C loads are issued before the first one is consumed, so
-  // their latencies overlap instead of adding up.
-  const float alpha = p.alpha, beta = p.beta;
-  const bool read_c = beta != 0.0f;
-#pragma unroll
-  for (int i = 0; i < T::FM; ++i) {
-    float cv[T::FN][16];
-    if (read_c) {
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
-        const int col = n0 + wn * T::WTN + j * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * T::WTM + i * 32 + mfma32_row(r, lane);
-          const bool ok = !EDGE || (row < p.M && col < p.N);
-          cv[j][r] = ok ? p.C[(size_t)row * p.ldc + col] : 0.0f;
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) {
-      const int col = n0 + wn * T::WTN + j * 32 + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * T::WTM + i * 32 + mfma32_row(r, lane);
-        if (EDGE && (row >= p.M || col >= p.N)) continue;
-        const float v = alpha * acc[i][j][r];
-        p.C[(size_t)row * p.ldc + col] = read_c ? __builtin_fmaf(beta, cv[j][r], v) : v;
-      }
-    }
-  }
+  sgemm_store<T, EDGE>(p, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
 }
 
 // C = beta * C (C = 0 when beta == 0, without reading C): the alpha == 0 / K == 0 case.
@@ -283,6 +324,258 @@ __global__ void __launch_bounds__(256) sgemm_scale_kernel(int M, int N, float be
     float* dst = C + i * ldc + j;
     *dst = (beta != 0.0f) ? beta * *dst : 0.0f;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant for whole tiles (M % BM == N % BN == 0, K % 32 == 0,
+// lda and ldb multiples of 4, A and B 16-byte aligned).
+//
+// Loads go straight from global memory into a ring of STAGES LDS stages with
+// global_load_lds_dwordx4 (lane l of one instruction writes its 16 bytes at
+// base + 16 l): no staging registers, no LDS stores, STAGES - 1 K tiles in
+// flight, and each wave reads the fragments of the next K tile while its MFMAs
+// work on the current one, with one barrier per K tile (the pipelined main loop
+// of the DeepGEMM page, 3.3; the double buffer of the Tiled-GEMM chapter, 11.4,
+// made deeper).  Each copy instruction chooses the global chunk of every LDS
+// slot, which sets the layout:
+//  * A: 64-byte rows (one row of a 16-wide K tile), the four 16-byte chunks of
+//    row r permuted by row64_swizzle(r); one instruction copies 16 whole rows.
+//    A fragment read (chunk 2 g + l / 32 of 32 consecutive rows) is then free
+//    of bank conflicts.
+//  * B: one instruction per row of the tile (BN = 256 floats = 1 KiB), rows
+//    padded to 1056 bytes so that the two k-slots of a B read (rows 4 apart)
+//    fall on different halves of the 64 banks.
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int STAGES_, int WAVES_PER_SIMD_ = 1>
+struct SDmaTile {
+  using MF = MfmaF32x32;
+  static constexpr int BM = BM_, BN = BN_, BK = 16, STAGES = STAGES_;
+  static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;
+  static constexpr int WAVES_M = 2, WAVES_N = 2, WAVES = 4;
+  static constexpr int THREADS = WAVES * kWave;
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int BLK = 32;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int A_BYTES = BM * BK * 4;          // 64-byte rows
+  static constexpr int B_ROW = BN * 4 + 32;            // bytes per padded LDS row of B
+  static constexpr int B_BYTES = BK * B_ROW;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_INSTR = A_BYTES / 1024;       // 16 rows per copy
+  static constexpr int B_INSTR = BK;                   // one row per copy
+  static constexpr int A_PER_WAVE = A_INSTR / WAVES;
+  static constexpr int B_PER_WAVE = B_INSTR / WAVES;
+  static constexpr int LOADS_PER_TILE = A_PER_WAVE + B_PER_WAVE;
+
+  static_assert(BN * 4 == 1024, "one copy instruction per row of the B tile");
+  static_assert(A_INSTR % WAVES == 0 && B_INSTR % WAVES == 0, "copies split evenly over waves");
+  static_assert(STAGE_BYTES % 16 == 0, "stages start on 16-byte boundaries");
+  static_assert(STAGES >= 3 && STAGES * STAGE_BYTES * WAVES_PER_SIMD <= 160 * 1024,
+                "the stages of every resident workgroup must fit in LDS");
+  static_assert((STAGES - 2) * LOADS_PER_TILE <= 63, "in-flight copies must fit vmcnt");
+  static_assert(FM * FN * 16 <= 256 / WAVES_PER_SIMD, "accumulators must leave room for operands");
+};
+
+// Per-lane byte offsets of a wave's copies relative to the K tile's A or B base
+// (a_base(kt) = A + m0 lda + 16 kt, b_base(kt) = B + 16 kt ldb + n0, floats),
+// and the LDS slot of copy v inside one stage.
+template <class T>
+struct SDmaPlan {
+  uint32_t off[T::LOADS_PER_TILE];
+  __device__ __forceinline__ SDmaPlan(const SgemmArgs& p, int wave, int lane) {
+#pragma unroll
+    for (int v = 0; v < T::LOADS_PER_TILE; ++v) {
+      if (v < T::A_PER_WAVE) {
+        const int r = (wave * T::A_PER_WAVE + v) * 16 + lane / 4;
+        const int chunk = (lane % 4) ^ row64_swizzle(r);
+        off[v] = (uint32_t)(((size_t)r * p.lda + 4 * chunk) * 4);
+      } else {
+        const int kr = wave * T::B_PER_WAVE + (v - T::A_PER_WAVE);
+        off[v] = (uint32_t)(((size_t)kr * p.ldb + 4 * lane) * 4);
+      }
+    }
+  }
+  static __device__ __forceinline__ uint32_t slot(int v, int wave) {
+    if (v < T::A_PER_WAVE) return (wave * T::A_PER_WAVE + v) * 1024;
+    return T::A_BYTES + (wave * T::B_PER_WAVE + (v - T::A_PER_WAVE)) * T::B_ROW;
+  }
+};
+
+template <class T>
+__device__ __forceinline__ void sdma_issue(const SgemmArgs& p, const SDmaPlan<T>& plan,
+                                           const float* a_tile, const float* b_tile, int kt,
+                                           uint32_t stage, int wave, int x) {
+  const float* base = x < T::A_PER_WAVE ? a_tile + kt * T::BK
+                                        : b_tile + (size_t)kt * T::BK * p.ldb;
+  dma16_sbase(base, plan.off[x], stage + SDmaPlan<T>::slot(x, wave));
+}
+
+// Fragments of one group of 8 k (four MFMA steps): a[i] holds A[row][8 g + 4 h
+// .. + 3] for the wave's m-block i (h = lane / 32 is the lane's k-slot), b[s][j]
+// holds B[8 g + 4 h + s][col] for n-block j.
+template <class T>
+struct SFrags {
+  f32x4 a[T::FM];
+  float b[4][T::FN];
+};
+
+template <class T>
+__device__ __forceinline__ void sload_frags(SFrags<T>& f, const uint8_t* stage, int g, int wm,
+                                            int wn, int lane) {
+  const int l32 = lane % 32, h = lane / 32;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    const int r = wm * T::WTM + i * 32 + l32;
+    f.a[i] = *reinterpret_cast<const f32x4*>(stage + r * 64 + 16 * ((2 * g + h) ^ row64_swizzle(r)));
+  }
+  const uint8_t* bs = stage + T::A_BYTES;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+      f.b[s][j] = *reinterpret_cast<const float*>(bs + (8 * g + 4 * h + s) * T::B_ROW +
+                                                  4 * (wn * T::WTN + j * 32 + l32));
+}
+
+// MFMA number idx (0 .. 4 FM FN - 1) of one group: step s, m-block i, n-block j.
+template <class T>
+__device__ __forceinline__ void smfma(f32x16 (&acc)[T::FM][T::FN], const SFrags<T>& f, int idx) {
+  const int s = idx / (T::FM * T::FN), i = (idx / T::FN) % T::FM, j = idx % T::FN;
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][s], f.b[s][j], acc[i][j], 0, 0, 0);
+}
+
+template <class T>
+__device__ __forceinline__ void swait_tiles(int ahead) {
+  static_assert(T::STAGES <= 5, "extend the cases below for deeper pipelines");
+  if (ahead >= 3 && T::STAGES >= 5) {
+    wait_vmcnt<(T::STAGES >= 5 ? 3 * T::LOADS_PER_TILE : 0)>();
+  } else if (ahead >= 2 && T::STAGES >= 4) {
+    wait_vmcnt<(T::STAGES >= 4 ? 2 * T::LOADS_PER_TILE : 0)>();
+  } else if (ahead >= 1) {
+    wait_vmcnt<T::LOADS_PER_TILE>();
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+// One K tile: MFMAs on the fragments of tile kt (x0: group 0, x1: group 1, read
+// during the previous tile), reads of tile kt + 1's fragments into y0 / y1, the
+// wait for tile kt + 1 and the barrier, and the copies of tile kt + STAGES - 1
+// (unconditional when STEADY: the caller guarantees that tile exists).  After
+// the last tile the reads hit a stage that is no longer used; their values are
+// dropped.
+template <class T, bool STEADY>
+__device__ __forceinline__ void sdma_tile(const SgemmArgs& p, f32x16 (&acc)[T::FM][T::FN], int kt,
+                                          int ktiles, SFrags<T>& x0, SFrags<T>& x1,
+                                          SFrags<T>& y0, SFrags<T>& y1, const uint8_t* lds,
+                                          uint32_t lds_base, const SDmaPlan<T>& plan,
+                                          const float* a_tile, const float* b_tile, int wave,
+                                          int wm, int wn, int lane) {
+  constexpr int NM = 4 * T::FM * T::FN;            // MFMAs per group
+  constexpr int NR = T::FM + 4 * T::FN;            // LDS reads per group
+  constexpr int PRE = 2;
+  constexpr int R0 = (NR + NM - PRE - 1) / (NM - PRE);
+  constexpr int TAIL = NM - T::LOADS_PER_TILE;
+  constexpr int R1 = (NR + TAIL - 1) / TAIL;
+  static_assert(TAIL >= NR / 2 && TAIL >= 1, "enough MFMAs to spread the reads over");
+  smfma<T>(acc, x0, 0);
+  smfma<T>(acc, x0, 1);
+  if constexpr (STEADY) {
+    wait_vmcnt<(T::STAGES - 3) * T::LOADS_PER_TILE>();
+  } else {
+    const int left = ktiles - 2 - kt;
+    swait_tiles<T>(left < 0 ? 0 : (left < T::STAGES - 3 ? left : T::STAGES - 3));
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  const uint8_t* next = lds + ((kt + 1) % T::STAGES) * T::STAGE_BYTES;
+  sload_frags<T>(y0, next, 0, wm, wn, lane);
+#pragma unroll
+  for (int x = PRE; x < NM; ++x) smfma<T>(acc, x0, x);
+#pragma unroll
+  for (int x = 0; x < NM - PRE; ++x) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int kt_issue = kt + T::STAGES - 1;
+  const bool issue = STEADY || kt_issue < ktiles;
+  const uint32_t st_issue = lds_base + (kt_issue % T::STAGES) * T::STAGE_BYTES;
+  sload_frags<T>(y1, next, 1, wm, wn, lane);
+#pragma unroll
+  for (int x = 0; x < TAIL; ++x) smfma<T>(acc, x1, x);
+#pragma unroll
+  for (int x = 0; x < TAIL; ++x) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, R1, 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int x = 0; x < T::LOADS_PER_TILE; ++x) {
+    smfma<T>(acc, x1, TAIL + x);
+    if (issue) sdma_issue<T>(p, plan, a_tile, b_tile, kt_issue, st_issue, wave, x);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <class T>
+__global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(T::WAVES_PER_SIMD)))
+sgemm_dma_kernel(SgemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[T::STAGES * T::STAGE_BYTES];
+
+  int tile_m, tile_n;
+  tile_of_workgroup(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
+  const int m0 = tile_m * T::BM;
+  const int n0 = tile_n * T::BN;
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = wave / T::WAVES_N;
+  const int wn = wave % T::WAVES_N;
+  const uint32_t lds_base = lds_offset(lds);
+
+  f32x16 acc[T::FM][T::FN];
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Tile kt lives in stage kt % STAGES; its copies are issued during tile
+  // kt - STAGES + 1 (the prologue issues the first STAGES - 1).  K is a multiple
+  // of 2 BK, so the loop body covers two tiles and the fragment sets alternate.
+  const int ktiles = p.K / T::BK;
+  const float* a_tile = p.A + (size_t)m0 * p.lda;
+  const float* b_tile = p.B + n0;
+  const SDmaPlan<T> plan(p, wave, lane);
+  SFrags<T> f0, f1, f2, f3;
+  if (ktiles > 0) {
+#pragma unroll
+    for (int st = 0; st < T::STAGES - 1; ++st)
+      if (st < ktiles) {
+#pragma unroll
+        for (int x = 0; x < T::LOADS_PER_TILE; ++x)
+          sdma_issue<T>(p, plan, a_tile, b_tile, st, lds_base + st * T::STAGE_BYTES, wave, x);
+      }
+    swait_tiles<T>(ktiles - 1 < T::STAGES - 2 ? ktiles - 1 : T::STAGES - 2);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    sload_frags<T>(f0, lds, 0, wm, wn, lane);
+    sload_frags<T>(f1, lds, 1, wm, wn, lane);
+  }
+  int kt = 0;
+  for (; kt + T::STAGES < ktiles; kt += 2) {
+    sdma_tile<T, true>(p, acc, kt, ktiles, f0, f1, f2, f3, lds, lds_base, plan, a_tile, b_tile,
+                       wave, wm, wn, lane);
+    sdma_tile<T, true>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, plan, a_tile, b_tile,
+                       wave, wm, wn, lane);
+  }
+  for (; kt < ktiles; kt += 2) {
+    sdma_tile<T, false>(p, acc, kt, ktiles, f0, f1, f2, f3, lds, lds_base, plan, a_tile, b_tile,
+                        wave, wm, wn, lane);
+    sdma_tile<T, false>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, plan, a_tile,
+                        b_tile, wave, wm, wn, lane);
+  }
+  sgemm_store<T, false>(p, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
 }
 
 // Second half of split-K: C = alpha * (sum of the `splits` partials, added in
@@ -310,12 +603,25 @@ using TileMedium = SgemmTile<128, 128, 16, 2, 2>;    // 4 waves, 64 x 64 each
 using TileSmall = SgemmTile<64, 64, 16, 2, 2>;       // 4 waves, 32 x 32 each
 using TileLargeK32 = SgemmTile<256, 256, 32, 2, 2>;  // as TileLarge, half the barriers
 using TileTall = SgemmTile<128, 256, 16, 2, 2, 2>;   // 4 waves, 64 x 128 each, 2 workgroups/CU
+// The same two shapes built from 16x16x4 MFMA blocks.
+using TileLarge16 = SgemmTile<256, 256, 16, 2, 2, 1, MfmaF16x16>;
+using TileTall16 = SgemmTile<128, 256, 16, 2, 2, 2, MfmaF16x16>;
+// Direct-to-LDS: 256 x 256, 4 stages of 32.5 KiB, one workgroup per CU / 128 x 256,
+// 3 stages of 24.5 KiB, two workgroups per CU.
+using SDmaLarge = SDmaTile<256, 256, 4, 1>;
+using SDmaTall = SDmaTile<128, 256, 3, 2>;
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 static_assert(TileLarge::BK == sgemm_tile_bk(0) && TileMedium::BK == sgemm_tile_bk(1) &&
                   TileSmall::BK == sgemm_tile_bk(2) && TileLargeK32::BK == sgemm_tile_bk(3) &&
-                  TileTall::BK == sgemm_tile_bk(4),
+                  TileTall::BK == sgemm_tile_bk(4) && TileLarge16::BK == sgemm_tile_bk(5) &&
+                  TileTall16::BK == sgemm_tile_bk(6) && TileLarge16::BM == sgemm_tile_bm(5) &&
+                  TileLarge16::BN == sgemm_tile_bn(5) && TileTall16::BM == sgemm_tile_bm(6) &&
+                  TileTall16::BN == sgemm_tile_bn(6) && TileTall::BM == sgemm_tile_bm(4) &&
+                  SDmaLarge::BK == sgemm_tile_bk(7) && SDmaTall::BK == sgemm_tile_bk(8) &&
+                  SDmaLarge::BM == sgemm_tile_bm(7) && SDmaLarge::BN == sgemm_tile_bn(7) &&
+                  SDmaTall::BM == sgemm_tile_bm(8) && SDmaTall::BN == sgemm_tile_bn(8),
               "the host-side planner's K steps must match the tiles");
 
 static hipError_t launch_reduce(const SgemmCall& c, int splits, const float* ws, hipStream_t s) {
@@ -359,14 +665,55 @@ static hipError_t launch_tile(const SgemmCall& c, const SgemmPlan& plan, int gro
   return hipGetLastError();
 }
 
+template <class T>
+static bool sdma_fits(const SgemmCall& c) {
+  return c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % (2 * T::BK) == 0 && c.lda % 4 == 0 &&
+         c.ldb % 4 == 0 && aligned16(c.A) && aligned16(c.B) &&
+         (int64_t)c.lda * T::BM * 4 < (int64_t(1) << 31) &&
+         (int64_t)c.ldb * T::BK * 4 < (int64_t(1) << 31);
+}
+
+template <class T>
+static hipError_t launch_sdma(const SgemmCall& c, int group_m, hipStream_t s) {
+  if (!sdma_fits<T>(c)) return hipErrorInvalidValue;
+  SgemmArgs p;
+  p.M = c.M; p.N = c.N; p.K = c.K;
+  p.alpha = c.alpha; p.beta = c.beta;
+  p.A = c.A; p.lda = c.lda; p.B = c.B; p.ldb = c.ldb; p.C = c.C; p.ldc = c.ldc;
+  p.tiles_m = c.M / T::BM;
+  p.tiles_n = c.N / T::BN;
+  p.group_m = group_m;
+  p.k_chunk = c.K;
+  p.ws = nullptr;
+  hipLaunchKernelGGL((sgemm_dma_kernel<T>), dim3(p.tiles_m * p.tiles_n), dim3(T::THREADS), 0, s, p);
+  return hipGetLastError();
+}
+
+int sgemm_resolve_tile(int tile, int M, int N, int K, int splits, bool operands_ok) {
+  // The direct-to-LDS kernels need whole tiles, K a multiple of 32, aligned
+  // operands and no K split; otherwise the register-staged 128 x 256 kernel
+  // (the best of those for large outputs) runs.
+  const bool whole = operands_ok && N % 256 == 0 && K % 32 == 0 && splits == 1;
+  if (tile == 7 && !(whole && M % 256 == 0)) return 4;
+  if (tile == 8 && !(whole && M % 128 == 0)) return 4;
+  return tile;
+}
+
 hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hipStream_t s) {
   if (plan.splits > 1 && ws == nullptr) return hipErrorInvalidValue;
-  switch (plan.tile) {
+  const bool operands_ok = c.lda % 4 == 0 && c.ldb % 4 == 0 && aligned16(c.A) && aligned16(c.B) &&
+                           (int64_t)c.lda * 256 * 4 < (int64_t(1) << 31) &&
+                           (int64_t)c.ldb * 16 * 4 < (int64_t(1) << 31);
+  switch (sgemm_resolve_tile(plan.tile, c.M, c.N, c.K, plan.splits, operands_ok)) {
     case 0: return launch_tile<TileLarge>(c, plan, 4, ws, s);
     case 1: return launch_tile<TileMedium>(c, plan, 8, ws, s);
     case 2: return launch_tile<TileSmall>(c, plan, 8, ws, s);
     case 3: return launch_tile<TileLargeK32>(c, plan, 4, ws, s);
     case 4: return launch_tile<TileTall>(c, plan, 8, ws, s);
+    case 5: return launch_tile<TileLarge16>(c, plan, 4, ws, s);
+    case 6: return launch_tile<TileTall16>(c, plan, 8, ws, s);
+    case 7: return launch_sdma<SDmaLarge>(c, 4, s);
+    case 8: return launch_sdma<SDmaTall>(c, 8, s);
     default: return hipErrorInvalidValue;
   }
 }

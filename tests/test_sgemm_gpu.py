@@ -17,7 +17,9 @@ from tests.gpu_helpers import FP32_TOL, note, run_sgemm, sgemm_error
 
 pytestmark = pytest.mark.gpu
 
-TILES = (0, 1, 2, 3, 4)   # 256x256, 128x128, 64x64, 256x256 (K step 32), 128x256
+# 256x256, 128x128, 64x64, 256x256 (K step 32), 128x256; 5, 6: 256x256 and 128x256 with
+# 16x16x4 MFMA blocks; 7, 8: 256x256 and 128x256 with direct-to-LDS copies
+TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8)
 
 
 @pytest.fixture(scope="module", autouse=True)
