@@ -182,7 +182,8 @@ def main():
     if w.op == "sgemm":
         tile, splits = lib.gemm_debug_pick_config(
             0, M, N, K, torch.cuda.get_device_properties(0).multi_processor_count)
-        kernel_name = "sgemm_mfma_kernel, tile config %d" % tile
+        kernel_name = "%s, tile config %d" % (
+            "sgemm_dma_kernel" if tile >= 7 else "sgemm_mfma_kernel", tile)
         if splits > 1:
             kernel_name += ", split-K x%d + sgemm_splitk_reduce_kernel (timed together)" % splits
     else:

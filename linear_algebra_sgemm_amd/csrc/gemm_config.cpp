@@ -43,8 +43,9 @@ int size_class(int x) {
 
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
-// Built-in tile rule, measured on MI355X: the 256x256 direct-to-LDS tile once
-// whole tiles give every CU one (4096^3: 143 TFLOP/s, 8192^3: 145); 128x256
+// Built-in tile rule, measured on MI355X: the 256x256 direct-to-LDS tile with
+// eight waves once whole tiles give every CU one (4096^3: 146 TFLOP/s, 8192^3:
+// 149; four waves: 143 and 146); 128x256
 // register-staged tiles at two workgroups per CU once they give every CU two
 // (4096^3: 134 vs 130 for 256x256); below that, 128x128 if it still gives two
 // tiles per CU, else 64x64 tiles, which spread small outputs over more CUs
@@ -53,7 +54,7 @@ int sgemm_rule_tile(int M, int N, int K, int cus) {
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_tall = ceil_div(M, 128) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
-  if (t_large >= cus && M % 256 == 0 && N % 256 == 0 && K % 32 == 0) return 7;
+  if (t_large >= cus && M % 256 == 0 && N % 256 == 0 && K % 32 == 0) return 9;
   if (t_tall >= 2L * cus) return 4;
   if (t_med >= 2L * cus) return 1;
   return 2;

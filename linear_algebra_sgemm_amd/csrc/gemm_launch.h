@@ -37,20 +37,20 @@ struct HgemmCall {
 // 32x32x2 MFMA blocks); 5 = 256x256 and 6 = 128x256 at two
 // workgroups per CU, both with 16x16x4 MFMA blocks; 7 = 256x256 and 8 = 128x256
 // at two workgroups per CU with direct-to-LDS copies into a multi-stage ring
-// (whole tiles only, else tile 4).
+// (whole tiles only, else tile 4); 9 = tile 7 with eight waves, two per SIMD.
 // HGEMM: 0 = 256x256, 1 = 128x128, 2 = 64x64 (register-staged, K step 64),
 // 3 = 256x256 direct-to-LDS, 4 stages of K step 32, 4 = 128x256 direct-to-LDS,
 // 3 stages, two workgroups per CU, 5 = 256x256 direct-to-LDS, 5 stages, 6 = 256x256
 // direct-to-LDS with eight waves (3 to 6 need whole tiles and K a multiple of 64;
 // other shapes fall back to 0).
-constexpr int kSgemmTileCount = 9;
+constexpr int kSgemmTileCount = 10;
 constexpr int kHgemmTileCount = 7;
 
 // K step of each SGEMM tile configuration (checked against the kernels).
 constexpr int sgemm_tile_bk(int tile) { return tile == 3 ? 32 : 16; }
 // Output tile of each SGEMM configuration.
 constexpr int sgemm_tile_bm(int tile) {
-  return tile == 0 || tile == 3 || tile == 5 || tile == 7 ? 256 : tile == 2 ? 64 : 128;
+  return tile == 0 || tile == 3 || tile == 5 || tile == 7 || tile == 9 ? 256 : tile == 2 ? 64 : 128;
 }
 constexpr int sgemm_tile_bn(int tile) {
   return tile == 1 ? 128 : tile == 2 ? 64 : 256;
@@ -77,7 +77,7 @@ struct SgemmPlan {
 SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_splits,
                      size_t ws_floats);
 // The FP32 configuration that actually runs for `tile` with `splits` K chunks:
-// the direct-to-LDS ones (7, 8) become 4 when the shape, the operands
+// the direct-to-LDS ones (7, 8, 9) become 4 when the shape, the operands
 // (`operands_ok`: lda, ldb multiples of 4, A and B 16-byte aligned) or a K
 // split do not suit them.
 int sgemm_resolve_tile(int tile, int M, int N, int K, int splits, bool operands_ok);

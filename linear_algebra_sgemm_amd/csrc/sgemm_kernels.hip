@@ -346,12 +346,14 @@ __global__ void __launch_bounds__(256) sgemm_scale_kernel(int M, int N, float be
 //    padded to 1056 bytes so that the two k-slots of a B read (rows 4 apart)
 //    fall on different halves of the 64 banks.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int STAGES_, int WAVES_PER_SIMD_ = 1>
+template <int BM_, int BN_, int STAGES_, int WAVES_PER_SIMD_ = 1, int WAVES_M_ = 2,
+          int WAVES_N_ = 2>
 struct SDmaTile {
   using MF = MfmaF32x32;
   static constexpr int BM = BM_, BN = BN_, BK = 16, STAGES = STAGES_;
   static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;
-  static constexpr int WAVES_M = 2, WAVES_N = 2, WAVES = 4;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M * WAVES_N;
+  static constexpr int WG_PER_CU = WAVES_PER_SIMD * 4 / WAVES;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int BLK = 32;
@@ -369,7 +371,7 @@ struct SDmaTile {
   static_assert(BN * 4 == 1024, "one copy instruction per row of the B tile");
   static_assert(A_INSTR % WAVES == 0 && B_INSTR % WAVES == 0, "copies split evenly over waves");
   static_assert(STAGE_BYTES % 16 == 0, "stages start on 16-byte boundaries");
-  static_assert(STAGES >= 3 && STAGES * STAGE_BYTES * WAVES_PER_SIMD <= 160 * 1024,
+  static_assert(STAGES >= 3 && STAGES * STAGE_BYTES * WG_PER_CU <= 160 * 1024,
                 "the stages of every resident workgroup must fit in LDS");
   static_assert((STAGES - 2) * LOADS_PER_TILE <= 63, "in-flight copies must fit vmcnt");
   static_assert(FM * FN * 16 <= 256 / WAVES_PER_SIMD, "accumulators must leave room for operands");
@@ -610,6 +612,8 @@ using TileTall16 = SgemmTile<128, 256, 16, 2, 2, 2, MfmaF16x16>;
 // 3 stages of 24.5 KiB, two workgroups per CU.
 using SDmaLarge = SDmaTile<256, 256, 4, 1>;
 using SDmaTall = SDmaTile<128, 256, 3, 2>;
+// 256 x 256 with eight waves (2 x 4, each 128 x 64), two per SIMD.
+using SDmaEight = SDmaTile<256, 256, 4, 2, 2, 4>;
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -621,7 +625,9 @@ static_assert(TileLarge::BK == sgemm_tile_bk(0) && TileMedium::BK == sgemm_tile_
                   TileTall16::BN == sgemm_tile_bn(6) && TileTall::BM == sgemm_tile_bm(4) &&
                   SDmaLarge::BK == sgemm_tile_bk(7) && SDmaTall::BK == sgemm_tile_bk(8) &&
                   SDmaLarge::BM == sgemm_tile_bm(7) && SDmaLarge::BN == sgemm_tile_bn(7) &&
-                  SDmaTall::BM == sgemm_tile_bm(8) && SDmaTall::BN == sgemm_tile_bn(8),
+                  SDmaTall::BM == sgemm_tile_bm(8) && SDmaTall::BN == sgemm_tile_bn(8) &&
+                  SDmaEight::BM == sgemm_tile_bm(9) && SDmaEight::BN == sgemm_tile_bn(9) &&
+                  SDmaEight::BK == sgemm_tile_bk(9),
               "the host-side planner's K steps must match the tiles");
 
 static hipError_t launch_reduce(const SgemmCall& c, int splits, const float* ws, hipStream_t s) {
@@ -696,6 +702,7 @@ int sgemm_resolve_tile(int tile, int M, int N, int K, int splits, bool operands_
   const bool whole = operands_ok && N % 256 == 0 && K % 32 == 0 && splits == 1;
   if (tile == 7 && !(whole && M % 256 == 0)) return 4;
   if (tile == 8 && !(whole && M % 128 == 0)) return 4;
+  if (tile == 9 && !(whole && M % 256 == 0)) return 4;
   return tile;
 }
 
@@ -714,6 +721,7 @@ hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hi
     case 6: return launch_tile<TileTall16>(c, plan, 8, ws, s);
     case 7: return launch_sdma<SDmaLarge>(c, 4, s);
     case 8: return launch_sdma<SDmaTall>(c, 8, s);
+    case 9: return launch_sdma<SDmaEight>(c, 4, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -146,15 +146,15 @@ def test_config_rule(so):
     """The built-in rule (tuned table off): the largest tile that still gives every
     CU two tiles, split-K only when the tiles do not cover the CUs."""
     cases = [
-        (0, 4096, 4096, 4096, 256, (7, 1)),   # whole 256x256 tiles: direct-to-LDS kernel
-        (0, 8192, 8192, 8192, 256, (7, 1)),
+        (0, 4096, 4096, 4096, 256, (9, 1)),   # whole 256x256 tiles: direct-to-LDS kernel
+        (0, 8192, 8192, 8192, 256, (9, 1)),
         (0, 4096, 4096, 4008, 256, (4, 1)),   # K not a multiple of 32
         (0, 256, 256, 256, 256, (2, 1)),      # K < 512: no split
         (0, 256, 256, 1024, 256, (2, 8)),     # 16 tiles; chunks of 128
         (0, 512, 512, 512, 256, (2, 4)),      # 64 tiles; chunks of 128
         (0, 1000, 3000, 777, 256, (2, 1)),    # 752 tiles
         (0, 2048, 2048, 2048, 256, (2, 1)),
-        (0, 4096, 4096, 4096, 64, (7, 1)),
+        (0, 4096, 4096, 4096, 64, (9, 1)),
         (0, 128, 128, 16384, 256, (2, 32)),   # 4 tiles; 256 chunks by CUs, capped at 32
         (0, 1024, 1024, 4096, 256, (2, 1)),   # 256 tiles of 64x64 cover the CUs
         (1, 4096, 14336, 4096, 256, (3, 1)),  # whole 256-tiles: direct-to-LDS kernel
@@ -243,15 +243,15 @@ def test_split_legality(so):
             M, N = rng.randint(1, 3000), rng.randint(1, 3000)
             K = rng.choice([1, 15, 16, 17, 100, 777, 4096, 20000])
             want = rng.choice([1, 2, 3, 5, 8, 16, 32])
-            tile = rng.choice([-1, 0, 1, 2, 3, 4, 5, 6, 7, 8])
+            tile = rng.choice([-1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
             assert lib.gemm_debug_force_tile(0, tile) == lib.STATUS_SUCCESS
             assert lib.gemm_debug_force_splits(0, want) == lib.STATUS_SUCCESS
             t, s = pick(0, M, N, K)
             if tile >= 0:
                 # direct-to-LDS tiles (7, 8) run as 0 / 4 unless the shape is whole and unsplit
-                assert t == tile or (tile, t) in ((7, 4), (8, 4))
+                assert t == tile or (tile, t) in ((7, 4), (8, 4), (9, 4))
                 if t != tile:
-                    assert s > 1 or M % (256 if tile == 7 else 128) or N % 256 or K % 32
+                    assert s > 1 or M % (128 if tile == 8 else 256) or N % 256 or K % 32
             bk = bk_of(t)
             ktiles = -(-K // bk)
             assert 1 <= s <= max(1, min(want, ktiles))
@@ -292,8 +292,8 @@ def test_forced_splits(so):
 
 
 def test_force_tile_values(so):
-    assert lib.gemm_debug_force_tile(0, 9) == lib.STATUS_INVALID_VALUE
-    assert lib.gemm_debug_force_tile(0, 8) == lib.STATUS_SUCCESS
+    assert lib.gemm_debug_force_tile(0, 10) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(0, 9) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(1, 7) == lib.STATUS_INVALID_VALUE
     assert lib.gemm_debug_force_tile(1, 6) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(1, 5) == lib.STATUS_SUCCESS
