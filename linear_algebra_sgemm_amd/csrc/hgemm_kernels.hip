@@ -622,6 +622,56 @@ hgemm_dma_kernel(HgemmArgs p) {
   // columns n = 8 q + 4 (l / 32) + 0..3 of row m = l % 32.
   const float alpha = p.alpha;
   const bool gelu = p.act == 1;
+  if (p.ldc % 8 == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15u) == 0) {
+    // Through LDS, so that every store instruction writes whole rows: the wave
+    // puts its finished WTM x WTN tile into its own region of the (now idle)
+    // stages, then reads it back 16 bytes per lane along rows.  16-byte chunks
+    // of row r are permuted by (r / rows-per-256-bytes) % chunks-per-row, so
+    // the writes of one column over 32 rows spread over the banks.
+    static_assert(T::BM * T::BN * 2 <= T::STAGES * T::STAGE_BYTES, "output tile must fit the stages");
+    constexpr int RB = T::WTN * 2;          // bytes per row of a wave's tile
+    constexpr int CPR = RB / 16;            // 16-byte chunks per row
+    constexpr int RPL = RB >= 256 ? 1 : 256 / RB;
+    static_assert(RB % 128 == 0 && 1024 % RB == 0, "rows of 128 or 256 bytes");
+    lds_barrier();   // every wave is done with the stages
+    uint8_t* region = lds + wave * (T::WTM * RB);
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cl = wn * T::WTN + 32 * j + 8 * q + 4 * (lane / 32);
+        float bias4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (p.bias != nullptr) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bias4[e] = p.bias[n0 + cl + e];
+        }
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) {
+          const int r = 32 * i + lane % 32;
+          uint16_t h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = __builtin_fmaf(alpha, acc[j][i][4 * q + e], bias4[e]);
+            if (gelu) x = gelu_tanh(x);
+            h[e] = T::E::bits(x);
+          }
+          const int chunk = 4 * j + q;
+          *reinterpret_cast<uint2*>(region + r * RB + 16 * (chunk ^ ((r / RPL) % CPR)) +
+                                    8 * (lane / 32)) = __builtin_bit_cast(uint2, h);
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < T::WTM * RB / 1024; ++it) {
+      const int r = it * (1024 / RB) + lane / CPR;
+      const int chunk = lane % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(region + r * RB +
+                                                      16 * (chunk ^ ((r / RPL) % CPR)));
+      *reinterpret_cast<u32x4*>(p.C + (size_t)(m0 + wm * T::WTM + r) * p.ldc + n0 +
+                                wn * T::WTN + 8 * chunk) = v;
+    }
+    return;
+  }
   const bool vec_store = (p.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.C) & 7u) == 0);
 #pragma unroll
   for (int j = 0; j < T::FN; ++j) {
