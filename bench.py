@@ -28,10 +28,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOPS at 4096³ FP32 (α,β) + % of MI355X matrix peak per dtype"
 PROFILES = os.path.join(ROOT, "profiles")
+_CSRC = os.path.join(ROOT, "linear_algebra_sgemm_amd", "csrc")
+# The sources that decide what one call of each op runs: its kernels, the shared
+# copy helpers and the shape -> configuration choice with its tuned table.
+_CHOICE = [os.path.join(_CSRC, f) for f in ("dma_common.h", "gemm_config.cpp", "gemm_tuned.inc")]
 KERNEL_SOURCES = {
-    "sgemm": os.path.join(ROOT, "linear_algebra_sgemm_amd", "csrc", "sgemm_kernels.hip"),
-    "hgemm_bias_gelu": os.path.join(ROOT, "linear_algebra_sgemm_amd", "csrc", "hgemm_kernels.hip"),
-    "bgemm_bias_gelu": os.path.join(ROOT, "linear_algebra_sgemm_amd", "csrc", "hgemm_kernels.hip"),
+    "sgemm": [os.path.join(_CSRC, "sgemm_kernels.hip")] + _CHOICE,
+    "hgemm_bias_gelu": [os.path.join(_CSRC, "hgemm_kernels.hip")] + _CHOICE,
+    "bgemm_bias_gelu": [os.path.join(_CSRC, "hgemm_kernels.hip")] + _CHOICE,
 }
 
 
@@ -47,14 +51,19 @@ def parse_args():
     return p.parse_args()
 
 
-def source_digest(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(paths) -> str:
+    """First 16 hex digits of the SHA-256 of the files' contents, in order."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def profiled_traffic(workload: str, op: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of this workload,
-    or None when there is none or the kernel source changed since it was taken."""
+    """HBM bytes per call (all kernels of one call) from the committed rocprofv3 counter
+    summary of this workload, or None when there is none or the sources that decide
+    what the call runs changed since it was taken."""
     path = os.path.join(PROFILES, "%s_counters.md" % workload)
     if not os.path.exists(path):
         return None
@@ -191,6 +200,8 @@ def main():
             1, M, N, K, torch.cuda.get_device_properties(0).multi_processor_count)
         kernel_name = "%s, %s, tile config %d" % (
             "hgemm_dma_kernel" if tile >= 3 else "hgemm_mfma_kernel", dtype, tile)
+        if tile == 7:
+            kernel_name += " (256x256 head + 128x256 tail launches, timed together)"
     line = {
         "metric": METRIC,
         "value": round(tflops, 3),

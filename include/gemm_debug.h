@@ -21,9 +21,10 @@ extern "C" {
  * 0 and 4 with direct-to-LDS copies (whole tiles and no K split only, else
  * tile 4), 9 = tile 7 with eight waves; the
  * half products also have 3 = 256 x 256 and 4 = 128 x 256 direct-to-LDS kernels
- * 5 = the 256 x 256 one with a five-stage pipeline and 6 = the 256 x 256 one
- * with eight waves (whole tiles only, else the 256 x 256 register-staged
- * kernel).
+ * 5 = the 256 x 256 one with a five-stage pipeline, 6 = the 256 x 256 one
+ * with eight waves and 7 = tile 6 on the columns that fill whole rounds of
+ * workgroups plus 128 x 256 tiles on the rest (whole tiles only, else the
+ * 256 x 256 register-staged kernel; 7 becomes 6 where no such split exists).
  * Whether the aligned fast path or the
  * bounds-checked path runs still follows the shape and alignment.  Returns
  * GEMM_STATUS_INVALID_VALUE for an unknown op or tile.  Pure host state: no

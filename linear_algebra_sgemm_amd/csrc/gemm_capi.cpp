@@ -250,7 +250,7 @@ int gemm_debug_pick_config(int op, int M, int N, int K, int cus, int* tile, int*
   if (op == 1) {
     const int forced = g_force_hgemm_tile.load();
     *tile = lasg::hgemm_resolve_tile(forced >= 0 ? forced : lasg::hgemm_pick_tile(M, N, K, cus, true),
-                                     M, N, K, true);
+                                     M, N, K, true, cus);
     *splits = 1;
     return GEMM_STATUS_SUCCESS;
   }

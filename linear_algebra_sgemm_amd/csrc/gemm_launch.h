@@ -41,10 +41,11 @@ struct HgemmCall {
 // HGEMM: 0 = 256x256, 1 = 128x128, 2 = 64x64 (register-staged, K step 64),
 // 3 = 256x256 direct-to-LDS, 4 stages of K step 32, 4 = 128x256 direct-to-LDS,
 // 3 stages, two workgroups per CU, 5 = 256x256 direct-to-LDS, 5 stages, 6 = 256x256
-// direct-to-LDS with eight waves (3 to 6 need whole tiles and K a multiple of 64;
-// other shapes fall back to 0).
+// direct-to-LDS with eight waves, 7 = tile 6 on the columns that fill whole
+// rounds of workgroups and 128 x 256 direct-to-LDS tiles on the rest (3 to 7 need
+// whole tiles and K a multiple of 64; other shapes fall back to 0).
 constexpr int kSgemmTileCount = 10;
-constexpr int kHgemmTileCount = 7;
+constexpr int kHgemmTileCount = 8;
 
 // K step of each SGEMM tile configuration (checked against the kernels).
 constexpr int sgemm_tile_bk(int tile) { return tile == 3 ? 32 : 16; }
@@ -92,7 +93,12 @@ int hgemm_pick_tile(int M, int N, int K, int cus, bool operands_ok);
 // The configuration that actually runs for `tile`: the direct-to-LDS ones (3,
 // 4) become the register-staged 256x256 one (0) when the shape or operands do
 // not suit them.
-int hgemm_resolve_tile(int tile, int M, int N, int K, bool operands_ok);
+// 7 (eight-wave 256 x 256 tiles with a 128 x 256 tail) becomes 6 when no split
+// of the columns fills whole rounds of `cus` workgroups with the head and one
+// round with the tail.
+int hgemm_resolve_tile(int tile, int M, int N, int K, bool operands_ok, int cus);
+// Column where that split falls (0: none).
+int hgemm_tail_split(int M, int N, int cus);
 
 // Whether the offline-tuned table is consulted (default on; a test hook turns
 // it off to see the built-in rule).

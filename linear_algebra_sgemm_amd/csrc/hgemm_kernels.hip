@@ -716,6 +716,9 @@ template <class E> using HDmaDeep = HDmaTile<E, 256, 256, 32, 5>;
 // 256 x 256 with eight waves (2 x 4, each 128 x 64), two per SIMD: while one
 // wave waits on its LDS reads or the barrier, the other can issue MFMAs.
 template <class E> using HDmaEight = HDmaTile<E, 256, 256, 32, 4, 2, 2, 4>;
+// 128 x 256 with eight waves of 64 x 64 and four stages: 96 KiB of LDS, so each
+// CU holds one workgroup and a round of them spreads over every CU.
+template <class E> using HDmaHalfEight = HDmaTile<E, 128, 256, 32, 4, 2, 2, 4>;
 
 template <class T>
 static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s) {
@@ -774,12 +777,27 @@ static_assert(HDmaLarge<EltF16>::BM == 256 && HDmaLarge<EltF16>::BN == 256 &&
                   2 * HDmaDeep<EltF16>::BK == 64,
               "hgemm_resolve_tile's shape conditions must match the direct-to-LDS tiles");
 
-int hgemm_resolve_tile(int tile, int M, int N, int K, bool operands_ok) {
+int hgemm_tail_split(int M, int N, int cus) {
+  // Columns [0, n1) in 256 x 256 tiles fill whole rounds of `cus` workgroups;
+  // the rest, in 128 x 256 tiles, must fit one round.
+  if (M % 256 != 0 || N % 256 != 0 || cus <= 0) return 0;
+  const long tm = M / 256, tn = N / 256;
+  if ((tm * tn) % cus == 0) return 0;   // no partial round to fix
+  for (long n1 = tn - 1; n1 >= 1; --n1) {
+    if ((tm * n1) % cus != 0) continue;
+    const long tail = (M / 128) * (tn - n1);
+    return tail <= cus ? (int)(n1 * 256) : 0;
+  }
+  return 0;
+}
+
+int hgemm_resolve_tile(int tile, int M, int N, int K, bool operands_ok, int cus) {
   // The direct-to-LDS kernels need whole tiles and K a multiple of 64;
   // otherwise the register-staged 256x256 kernel, which handles every shape, runs.
-  if ((tile == 3 || tile == 5 || tile == 6) &&
+  if ((tile == 3 || tile == 5 || tile == 6 || tile == 7) &&
       !(operands_ok && M % 256 == 0 && N % 256 == 0 && K % 64 == 0))
     return 0;
+  if (tile == 7 && hgemm_tail_split(M, N, cus) == 0) return 6;
   if (tile == 4 && !(operands_ok && M % 128 == 0 && N % 256 == 0 && K % 64 == 0)) return 0;
   return tile;
 }
@@ -794,7 +812,7 @@ static hipError_t launch_half(const HgemmCall& c, int cus, int force_tile, hipSt
                            (int64_t)c.lda * 256 * 2 < (int64_t(1) << 31) &&
                            (int64_t)c.ldb * 32 * 2 < (int64_t(1) << 31);
   int tile = force_tile >= 0 ? force_tile : hgemm_pick_tile(c.M, c.N, c.K, cus, operands_ok);
-  tile = hgemm_resolve_tile(tile, c.M, c.N, c.K, operands_ok);
+  tile = hgemm_resolve_tile(tile, c.M, c.N, c.K, operands_ok, cus);
   switch (tile) {
     case 0: return launch_htile<HTileLarge<E>>(c, 4, s);
     case 1: return launch_htile<HTileMedium<E>>(c, 8, s);
@@ -811,6 +829,22 @@ static hipError_t launch_half(const HgemmCall& c, int cus, int force_tile, hipSt
     case 6:
       if (!dma_fits<HDmaEight<E>>(c)) return hipErrorInvalidValue;
       return launch_hdma<HDmaEight<E>>(c, 4, s);
+    case 7: {
+      // Columns [0, n1): eight-wave 256 x 256 tiles in whole rounds; the rest:
+      // 128 x 256 tiles, twice as many half-size tiles in the last round.
+      const int n1 = hgemm_tail_split(c.M, c.N, cus);
+      HgemmCall head = c, tail = c;
+      head.N = n1;
+      tail.N = c.N - n1;
+      tail.B = c.B + n1;
+      tail.C = c.C + n1;
+      tail.bias = c.bias ? c.bias + n1 : nullptr;
+      if (n1 == 0 || !dma_fits<HDmaEight<E>>(head) || !dma_fits<HDmaHalfEight<E>>(tail))
+        return hipErrorInvalidValue;
+      const hipError_t e = launch_hdma<HDmaEight<E>>(head, 4, s);
+      if (e != hipSuccess) return e;
+      return launch_hdma<HDmaHalfEight<E>>(tail, 8, s);
+    }
     default: return hipErrorInvalidValue;
   }
 }

@@ -50,14 +50,15 @@ DEFAULT_REPORT = os.path.join(ROOT, "profiles", "size_sweep.md")
 
 OPS = {"sgemm": 0, "half": 1}
 SGEMM_TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9)
-HALF_TILES = (0, 1, 2, 3, 4, 5, 6)
+HALF_TILES = (0, 1, 2, 3, 4, 5, 6, 7)
 SPLITS = (1, 2, 4, 8, 16, 32)
 TILE_NAMES = {
     0: {0: "256x256", 1: "128x128", 2: "64x64", 3: "256x256 (BK 32)", 4: "128x256 (2 WG/CU)",
         5: "256x256 (16x16 MFMA)", 6: "128x256 (2 WG/CU, 16x16 MFMA)", 7: "256x256 direct",
         8: "128x256 direct (2 WG/CU)", 9: "256x256 direct, 8 waves"},
     1: {0: "256x256 reg", 1: "128x128 reg", 2: "64x64 reg", 3: "256x256 direct",
-        4: "128x256 direct", 5: "256x256 direct, 5 stages", 6: "256x256 direct, 8 waves"},
+        4: "128x256 direct", 5: "256x256 direct, 5 stages", 6: "256x256 direct, 8 waves",
+        7: "256x256 direct, 8 waves + 128x256 tail"},
 }
 
 
@@ -332,7 +333,17 @@ def main(argv=None):
                 for op, (results, rule, _, _) in all_results.items()}
         with open(args.dump, "w") as f:
             json.dump(dump, f)
-    write_table(args.table, entries, header)
+    # Ops not tuned in this run keep their entries from the compiled-in table.
+    tuned_ops = set(all_results)
+    kept = []
+    if os.path.exists(DEFAULT_TABLE):
+        for line in open(DEFAULT_TABLE):
+            line = line.strip()
+            if line.startswith("{") and line.endswith("},"):
+                vals = [int(x) for x in line[1:-2].split(",")]
+                if vals[0] not in tuned_ops:
+                    kept.append(tuple(vals) + (0.0, 0.0))
+    write_table(args.table, kept + entries, header)
     write_report(args.report, all_results, header, command, args.margin)
     log("wrote %s (%d entries) and %s" % (args.table, len(entries), args.report))
 

@@ -19,8 +19,8 @@ from tests.gpu_helpers import FP16_TOL, f16_bits, hgemm_error, note, run_hgemm
 
 pytestmark = pytest.mark.gpu
 
-TILES = (0, 1, 2, 3, 4, 5, 6)   # register-staged 256, 128, 64; direct-to-LDS 256x256, 128x256,
-#                                  256x256 5-stage, 256x256 eight waves
+TILES = (0, 1, 2, 3, 4, 5, 6, 7)   # register-staged 256, 128, 64; direct-to-LDS 256x256,
+#                           128x256, 256x256 5-stage, 256x256 eight waves, eight waves + tail
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -174,6 +174,33 @@ def test_workload_ffn_full_size_sampled():
     ref, den = oracle.hgemm_entries(w.K, w.alpha, f16_bits(A), w.K, f16_bits(B), w.N, bias.numpy(),
                                     oracle.ACT_GELU_TANH, rows, cols)
     e = oracle.normalized_error(got.float().numpy()[rows, cols], ref, den)
+    assert float(e.max()) <= FP16_TOL, "max normalised error %.3g" % e.max()
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(4096, 5120, 128), (2048, 10240, 192)])
+def test_head_and_tail_split(fmt, M, N, K, tile_forced):
+    """Tile 7: eight-wave 256x256 tiles on the columns that fill whole rounds of
+    workgroups, 128x256 tiles on the rest; checked on sampled entries and on every
+    entry of the columns next to the split and at the right edge."""
+    lib.gemm_debug_force_tile(1, 7)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert lib.gemm_debug_pick_config(1, M, N, K, cus)[0] == 7, "no split for this shape"
+    A, B, bias = inputs.hgemm_inputs(M, N, K, 41 + K, fmt=fmt)
+    dt = torch.bfloat16 if fmt == "bf16" else torch.float16
+    C = torch.full((M, N), float("nan"), dtype=dt)
+    note("hgemm head+tail split %s %dx%dx%d" % (fmt, M, N, K))
+    got = run_hgemm(M, N, K, 1.25, A, K, B, N, bias, lib.ACT_GELU_TANH, C, N).cpu().float()
+    assert torch.isfinite(got).all(), "every output written"
+    rows, cols = inputs.sample_indices(M, N, 4096, K)
+    tn = N // 256
+    n1 = max(n for n in range(1, tn) if (M // 256 * n) % cus == 0) * 256
+    edge_cols = np.array([n1 - 1, n1, n1 + 1, N - 1])
+    rows = np.concatenate([rows, np.repeat(np.arange(M), len(edge_cols))])
+    cols = np.concatenate([cols, np.tile(edge_cols, M)])
+    ref, den = oracle.hgemm_entries(K, 1.25, f16_bits(A), K, f16_bits(B), N, bias.numpy(),
+                                    oracle.ACT_GELU_TANH, rows, cols, fmt=fmt)
+    e = oracle.normalized_error(got.numpy()[rows, cols], ref, den)
     assert float(e.max()) <= FP16_TOL, "max normalised error %.3g" % e.max()
 
 
