@@ -173,13 +173,17 @@ struct HStage {
 };
 
 // GELU, tanh form: 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
-// Since 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), this is x / (1 + exp(-2u));
-// it tends to x for large positive x and to -0 for large negative x.
+// Since 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), this is x / (1 + exp(-2u)),
+// computed as x * rcp(1 + 2^t) with t = -2 u log2(e): the hardware base-2
+// exponential and reciprocal (about 1 ulp each, far inside the 16-bit output's
+// rounding) instead of a full-precision division, which costs about ten
+// instructions per element in the epilogue.  It tends to x for large positive x
+// and to -0 for large negative x.
 __device__ __forceinline__ float gelu_tanh(float x) {
-  const float k0 = 0.7978845608028654f;   // sqrt(2 / pi)
   const float k1 = 0.044715f;
-  const float u = k0 * __builtin_fmaf(k1 * x, x * x, x);
-  return x / (1.0f + __expf(-2.0f * u));
+  const float c = -2.302208198f;   // -2 sqrt(2 / pi) log2(e)
+  const float t = c * __builtin_fmaf(k1 * x, x * x, x);
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
 template <class T, bool EDGE>
