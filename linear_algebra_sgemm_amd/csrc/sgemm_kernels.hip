@@ -108,6 +108,9 @@ struct SgemmArgs {
   // and writes its raw partial to ws + y * M * N (M x N, row stride N).
   int k_chunk;
   float* ws;
+  // Bounds-checked path: rows of A (B) are 16-byte aligned, so a 4-float chunk that
+  // lies wholly inside the matrix may be read with one 16-byte load.
+  int a_vec, b_vec;
 };
 
 // Global -> register staging of one K tile.  EDGE selects bounds-checked scalar
@@ -130,9 +133,13 @@ struct Stage {
         a[v] = *reinterpret_cast<const f32x4*>(p.A + (size_t)gm * p.lda + gk);
       } else {
         const float* src = p.A + (size_t)gm * p.lda;
+        if (p.a_vec && gm < p.M && gk + 3 < p.K) {
+          a[v] = *reinterpret_cast<const f32x4*>(src + gk);   // whole chunk inside, 16-byte aligned
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          a[v][e] = (gm < p.M && gk + e < p.K) ? src[gk + e] : 0.0f;
+          for (int e = 0; e < 4; ++e)
+            a[v][e] = (gm < p.M && gk + e < p.K) ? src[gk + e] : 0.0f;
+        }
       }
     }
 #pragma unroll
@@ -146,9 +153,13 @@ struct Stage {
         b[v] = *reinterpret_cast<const f32x4*>(p.B + (size_t)gk * p.ldb + gn);
       } else {
         const float* src = p.B + (size_t)gk * p.ldb;
+        if (p.b_vec && gk < p.K && gn + 3 < p.N) {
+          b[v] = *reinterpret_cast<const f32x4*>(src + gn);   // whole chunk inside, 16-byte aligned
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          b[v][e] = (gk < p.K && gn + e < p.N) ? src[gn + e] : 0.0f;
+          for (int e = 0; e < 4; ++e)
+            b[v][e] = (gk < p.K && gn + e < p.N) ? src[gn + e] : 0.0f;
+        }
       }
     }
   }
@@ -651,6 +662,8 @@ static hipError_t launch_tile(const SgemmCall& c, const SgemmPlan& plan, int gro
   p.group_m = group_m;
   p.k_chunk = plan.k_chunk;
   p.ws = ws;
+  p.a_vec = c.lda % 4 == 0 && aligned16(c.A);
+  p.b_vec = c.ldb % 4 == 0 && aligned16(c.B);
   const bool edge = !(c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % T::BK == 0 &&
                       c.lda % 4 == 0 && c.ldb % 4 == 0 && aligned16(c.A) && aligned16(c.B));
   const bool split = plan.splits > 1;
@@ -691,6 +704,7 @@ static hipError_t launch_sdma(const SgemmCall& c, int group_m, hipStream_t s) {
   p.group_m = group_m;
   p.k_chunk = c.K;
   p.ws = nullptr;
+  p.a_vec = p.b_vec = 1;
   hipLaunchKernelGGL((sgemm_dma_kernel<T>), dim3(p.tiles_m * p.tiles_n), dim3(T::THREADS), 0, s, p);
   return hipGetLastError();
 }
