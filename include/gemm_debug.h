@@ -33,11 +33,12 @@ extern "C" {
 int gemm_debug_force_tile(int op, int tile);
 
 /*
- * Force the number of K chunks (split-K) of later sgemm calls: op 0 only;
- * splits -1 = choose by shape (the default), 1 = never split, 2 .. 32 = that
- * many chunks (still reduced to what K and the workspace allow).  Returns
- * GEMM_STATUS_INVALID_VALUE for another op or count.  Pure host state, not
- * synchronised with calls in flight on other threads.
+ * Force the number of K chunks (split-K) of later calls: op 0 = sgemm, op 1 =
+ * the half products; splits -1 = choose by shape (the default), 1 = never
+ * split, 2 .. 32 = that many chunks (still reduced to what K and the workspace
+ * allow; the half products split only on their register-staged tiles 0-2).
+ * Returns GEMM_STATUS_INVALID_VALUE for another op or count.  Pure host state,
+ * not synchronised with calls in flight on other threads.
  */
 int gemm_debug_force_splits(int op, int splits);
 
@@ -54,8 +55,8 @@ int gemm_debug_use_tuned_table(int on);
  * with `cus` compute units, forced values included: *tile receives the tile
  * configuration, *splits the number of K chunks (1 = no split).  op 0 = sgemm
  * with 16-byte-aligned operands; op 1 = the half products with 16-byte-aligned
- * operands and lda, ldb multiples of 8 (always *splits = 1; a direct-to-LDS
- * tile the shape does not suit is reported as the tile that runs instead).  Returns GEMM_STATUS_INVALID_VALUE for an
+ * operands and lda, ldb multiples of 8 (a direct-to-LDS tile the shape does not
+ * suit is reported as the tile that runs instead).  Returns GEMM_STATUS_INVALID_VALUE for an
  * unknown op, negative sizes, cus <= 0 or a null output pointer.  Pure host
  * computation: no HIP call, no library state needed.
  */

@@ -48,6 +48,7 @@ std::atomic<int> g_cus{256};
 std::atomic<int> g_force_sgemm_tile{-1};
 std::atomic<int> g_force_hgemm_tile{-1};
 std::atomic<int> g_force_sgemm_splits{-1};
+std::atomic<int> g_force_half_splits{-1};
 
 thread_local char t_last_error[256] = "";
 
@@ -58,6 +59,26 @@ int hip_failure(hipError_t e) {
 }
 
 bool ld_ok(int ld, int cols) { return ld >= (cols > 1 ? cols : 1); }
+
+// Runs `launch(ws)` with the split-K workspace, ordered after the previous
+// workspace user when that ran on another stream, and records the event after it.
+template <class F>
+int with_workspace(hipStream_t stream, F launch) {
+  std::lock_guard<std::mutex> wl(g_ws.mu);
+  if (g_ws.ptr == nullptr) return GEMM_STATUS_NOT_INITIALIZED;
+  hipError_t e;
+  if (g_ws.used && g_ws.last != stream) {
+    e = hipStreamWaitEvent(stream, g_ws.done, 0);
+    if (e != hipSuccess) return hip_failure(e);
+  }
+  e = launch(g_ws.ptr);
+  if (e != hipSuccess) return hip_failure(e);
+  e = hipEventRecord(g_ws.done, stream);
+  if (e != hipSuccess) return hip_failure(e);
+  g_ws.last = stream;
+  g_ws.used = true;
+  return GEMM_STATUS_SUCCESS;
+}
 
 }  // namespace
 
@@ -147,17 +168,7 @@ int sgemm(int M, int N, int K, float alpha, const float* A, int lda, const float
         lasg::plan_sgemm(M, N, K, g_cus.load(), g_force_sgemm_tile.load(),
                          g_force_sgemm_splits.load(), g_ws.floats);
     if (plan.splits > 1) {
-      std::lock_guard<std::mutex> wl(g_ws.mu);
-      if (g_ws.ptr == nullptr) return GEMM_STATUS_NOT_INITIALIZED;
-      if (g_ws.used && g_ws.last != stream) {
-        e = hipStreamWaitEvent(stream, g_ws.done, 0);
-        if (e != hipSuccess) return hip_failure(e);
-      }
-      e = lasg::launch_sgemm(c, plan, g_ws.ptr, stream);
-      if (e != hipSuccess) return hip_failure(e);
-      e = hipEventRecord(g_ws.done, stream);
-      g_ws.last = stream;
-      g_ws.used = true;
+      return with_workspace(stream, [&](float* ws) { return lasg::launch_sgemm(c, plan, ws, stream); });
     } else {
       e = lasg::launch_sgemm(c, plan, nullptr, stream);
     }
@@ -182,9 +193,15 @@ int half_product(bool bf16, int M, int N, int K, float alpha, const uint16_t* A,
   // alpha == 0 or K == 0: the product is zero and A, B stay unread; the kernel
   // skips its K loop and still applies bias and activation.
   lasg::HgemmCall c{M, N, reads_ab ? K : 0, alpha, A, lda, B, ldb, bias, act, C, ldc};
-  const int force = g_force_hgemm_tile.load();
-  hipError_t e = bf16 ? lasg::launch_bgemm(c, g_cus.load(), force, stream)
-                      : lasg::launch_hgemm(c, g_cus.load(), force, stream);
+  const int cus = g_cus.load();
+  const lasg::HalfPlan plan = lasg::plan_half_call(c, cus, g_force_hgemm_tile.load(),
+                                                   g_force_half_splits.load(), g_ws.floats);
+  auto launch = [&](float* ws) {
+    return bf16 ? lasg::launch_bgemm(c, plan, cus, ws, stream)
+                : lasg::launch_hgemm(c, plan, cus, ws, stream);
+  };
+  if (plan.splits > 1) return with_workspace(stream, launch);
+  const hipError_t e = launch(nullptr);
   return e == hipSuccess ? GEMM_STATUS_SUCCESS : hip_failure(e);
 }
 
@@ -224,9 +241,9 @@ int gemm_debug_force_tile(int op, int tile) {
 }
 
 int gemm_debug_force_splits(int op, int splits) {
-  if (op != 0) return GEMM_STATUS_INVALID_VALUE;
+  if (op != 0 && op != 1) return GEMM_STATUS_INVALID_VALUE;
   if (splits != -1 && (splits < 1 || splits > lasg::kMaxSplits)) return GEMM_STATUS_INVALID_VALUE;
-  g_force_sgemm_splits.store(splits);
+  (op == 0 ? g_force_sgemm_splits : g_force_half_splits).store(splits);
   return GEMM_STATUS_SUCCESS;
 }
 
@@ -248,10 +265,11 @@ int gemm_debug_pick_config(int op, int M, int N, int K, int cus, int* tile, int*
     return GEMM_STATUS_SUCCESS;
   }
   if (op == 1) {
-    const int forced = g_force_hgemm_tile.load();
-    *tile = lasg::hgemm_resolve_tile(forced >= 0 ? forced : lasg::hgemm_pick_tile(M, N, K, cus, true),
-                                     M, N, K, true, cus);
-    *splits = 1;
+    const lasg::HalfPlan p =
+        lasg::plan_half(M, N, K, cus, g_force_hgemm_tile.load(), g_force_half_splits.load(),
+                        lasg::kWorkspaceBytes / sizeof(float), true);
+    *tile = p.tile;
+    *splits = p.splits;
     return GEMM_STATUS_SUCCESS;
   }
   return GEMM_STATUS_INVALID_VALUE;

@@ -124,21 +124,75 @@ SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_spl
   return p;
 }
 
-int hgemm_pick_tile(int M, int N, int K, int cus, bool operands_ok) {
-  int tuned_tile = -1, tuned_splits = 1;
-  if (tuned_config(1, M, N, K, &tuned_tile, &tuned_splits) && tuned_tile >= 0 &&
-      tuned_tile < kHgemmTileCount)
-    return tuned_tile;
+namespace {
+
+int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   // Built-in rule (from the size sweep): 256x256 tiles once they give every CU
-  // one and K is at least 512 (the direct-to-LDS kernel when the shape and
-  // operands allow it); 128x128 tiles once they give every CU two; else 64x64
-  // tiles, which spread small outputs over the most CUs.
+  // one and K is at least 512 -- with direct-to-LDS copies when the shape and
+  // operands allow it: eight waves with the head/tail column split (tile 7, which
+  // runs as tile 6 where no split exists) for K >= 2048, four waves (tile 3) for
+  // shorter K, where the eight-wave tile lost up to 14 % -- else 128x128 tiles
+  // once they give every CU two, else 64x64 tiles, which spread small outputs
+  // over the most CUs.
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
-  if (t_large >= cus && K >= 512)
-    return (M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && operands_ok) ? 3 : 0;
+  if (t_large >= cus && K >= 512) {
+    if (!(M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && operands_ok)) return 0;
+    return K >= 2048 ? 7 : 3;
+  }
   if (t_med >= 2L * cus) return 1;
   return 2;
+}
+
+// Built-in split rule of the half products, as for FP32: split K (register-
+// staged tiles only) when the tiles do not cover the CUs and K is at least 512,
+// aiming at four workgroups per CU with chunks of at least 128.
+int half_rule_splits(int M, int N, int K, int tile, int cus) {
+  if (tile > 2) return 1;
+  const long tiles = ceil_div(M, half_tile_bm(tile)) * ceil_div(N, half_tile_bm(tile));
+  if (tiles >= cus || K < 512) return 1;
+  const long by_cus = ceil_div(4L * cus, tiles);
+  const long by_k = ceil_div(K, kHalfBK) * kHalfBK / 128;
+  long s = by_cus < by_k ? by_cus : by_k;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : (int)s;
+}
+
+}  // namespace
+
+HalfPlan plan_half(int M, int N, int K, int cus, int force_tile, int force_splits,
+                   size_t ws_floats, bool operands_ok) {
+  int tuned_tile = -1, tuned_splits = -1;
+  const bool tuned = tuned_config(1, M, N, K, &tuned_tile, &tuned_splits) && tuned_tile >= 0 &&
+                     tuned_tile < kHgemmTileCount && tuned_splits >= 1;
+  HalfPlan p;
+  p.tile = force_tile >= 0 ? force_tile
+           : tuned         ? tuned_tile
+                           : half_rule_tile(M, N, K, cus, operands_ok);
+  p.tile = hgemm_resolve_tile(p.tile, M, N, K, operands_ok, cus);
+  long s = force_splits > 0 ? force_splits
+           : (tuned && force_tile < 0) ? tuned_splits
+                                       : half_rule_splits(M, N, K, p.tile, cus);
+  // Legality: register-staged tiles only, whole K steps per chunk, no empty
+  // chunk, partials fit the workspace.
+  const long ktiles = ceil_div(K, kHalfBK);
+  const long mn = (long)M * N;
+  if (p.tile > 2) s = 1;
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s > ktiles) s = ktiles;
+  if (mn > 0 && s > (long)(ws_floats / (size_t)mn)) s = (long)(ws_floats / (size_t)mn);
+  long chunk = K;
+  if (s > 1) {
+    chunk = ceil_div(ktiles, s) * kHalfBK;
+    s = ceil_div(K, chunk);
+  }
+  if (s <= 1) {
+    s = 1;
+    chunk = K;
+  }
+  p.splits = (int)s;
+  p.k_chunk = (int)chunk;
+  return p;
 }
 
 }  // namespace lasg

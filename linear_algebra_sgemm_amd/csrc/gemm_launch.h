@@ -87,9 +87,27 @@ int sgemm_resolve_tile(int tile, int M, int N, int K, int splits, bool operands_
 // size class: op 0 = sgemm, op 1 = the half products.
 bool tuned_config(int op, int M, int N, int K, int* tile, int* splits);
 
-// Tile configuration of the half products (`operands_ok`: lda and ldb are
-// multiples of 8 and A, B 16-byte aligned, as the direct-to-LDS kernels need).
-int hgemm_pick_tile(int M, int N, int K, int cus, bool operands_ok);
+// How one half-product call runs: tile configuration, number of K chunks (1 =
+// no split; only the register-staged tiles 0-2 split) and the chunk length.
+struct HalfPlan {
+  int tile;
+  int splits;
+  int k_chunk;
+};
+// Output tile of the register-staged half configurations 0-2 (K step 64).
+constexpr int half_tile_bm(int tile) { return tile == 0 ? 256 : tile == 1 ? 128 : 64; }
+constexpr int kHalfBK = 64;
+
+// The plan for an M x N x K half product on `cus` compute units (`operands_ok`:
+// lda and ldb are multiples of 8 and A, B 16-byte aligned, as the direct-to-LDS
+// kernels need).  force_tile / force_splits < 0 let the shape decide (tuned
+// table, else the built-in rule); the result is resolved to what runs and the
+// split count is clamped to the K tiles and to `ws_floats` of workspace.
+HalfPlan plan_half(int M, int N, int K, int cus, int force_tile, int force_splits,
+                   size_t ws_floats, bool operands_ok);
+// plan_half with the operand conditions read from the call.
+HalfPlan plan_half_call(const HgemmCall& c, int cus, int force_tile, int force_splits,
+                        size_t ws_floats);
 // The configuration that actually runs for `tile`: the direct-to-LDS ones (3,
 // 4) become the register-staged 256x256 one (0) when the shape or operands do
 // not suit them.
@@ -110,7 +128,10 @@ hipError_t launch_sgemm_scale(int M, int N, float beta, float* C, int ldc, hipSt
 
 // The half-precision product: binary16 (hgemm) or bfloat16 (bgemm) inputs and
 // output, FP32 accumulation; same kernels, tiles and tile choice.
-hipError_t launch_hgemm(const HgemmCall& c, int cus, int force_tile, hipStream_t s);
-hipError_t launch_bgemm(const HgemmCall& c, int cus, int force_tile, hipStream_t s);
+// `ws` holds at least plan.splits * M * N floats when plan.splits > 1.
+hipError_t launch_hgemm(const HgemmCall& c, const HalfPlan& plan, int cus, float* ws,
+                        hipStream_t s);
+hipError_t launch_bgemm(const HgemmCall& c, const HalfPlan& plan, int cus, float* ws,
+                        hipStream_t s);
 
 }  // namespace lasg

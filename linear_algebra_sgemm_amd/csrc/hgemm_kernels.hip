@@ -88,6 +88,11 @@ struct HgemmArgs {
   uint16_t* C;
   int ldc;
   int tiles_m, tiles_n, group_m;
+  // Split-K (register-staged kernel): workgroup row blockIdx.y covers K range
+  // [y * k_chunk, min(K, (y + 1) * k_chunk)) and writes its raw FP32 partial to
+  // ws + y * M * N (M x N, row stride N).
+  int k_chunk;
+  float* ws;
 };
 
 template <class T, bool EDGE>
@@ -186,8 +191,16 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
-template <class T, bool EDGE>
+template <class T, bool EDGE, bool SPLIT>
 __global__ void __launch_bounds__(T::THREADS) hgemm_mfma_kernel(HgemmArgs p) {
+  if constexpr (SPLIT) {
+    // This workgroup's K chunk (a multiple of BK): shift A and B, shorten K.
+    const int kbeg = blockIdx.y * p.k_chunk;
+    const int klen = p.K - kbeg < p.k_chunk ? p.K - kbeg : p.k_chunk;
+    p.A += kbeg;
+    p.B += (size_t)kbeg * p.ldb;
+    p.K = klen;
+  }
   __shared__ __attribute__((aligned(16))) uint16_t lds[T::LDS_HALVES];
   uint16_t* const As0 = lds;
   uint16_t* const Bt0 = lds + T::A_STAGE;
@@ -252,6 +265,24 @@ __global__ void __launch_bounds__(T::THREADS) hgemm_mfma_kernel(HgemmArgs p) {
 
     if (more) st.store(odd ? As0 : As1, odd ? Bt0 : Bt1, tid);
     __syncthreads();
+  }
+
+  if constexpr (SPLIT) {
+    // Raw partial sums into this K chunk's slice of the workspace.
+    float* W = p.ws + (size_t)blockIdx.y * p.M * p.N;
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+      const int col = n0 + wn * T::WTN + j * 32 + l32;
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * T::WTM + i * 32 + mfma32_row(r, lane);
+          if (EDGE && (row >= p.M || col >= p.N)) continue;
+          W[(size_t)row * p.N + col] = acc[i][j][r];
+        }
+    }
+    return;
   }
 
   // Epilogue: x = alpha * acc + bias[col]; y = act(x); C = fp16(y).
@@ -724,8 +755,28 @@ template <class E> using HDmaEight = HDmaTile<E, 256, 256, 32, 4, 2, 2, 4>;
 // CU holds one workgroup and a round of them spreads over every CU.
 template <class E> using HDmaHalfEight = HDmaTile<E, 128, 256, 32, 4, 2, 2, 4>;
 
+// Second half of split-K: C = act(alpha * (sum of the `splits` partials, added
+// in order 0, 1, ...) + bias[col]), rounded to the 16-bit format.
+template <class E>
+__global__ void __launch_bounds__(256) half_splitk_reduce_kernel(int M, int N, int splits,
+                                                                 const float* ws, float alpha,
+                                                                 const float* bias, int act,
+                                                                 uint16_t* C, int ldc) {
+  const int64_t total = (int64_t)M * N;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    float sum = ws[t];
+    for (int q = 1; q < splits; ++q) sum += ws[q * total + t];
+    const int64_t i = t / N, j = t % N;
+    float x = __builtin_fmaf(alpha, sum, bias != nullptr ? bias[j] : 0.0f);
+    if (act == 1) x = gelu_tanh(x);
+    C[i * ldc + j] = E::bits(x);
+  }
+}
+
 template <class T>
-static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s) {
+static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s, int splits = 1,
+                               int k_chunk = 0, float* ws = nullptr) {
   HgemmArgs p;
   p.M = c.M; p.N = c.N; p.K = c.K;
   p.alpha = c.alpha;
@@ -735,15 +786,33 @@ static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s) {
   p.tiles_m = (c.M + T::BM - 1) / T::BM;
   p.tiles_n = (c.N + T::BN - 1) / T::BN;
   p.group_m = group_m;
+  p.k_chunk = k_chunk;
+  p.ws = ws;
   const bool fast = c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % T::BK == 0 &&
                     c.lda % 8 == 0 && c.ldb % 8 == 0 &&
                     (reinterpret_cast<uintptr_t>(c.A) & 15u) == 0 &&
                     (reinterpret_cast<uintptr_t>(c.B) & 15u) == 0;
+  if (splits > 1) {
+    if (ws == nullptr || k_chunk % T::BK != 0) return hipErrorInvalidValue;
+    const dim3 grid(p.tiles_m * p.tiles_n, splits), block(T::THREADS);
+    if (fast)
+      hipLaunchKernelGGL((hgemm_mfma_kernel<T, false, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((hgemm_mfma_kernel<T, true, true>), grid, block, 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t total = (int64_t)c.M * c.N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(half_splitk_reduce_kernel<typename T::E>, dim3((unsigned)blocks), dim3(256),
+                       0, s, c.M, c.N, splits, (const float*)ws, c.alpha, c.bias, c.act, c.C, c.ldc);
+    return hipGetLastError();
+  }
   const dim3 grid(p.tiles_m * p.tiles_n), block(T::THREADS);
   if (fast)
-    hipLaunchKernelGGL((hgemm_mfma_kernel<T, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((hgemm_mfma_kernel<T, false, false>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((hgemm_mfma_kernel<T, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((hgemm_mfma_kernel<T, true, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
@@ -806,18 +875,32 @@ int hgemm_resolve_tile(int tile, int M, int N, int K, bool operands_ok, int cus)
   return tile;
 }
 
-template <class E>
-static hipError_t launch_half(const HgemmCall& c, int cus, int force_tile, hipStream_t s) {
+static bool half_operands_ok(const HgemmCall& c) {
   // The direct loads address A and B as a tile base plus a 32-bit byte offset
   // of at most 256 rows of A or 32 rows of B.
-  const bool operands_ok = c.lda % 8 == 0 && c.ldb % 8 == 0 &&
-                           (reinterpret_cast<uintptr_t>(c.A) & 15u) == 0 &&
-                           (reinterpret_cast<uintptr_t>(c.B) & 15u) == 0 &&
-                           (int64_t)c.lda * 256 * 2 < (int64_t(1) << 31) &&
-                           (int64_t)c.ldb * 32 * 2 < (int64_t(1) << 31);
-  int tile = force_tile >= 0 ? force_tile : hgemm_pick_tile(c.M, c.N, c.K, cus, operands_ok);
-  tile = hgemm_resolve_tile(tile, c.M, c.N, c.K, operands_ok, cus);
-  switch (tile) {
+  return c.lda % 8 == 0 && c.ldb % 8 == 0 && (reinterpret_cast<uintptr_t>(c.A) & 15u) == 0 &&
+         (reinterpret_cast<uintptr_t>(c.B) & 15u) == 0 &&
+         (int64_t)c.lda * 256 * 2 < (int64_t(1) << 31) &&
+         (int64_t)c.ldb * 32 * 2 < (int64_t(1) << 31);
+}
+
+HalfPlan plan_half_call(const HgemmCall& c, int cus, int force_tile, int force_splits,
+                        size_t ws_floats) {
+  return plan_half(c.M, c.N, c.K, cus, force_tile, force_splits, ws_floats, half_operands_ok(c));
+}
+
+template <class E>
+static hipError_t launch_half(const HgemmCall& c, const HalfPlan& plan, int cus, float* ws,
+                              hipStream_t s) {
+  if (plan.splits > 1) {
+    if (plan.tile > 2 || ws == nullptr) return hipErrorInvalidValue;
+    switch (plan.tile) {
+      case 0: return launch_htile<HTileLarge<E>>(c, 4, s, plan.splits, plan.k_chunk, ws);
+      case 1: return launch_htile<HTileMedium<E>>(c, 8, s, plan.splits, plan.k_chunk, ws);
+      default: return launch_htile<HTileSmall<E>>(c, 8, s, plan.splits, plan.k_chunk, ws);
+    }
+  }
+  switch (plan.tile) {
     case 0: return launch_htile<HTileLarge<E>>(c, 4, s);
     case 1: return launch_htile<HTileMedium<E>>(c, 8, s);
     case 2: return launch_htile<HTileSmall<E>>(c, 8, s);
@@ -853,12 +936,14 @@ static hipError_t launch_half(const HgemmCall& c, int cus, int force_tile, hipSt
   }
 }
 
-hipError_t launch_hgemm(const HgemmCall& c, int cus, int force_tile, hipStream_t s) {
-  return launch_half<EltF16>(c, cus, force_tile, s);
+hipError_t launch_hgemm(const HgemmCall& c, const HalfPlan& plan, int cus, float* ws,
+                        hipStream_t s) {
+  return launch_half<EltF16>(c, plan, cus, ws, s);
 }
 
-hipError_t launch_bgemm(const HgemmCall& c, int cus, int force_tile, hipStream_t s) {
-  return launch_half<EltBF16>(c, cus, force_tile, s);
+hipError_t launch_bgemm(const HgemmCall& c, const HalfPlan& plan, int cus, float* ws,
+                        hipStream_t s) {
+  return launch_half<EltBF16>(c, plan, cus, ws, s);
 }
 
 }  // namespace lasg

@@ -127,33 +127,28 @@ def candidates(op, M, N, K, cus):
     """Distinct (tile, splits) the library would run, over every forced pair."""
     seen = []
     tiles = SGEMM_TILES if op == 0 else HALF_TILES
-    splits = SPLITS if op == 0 else (1,)
     try:
         for t in tiles:
             lib.gemm_debug_force_tile(op, t)
-            for s in splits:
-                if op == 0:
-                    lib.gemm_debug_force_splits(0, s)
+            for s in SPLITS:
+                lib.gemm_debug_force_splits(op, s)
                 cfg = lib.gemm_debug_pick_config(op, M, N, K, cus)
                 if cfg not in seen:
                     seen.append(cfg)
     finally:
         lib.gemm_debug_force_tile(op, -1)
-        if op == 0:
-            lib.gemm_debug_force_splits(0, -1)
+        lib.gemm_debug_force_splits(op, -1)
     return seen
 
 
 def force(op, cfg):
     lib.gemm_debug_force_tile(op, cfg[0])
-    if op == 0:
-        lib.gemm_debug_force_splits(0, cfg[1])
+    lib.gemm_debug_force_splits(op, cfg[1])
 
 
 def unforce(op):
     lib.gemm_debug_force_tile(op, -1)
-    if op == 0:
-        lib.gemm_debug_force_splits(0, -1)
+    lib.gemm_debug_force_splits(op, -1)
 
 
 def size_class(x):

@@ -157,12 +157,17 @@ def test_config_rule(so):
         (0, 4096, 4096, 4096, 64, (9, 1)),
         (0, 128, 128, 16384, 256, (2, 32)),   # 4 tiles; 256 chunks by CUs, capped at 32
         (0, 1024, 1024, 4096, 256, (2, 1)),   # 256 tiles of 64x64 cover the CUs
-        (1, 4096, 14336, 4096, 256, (3, 1)),  # whole 256-tiles: direct-to-LDS kernel
+        (1, 4096, 14336, 4096, 256, (7, 1)),  # whole 256-tiles, long K: eight waves + tail split
+        (1, 4096, 4096, 4096, 256, (6, 1)),   # no partial round: eight waves, no split
+        (1, 4096, 4096, 1024, 256, (3, 1)),   # shorter K: four waves
         (1, 4096, 4000, 4096, 256, (0, 1)),
         (1, 2048, 2000, 4096, 256, (2, 1)),
         (1, 4096, 2048, 4096, 256, (1, 1)),   # 512 tiles of 128x128
         (1, 4096, 4096, 256, 256, (1, 1)),    # K < 512: not the 256x256 tiles
-        (1, 300, 500, 4096, 256, (2, 1)),
+        (1, 300, 500, 4096, 256, (2, 22)),     # 40 tiles of 64x64: ~4 workgroups per CU
+        (1, 1024, 1024, 4096, 256, (2, 1)),    # 256 tiles of 64x64 cover the CUs
+        (1, 512, 512, 4096, 256, (2, 16)),     # 64 tiles; 16 chunks of 256
+        (1, 512, 512, 256, 256, (2, 1)),       # K < 512: no split
     ]
     assert lib.gemm_debug_use_tuned_table(False) == lib.STATUS_SUCCESS
     try:
@@ -197,27 +202,45 @@ def test_sgemm_direct_tile_resolution(so):
         lib.gemm_debug_force_splits(0, -1)
 
 
+def test_half_split_legality(so):
+    """The half products split only on register-staged tiles, in whole K steps of 64."""
+    try:
+        assert lib.gemm_debug_force_splits(1, 8) == lib.STATUS_SUCCESS
+        assert lib.gemm_debug_force_tile(1, 2) == lib.STATUS_SUCCESS
+        assert pick(1, 256, 256, 4096) == (2, 8)       # 64 K steps, 8 per chunk
+        assert pick(1, 256, 256, 200) == (2, 4)        # 4 K steps only
+        assert lib.gemm_debug_force_tile(1, 6) == lib.STATUS_SUCCESS
+        assert pick(1, 4096, 4096, 4096) == (6, 1)     # direct-to-LDS tiles never split
+        assert lib.gemm_debug_force_tile(1, 0) == lib.STATUS_SUCCESS
+        assert lib.gemm_debug_force_splits(1, 32) == lib.STATUS_SUCCESS
+        assert pick(1, 4096, 4096, 4096) == (0, 1)     # 32 x 64 MiB exceeds the workspace
+        assert pick(1, 1024, 1024, 8192) == (0, 16)    # 16 M floats: 16 partials fit
+    finally:
+        lib.gemm_debug_force_tile(1, -1)
+        lib.gemm_debug_force_splits(1, -1)
+
+
 def test_half_tile_resolution(so):
     """A forced direct-to-LDS tile that the shape does not suit is reported (and run)
     as the register-staged 256x256 configuration."""
     try:
         assert lib.gemm_debug_force_tile(1, 3) == lib.STATUS_SUCCESS
-        assert pick(1, 4096, 4096, 4096) == (3, 1)
-        assert pick(1, 300, 512, 4096) == (0, 1)
-        assert pick(1, 512, 512, 96) == (0, 1)
+        assert pick(1, 4096, 4096, 4096)[0] == 3
+        assert pick(1, 300, 512, 4096)[0] == 0
+        assert pick(1, 512, 512, 96)[0] == 0
         assert lib.gemm_debug_force_tile(1, 4) == lib.STATUS_SUCCESS
-        assert pick(1, 128, 256, 64) == (4, 1)
-        assert pick(1, 128, 128, 64) == (0, 1)
+        assert pick(1, 128, 256, 64)[0] == 4
+        assert pick(1, 128, 128, 64)[0] == 0
         assert lib.gemm_debug_force_tile(1, 1) == lib.STATUS_SUCCESS
-        assert pick(1, 128, 128, 64) == (1, 1)
+        assert pick(1, 128, 128, 64)[0] == 1
         # tile 7 splits the columns only where whole rounds plus one short round exist
         assert lib.gemm_debug_force_tile(1, 7) == lib.STATUS_SUCCESS
-        assert pick(1, 4096, 14336, 4096) == (7, 1)    # 768 + 256 half tiles
-        assert pick(1, 4096, 4096, 4096) == (6, 1)     # 256 tiles: whole rounds already
-        assert pick(1, 4096, 5120, 128) == (7, 1)
-        assert pick(1, 4096, 5120, 128, cus=128) == (7, 1)   # 2 rounds + 128 half tiles
-        assert pick(1, 4096, 5120, 128, cus=64) == (6, 1)    # the tail would need 2 rounds
-        assert pick(1, 300, 5120, 128) == (0, 1)
+        assert pick(1, 4096, 14336, 4096)[0] == 7    # 768 + 256 half tiles
+        assert pick(1, 4096, 4096, 4096)[0] == 6     # 256 tiles: whole rounds already
+        assert pick(1, 4096, 5120, 128)[0] == 7
+        assert pick(1, 4096, 5120, 128, cus=128)[0] == 7   # 2 rounds + 128 half tiles
+        assert pick(1, 4096, 5120, 128, cus=64)[0] == 6    # the tail would need 2 rounds
+        assert pick(1, 300, 5120, 128)[0] == 0
     finally:
         lib.gemm_debug_force_tile(1, -1)
 
@@ -290,7 +313,8 @@ def test_forced_splits(so):
         lib.gemm_debug_force_splits(0, -1)
     assert lib.gemm_debug_force_splits(0, 0) == lib.STATUS_INVALID_VALUE
     assert lib.gemm_debug_force_splits(0, 33) == lib.STATUS_INVALID_VALUE
-    assert lib.gemm_debug_force_splits(1, 2) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_splits(2, 2) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_splits(1, 33) == lib.STATUS_INVALID_VALUE
     assert lib.gemm_debug_force_splits(0, -1) == lib.STATUS_SUCCESS
     with pytest.raises(lib.GemmError):
         pick(2, 300, 500, 64)
