@@ -18,7 +18,7 @@ extern "C" {
  * largest tile, 1 = medium, 2 = small; sgemm also has 3 = largest tile with a
  * K step of 32, 4 = 128 x 256 tiles at two workgroups per compute unit, 5
  * and 6 = tiles 0 and 4 built from 16 x 16 x 4 MFMA blocks, and 7 and 8 = tiles
- * 0 and 4 with direct-to-LDS copies (whole tiles and no K split only, else
+ * 0 and 4 with direct-to-LDS copies (whole tiles and K a multiple of 32 only, else
  * tile 4), 9 = tile 7 with eight waves; the
  * half products also have 3 = 256 x 256 and 4 = 128 x 256 direct-to-LDS kernels
  * 5 = the 256 x 256 one with a five-stage pipeline, 6 = the 256 x 256 one

@@ -54,7 +54,11 @@ int sgemm_rule_tile(int M, int N, int K, int cus) {
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_tall = ceil_div(M, 128) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
-  if (t_large >= cus && M % 256 == 0 && N % 256 == 0 && K % 32 == 0) return 9;
+  const bool whole = M % 256 == 0 && N % 256 == 0 && K % 32 == 0;
+  if (whole && t_large >= cus) return 9;
+  // Fewer whole 256x256 tiles than CUs: the same kernel with K split over up to
+  // eight chunks of at least 512, one workgroup per CU.
+  if (whole && 8 * t_large >= cus && K / ceil_div(cus, t_large) >= 512) return 9;
   if (t_tall >= 2L * cus) return 4;
   if (t_med >= 2L * cus) return 1;
   return 2;
@@ -62,11 +66,13 @@ int sgemm_rule_tile(int M, int N, int K, int cus) {
 
 // Built-in split rule (from the size sweep): when the output has fewer tiles
 // than there are CUs and K is at least 512, split K until there are about four
-// workgroups per CU (small tiles share a CU), keeping chunks of at least 128.
+// workgroups per CU (small tiles share a CU; the 256x256 direct-to-LDS tiles
+// fill one CU each, so one per CU), keeping chunks of at least 128.
 int sgemm_rule_splits(int M, int N, int K, int tile, int cus) {
   const long tiles = ceil_div(M, sgemm_tile_bm(tile)) * ceil_div(N, sgemm_tile_bn(tile));
   if (tiles >= cus || K < 512) return 1;
-  const long by_cus = ceil_div(4L * cus, tiles);
+  const long per_cu = (tile == 7 || tile == 9) ? 1 : 4;
+  const long by_cus = ceil_div(per_cu * cus, tiles);
   const long by_k = ceil_div(K, sgemm_tile_bk(tile)) * sgemm_tile_bk(tile) / 128;
   long s = by_cus < by_k ? by_cus : by_k;
   if (s > kMaxSplits) s = kMaxSplits;

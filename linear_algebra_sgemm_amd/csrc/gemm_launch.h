@@ -47,8 +47,9 @@ struct HgemmCall {
 constexpr int kSgemmTileCount = 10;
 constexpr int kHgemmTileCount = 8;
 
-// K step of each SGEMM tile configuration (checked against the kernels).
-constexpr int sgemm_tile_bk(int tile) { return tile == 3 ? 32 : 16; }
+// K granularity of each SGEMM tile configuration: the K step, or for the
+// direct-to-LDS tiles (7-9) their two-tile loop body (checked against the kernels).
+constexpr int sgemm_tile_bk(int tile) { return tile == 3 || tile >= 7 ? 32 : 16; }
 // Output tile of each SGEMM configuration.
 constexpr int sgemm_tile_bm(int tile) {
   return tile == 0 || tile == 3 || tile == 5 || tile == 7 || tile == 9 ? 256 : tile == 2 ? 64 : 128;
@@ -78,9 +79,9 @@ struct SgemmPlan {
 SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_splits,
                      size_t ws_floats);
 // The FP32 configuration that actually runs for `tile` with `splits` K chunks:
-// the direct-to-LDS ones (7, 8, 9) become 4 when the shape, the operands
-// (`operands_ok`: lda, ldb multiples of 4, A and B 16-byte aligned) or a K
-// split do not suit them.
+// the direct-to-LDS ones (7, 8, 9) become 4 when the shape or the operands
+// (`operands_ok`: lda, ldb multiples of 4, A and B 16-byte aligned) do not
+// suit them.
 int sgemm_resolve_tile(int tile, int M, int N, int K, int splits, bool operands_ok);
 
 // Offline-tuned choice for (op, M, N, K) if the table has one for the shape's

@@ -530,10 +530,18 @@ __device__ __forceinline__ void sdma_tile(const SgemmArgs& p, f32x16 (&acc)[T::F
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <class T>
+template <class T, bool SPLIT>
 __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(T::WAVES_PER_SIMD)))
 sgemm_dma_kernel(SgemmArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[T::STAGES * T::STAGE_BYTES];
+  if constexpr (SPLIT) {
+    // This workgroup's K chunk (a multiple of 2 BK): shift A and B, shorten K.
+    const int kbeg = blockIdx.y * p.k_chunk;
+    const int klen = p.K - kbeg < p.k_chunk ? p.K - kbeg : p.k_chunk;
+    p.A += kbeg;
+    p.B += (size_t)kbeg * p.ldb;
+    p.K = klen;
+  }
 
   int tile_m, tile_n;
   tile_of_workgroup(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
@@ -588,6 +596,22 @@ sgemm_dma_kernel(SgemmArgs p) {
     sdma_tile<T, false>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, plan, a_tile,
                         b_tile, wave, wm, wn, lane);
   }
+  if constexpr (SPLIT) {
+    // Raw partial sums into this K chunk's slice of the workspace.
+    float* W = p.ws + (size_t)blockIdx.y * p.M * p.N;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) {
+        const int col = n0 + wn * T::WTN + j * 32 + lane % 32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * T::WTM + i * 32 + mfma32_row(r, lane);
+          W[(size_t)row * p.N + col] = acc[i][j][r];
+        }
+      }
+    return;
+  }
   sgemm_store<T, false>(p, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
 }
 
@@ -634,11 +658,11 @@ static_assert(TileLarge::BK == sgemm_tile_bk(0) && TileMedium::BK == sgemm_tile_
                   TileTall16::BK == sgemm_tile_bk(6) && TileLarge16::BM == sgemm_tile_bm(5) &&
                   TileLarge16::BN == sgemm_tile_bn(5) && TileTall16::BM == sgemm_tile_bm(6) &&
                   TileTall16::BN == sgemm_tile_bn(6) && TileTall::BM == sgemm_tile_bm(4) &&
-                  SDmaLarge::BK == sgemm_tile_bk(7) && SDmaTall::BK == sgemm_tile_bk(8) &&
+                  2 * SDmaLarge::BK == sgemm_tile_bk(7) && 2 * SDmaTall::BK == sgemm_tile_bk(8) &&
                   SDmaLarge::BM == sgemm_tile_bm(7) && SDmaLarge::BN == sgemm_tile_bn(7) &&
                   SDmaTall::BM == sgemm_tile_bm(8) && SDmaTall::BN == sgemm_tile_bn(8) &&
                   SDmaEight::BM == sgemm_tile_bm(9) && SDmaEight::BN == sgemm_tile_bn(9) &&
-                  SDmaEight::BK == sgemm_tile_bk(9),
+                  2 * SDmaEight::BK == sgemm_tile_bk(9),
               "the host-side planner's K steps must match the tiles");
 
 static hipError_t launch_reduce(const SgemmCall& c, int splits, const float* ws, hipStream_t s) {
@@ -693,8 +717,11 @@ static bool sdma_fits(const SgemmCall& c) {
 }
 
 template <class T>
-static hipError_t launch_sdma(const SgemmCall& c, int group_m, hipStream_t s) {
+static hipError_t launch_sdma(const SgemmCall& c, const SgemmPlan& plan, int group_m, float* ws,
+                              hipStream_t s) {
   if (!sdma_fits<T>(c)) return hipErrorInvalidValue;
+  if (plan.splits > 1 && (ws == nullptr || plan.k_chunk % (2 * T::BK) != 0))
+    return hipErrorInvalidValue;
   SgemmArgs p;
   p.M = c.M; p.N = c.N; p.K = c.K;
   p.alpha = c.alpha; p.beta = c.beta;
@@ -702,18 +729,27 @@ static hipError_t launch_sdma(const SgemmCall& c, int group_m, hipStream_t s) {
   p.tiles_m = c.M / T::BM;
   p.tiles_n = c.N / T::BN;
   p.group_m = group_m;
-  p.k_chunk = c.K;
-  p.ws = nullptr;
+  p.k_chunk = plan.splits > 1 ? plan.k_chunk : c.K;
+  p.ws = ws;
   p.a_vec = p.b_vec = 1;
-  hipLaunchKernelGGL((sgemm_dma_kernel<T>), dim3(p.tiles_m * p.tiles_n), dim3(T::THREADS), 0, s, p);
+  if (plan.splits > 1) {
+    hipLaunchKernelGGL((sgemm_dma_kernel<T, true>), dim3(p.tiles_m * p.tiles_n, plan.splits),
+                       dim3(T::THREADS), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_reduce(c, plan.splits, ws, s);
+  }
+  hipLaunchKernelGGL((sgemm_dma_kernel<T, false>), dim3(p.tiles_m * p.tiles_n), dim3(T::THREADS), 0,
+                     s, p);
   return hipGetLastError();
 }
 
 int sgemm_resolve_tile(int tile, int M, int N, int K, int splits, bool operands_ok) {
-  // The direct-to-LDS kernels need whole tiles, K a multiple of 32, aligned
-  // operands and no K split; otherwise the register-staged 128 x 256 kernel
-  // (the best of those for large outputs) runs.
-  const bool whole = operands_ok && N % 256 == 0 && K % 32 == 0 && splits == 1;
+  // The direct-to-LDS kernels need whole tiles, K a multiple of 32 and aligned
+  // operands (K chunks of a split are multiples of 32 too); otherwise the
+  // register-staged 128 x 256 kernel (the best of those for large outputs) runs.
+  (void)splits;
+  const bool whole = operands_ok && N % 256 == 0 && K % 32 == 0;
   if (tile == 7 && !(whole && M % 256 == 0)) return 4;
   if (tile == 8 && !(whole && M % 128 == 0)) return 4;
   if (tile == 9 && !(whole && M % 256 == 0)) return 4;
@@ -733,9 +769,9 @@ hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hi
     case 4: return launch_tile<TileTall>(c, plan, 8, ws, s);
     case 5: return launch_tile<TileLarge16>(c, plan, 4, ws, s);
     case 6: return launch_tile<TileTall16>(c, plan, 8, ws, s);
-    case 7: return launch_sdma<SDmaLarge>(c, 4, s);
-    case 8: return launch_sdma<SDmaTall>(c, 8, s);
-    case 9: return launch_sdma<SDmaEight>(c, 4, s);
+    case 7: return launch_sdma<SDmaLarge>(c, plan, 4, ws, s);
+    case 8: return launch_sdma<SDmaTall>(c, plan, 8, ws, s);
+    case 9: return launch_sdma<SDmaEight>(c, plan, 4, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -153,10 +153,12 @@ def test_config_rule(so):
         (0, 256, 256, 1024, 256, (2, 8)),     # 16 tiles; chunks of 128
         (0, 512, 512, 512, 256, (2, 4)),      # 64 tiles; chunks of 128
         (0, 1000, 3000, 777, 256, (2, 1)),    # 752 tiles
-        (0, 2048, 2048, 2048, 256, (2, 1)),
+        (0, 2048, 2048, 2048, 256, (9, 4)),   # 64 whole tiles: direct-to-LDS, 4 chunks of 512
+        (0, 2048, 2048, 8192, 256, (9, 4)),
+        (0, 1024, 2048, 4096, 256, (9, 8)),   # 32 whole tiles, 8 chunks of 512
+        (0, 1024, 1024, 4096, 256, (2, 1)),   # 16 whole tiles would need chunks under 512
         (0, 4096, 4096, 4096, 64, (9, 1)),
         (0, 128, 128, 16384, 256, (2, 32)),   # 4 tiles; 256 chunks by CUs, capped at 32
-        (0, 1024, 1024, 4096, 256, (2, 1)),   # 256 tiles of 64x64 cover the CUs
         (1, 4096, 14336, 4096, 256, (7, 1)),  # whole 256-tiles, long K: eight waves + tail split
         (1, 4096, 4096, 4096, 256, (6, 1)),   # no partial round: eight waves, no split
         (1, 4096, 4096, 1024, 256, (3, 1)),   # shorter K: four waves
@@ -184,7 +186,7 @@ def test_config_rule(so):
 
 
 def test_sgemm_direct_tile_resolution(so):
-    """The FP32 direct-to-LDS tiles run only on whole tiles without a K split."""
+    """The FP32 direct-to-LDS tiles run only on whole tiles with K a multiple of 32."""
     try:
         assert lib.gemm_debug_force_tile(0, 7) == lib.STATUS_SUCCESS
         assert lib.gemm_debug_force_splits(0, 1) == lib.STATUS_SUCCESS
@@ -192,7 +194,7 @@ def test_sgemm_direct_tile_resolution(so):
         assert pick(0, 4096, 4096, 4008) == (4, 1)      # K not a multiple of 32
         assert pick(0, 4000, 4096, 4096) == (4, 1)      # ragged M
         assert lib.gemm_debug_force_splits(0, 4) == lib.STATUS_SUCCESS
-        assert pick(0, 256, 256, 4096) == (4, 4)        # split: the register-staged kernel
+        assert pick(0, 256, 256, 4096) == (7, 4)        # the direct-to-LDS tiles split too
         assert lib.gemm_debug_force_tile(0, 8) == lib.STATUS_SUCCESS
         assert lib.gemm_debug_force_splits(0, 1) == lib.STATUS_SUCCESS
         assert pick(0, 128, 256, 64) == (8, 1)
@@ -263,7 +265,7 @@ def test_config_tuned_entries_are_used(so):
 
 
 def bk_of(tile):
-    return 32 if tile == 3 else 16
+    return 32 if tile == 3 or tile >= 7 else 16
 
 
 def test_split_legality(so):
@@ -284,13 +286,20 @@ def test_split_legality(so):
                 assert t == tile or (tile, t) in ((7, 4), (8, 4), (9, 4))
                 if t != tile:
                     assert s > 1 or M % (128 if tile == 8 else 256) or N % 256 or K % 32
-            bk = bk_of(t)
-            ktiles = -(-K // bk)
-            assert 1 <= s <= max(1, min(want, ktiles))
+            # the chunks are planned in the K granularity of the tile asked for (the
+            # tuned or forced one) before a direct-to-LDS tile resolves to tile 4
+            ok = False
+            for bk in {bk_of(t), 32}:
+                ktiles = -(-K // bk)
+                if not 1 <= s <= max(1, min(want, ktiles)):
+                    continue
+                if s > 1:
+                    chunk = -(-ktiles // min(want, ktiles, (64 << 20) // 4 // (M * N))) * bk
+                    if not (s == -(-K // chunk) and (s - 1) * chunk < K):
+                        continue
+                ok = True
+            assert ok, (M, N, K, want, tile, t, s)
             assert s * M * N <= (64 << 20) // 4 or s == 1
-            if s > 1:
-                chunk = -(-ktiles // min(want, ktiles, (64 << 20) // 4 // (M * N))) * bk
-                assert s == -(-K // chunk) and (s - 1) * chunk < K
     finally:
         lib.gemm_debug_force_tile(0, -1)
         lib.gemm_debug_force_splits(0, -1)
