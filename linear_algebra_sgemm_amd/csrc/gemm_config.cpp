@@ -56,11 +56,11 @@ int sgemm_rule_tile(int M, int N, int K, int cus) {
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
   const bool whole = M % 256 == 0 && N % 256 == 0 && K % 32 == 0;
   if (whole && t_large >= cus) return 9;
-  // Fewer whole 256x256 tiles than CUs: the same kernel with K split over up to
-  // eight chunks of at least 512, one workgroup per CU.
-  if (whole && 8 * t_large >= cus && K / ceil_div(cus, t_large) >= 512) return 9;
   if (t_tall >= 2L * cus) return 4;
   if (t_med >= 2L * cus) return 1;
+  // Fewer whole 256x256 tiles than CUs and a long K: the same kernel with K split
+  // over up to sixteen chunks of at least 512, one workgroup per CU.
+  if (whole && 16 * t_large >= cus && K / ceil_div(cus, t_large) >= 512) return 9;
   return 2;
 }
 

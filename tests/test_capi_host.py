@@ -157,6 +157,8 @@ def test_config_rule(so):
         (0, 2048, 2048, 8192, 256, (9, 4)),
         (0, 1024, 2048, 4096, 256, (9, 8)),   # 32 whole tiles, 8 chunks of 512
         (0, 1024, 1024, 4096, 256, (2, 1)),   # 16 whole tiles would need chunks under 512
+        (0, 1024, 1024, 8192, 256, (9, 16)),  # 16 whole tiles, 16 chunks of 512
+        (0, 2048, 4096, 1024, 256, (1, 1)),   # 512 tiles of 128x128 before a split
         (0, 4096, 4096, 4096, 64, (9, 1)),
         (0, 128, 128, 16384, 256, (2, 32)),   # 4 tiles; 256 chunks by CUs, capped at 32
         (1, 4096, 14336, 4096, 256, (7, 1)),  # whole 256-tiles, long K: eight waves + tail split
