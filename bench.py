@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the MI355X GEMM library on one GPU.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload sgemm_4096]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 100] [--workload sgemm_4096]
 
 One step is one library call on the named workload (default: FP32
 C = alpha*A*B + beta*C at M = N = K = 4096, alpha = 1, beta = 0.5, inputs
@@ -43,7 +43,9 @@ def parse_args():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=10)
+    # The card raises its clocks over the first tens of milliseconds of load: 100
+    # untimed calls (about 0.1 s at 4096^3) reach the steady state.
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="sgemm_4096")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample")
