@@ -164,9 +164,12 @@ int sgemm(int M, int N, int K, float alpha, const float* A, int lda, const float
     e = lasg::launch_sgemm_scale(M, N, beta, C, ldc, stream);
   } else {
     lasg::SgemmCall c{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+    const bool operands_ok = lda % 4 == 0 && ldb % 4 == 0 &&
+                             (reinterpret_cast<uintptr_t>(A) & 15u) == 0 &&
+                             (reinterpret_cast<uintptr_t>(B) & 15u) == 0;
     const lasg::SgemmPlan plan =
         lasg::plan_sgemm(M, N, K, g_cus.load(), g_force_sgemm_tile.load(),
-                         g_force_sgemm_splits.load(), g_ws.floats);
+                         g_force_sgemm_splits.load(), g_ws.floats, operands_ok);
     if (plan.splits > 1) {
       return with_workspace(stream, [&](float* ws) { return lasg::launch_sgemm(c, plan, ws, stream); });
     } else {
@@ -257,9 +260,10 @@ int gemm_debug_pick_config(int op, int M, int N, int K, int cus, int* tile, int*
   if (M < 0 || N < 0 || K < 0 || cus <= 0 || tile == nullptr || splits == nullptr)
     return GEMM_STATUS_INVALID_VALUE;
   if (op == 0) {
+    // Packed operands (lda = K, ldb = N) on 16-byte-aligned bases.
     const lasg::SgemmPlan p =
         lasg::plan_sgemm(M, N, K, cus, g_force_sgemm_tile.load(), g_force_sgemm_splits.load(),
-                         lasg::kWorkspaceBytes / sizeof(float));
+                         lasg::kWorkspaceBytes / sizeof(float), K % 4 == 0 && N % 4 == 0);
     *tile = p.tile;
     *splits = p.splits;
     return GEMM_STATUS_SUCCESS;

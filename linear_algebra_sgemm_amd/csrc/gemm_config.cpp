@@ -43,36 +43,76 @@ int size_class(int x) {
 
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
-// Built-in tile rule, measured on MI355X: the 256x256 direct-to-LDS tile with
-// eight waves once whole tiles give every CU one (4096^3: 146 TFLOP/s, 8192^3:
-// 149; four waves: 143 and 146); 128x256
-// register-staged tiles at two workgroups per CU once they give every CU two
-// (4096^3: 134 vs 130 for 256x256); below that, 128x128 if it still gives two
-// tiles per CU, else 64x64 tiles, which spread small outputs over more CUs
-// (2048^3: 106 vs 104; 1000x3000x777: 51 vs 42).
-int sgemm_rule_tile(int M, int N, int K, int cus) {
+// K chunks of the one-per-CU direct-to-LDS tiles when their tiles do not
+// cover the CUs: as many as keep every chunk in one round (at most 16), with
+// chunks of at least 384 (shorter ones lose to the fixed cost of a workgroup,
+// its prologue and epilogue, and to the extra traffic of the reduction).
+long direct_splits(long tiles, int K, int cus) {
+  if (tiles >= cus) return 1;
+  long s = cus / tiles;
+  if (s > 16) s = 16;
+  while (s > 1 && K / s < 384) --s;
+  return s;
+}
+
+// Share of the workgroup slots of the last round that the tiles use, in
+// percent, for tiles that fill one CU each (`per_cu` 1) or two per CU (2; a
+// last round of at most one workgroup per CU runs each at the full CU rate and
+// counts as half a round).
+long round_use(long tiles, int cus, int per_cu) {
+  const long slots = (long)per_cu * cus;
+  const long full = tiles / slots, rem = tiles % slots;
+  const long halves = 2 * full + (rem == 0 ? 0 : (per_cu == 2 && rem <= cus) ? 1 : 2);
+  return 200 * tiles / (halves * slots);
+}
+
+// Built-in tile rule, measured on MI355X (the size sweep over powers of two and
+// a sweep of ragged shapes):
+//  * The direct-to-LDS kernels wherever their copies are legal (rows of A and B
+//    16-byte aligned, N a multiple of 4) and their 256x256 tiles cover the CUs:
+//    eight waves of 256x256 (4096^3: 146 TFLOP/s, 8192^3: 149; ragged 4000^3:
+//    138 vs 111 for the best register-staged tile), or 128x256 at two per CU
+//    when that wastes less of the last round (6000^3: 116 vs 104; 7000 x 3000 x
+//    2000: 109 vs 89) — weighed by their full-round rates, 89 vs 93 % of peak.
+//    On a ragged shape K must reach 384 (5000 x 5000 x 333: 64 vs 74 for 64x64).
+//  * Else the register-staged 128x256 tile at two per CU, then 128x128, where
+//    their tiles give every CU two (4096^3: 134 vs 130 for 256x256) — on shapes
+//    the direct-to-LDS kernel takes, only where they are whole (their
+//    bounds-checked form is slow: 3000^3 at 128x128: 77).
+//  * Else the 256x256 direct-to-LDS tile with K split so that one round uses at
+//    least 70 % of the CUs (2048^3: 114, 1024 x 1024 x 8192: 116 vs 81; ragged
+//    2500^3: 99 vs 90, 4000 x 2000 x 3000: 128 vs 105), or unsplit when its
+//    tiles alone fill 70 % (3500^3: 106 vs 104).
+//  * Else 64x64 tiles, which spread small outputs over more CUs (3000^3: 101 vs
+//    78 for 256x256 at 144 tiles; 1000x3000x777: 63 vs 50 for 128x128).
+int sgemm_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_tall = ceil_div(M, 128) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
+  const bool direct = operands_ok && N % 4 == 0;
   const bool whole = M % 256 == 0 && N % 256 == 0 && K % 32 == 0;
-  if (whole && t_large >= cus) return 9;
-  if (t_tall >= 2L * cus) return 4;
-  if (t_med >= 2L * cus) return 1;
-  // Fewer whole 256x256 tiles than CUs and a long K: the same kernel with K split
-  // over up to sixteen chunks of at least 512, one workgroup per CU.
-  if (whole && 16 * t_large >= cus && K / ceil_div(cus, t_large) >= 512) return 9;
+  if (direct && t_large >= cus && (whole || K >= 384))
+    return 89 * round_use(t_tall, cus, 2) > 93 * round_use(t_large, cus, 1) ? 8 : 9;
+  // (on shapes the direct-to-LDS kernel can take, only where these tiles are whole)
+  if (t_tall >= 2L * cus && (!direct || (M % 128 == 0 && N % 256 == 0 && K % 16 == 0))) return 4;
+  if (t_med >= 2L * cus && (!direct || (M % 128 == 0 && N % 128 == 0 && K % 16 == 0))) return 1;
+  if (direct && K >= 384 && t_large < cus) {
+    const long s = direct_splits(t_large, K, cus);
+    if (10 * t_large * s >= 7L * cus) return 9;
+  }
   return 2;
 }
 
-// Built-in split rule (from the size sweep): when the output has fewer tiles
+// Built-in split rule: the direct-to-LDS tiles as in direct_splits; for the
+// register-staged tiles (from the size sweep), when the output has fewer tiles
 // than there are CUs and K is at least 512, split K until there are about four
-// workgroups per CU (small tiles share a CU; the 256x256 direct-to-LDS tiles
-// fill one CU each, so one per CU), keeping chunks of at least 128.
+// workgroups per CU (small tiles share a CU), keeping chunks of at least 128.
 int sgemm_rule_splits(int M, int N, int K, int tile, int cus) {
   const long tiles = ceil_div(M, sgemm_tile_bm(tile)) * ceil_div(N, sgemm_tile_bn(tile));
+  if (tile == 7 || tile == 9) return (int)direct_splits(tiles, K, cus);
+  if (tile == 8) return (int)direct_splits((tiles + 1) / 2, K, cus);
   if (tiles >= cus || K < 512) return 1;
-  const long per_cu = (tile == 7 || tile == 9) ? 1 : 4;
-  const long by_cus = ceil_div(per_cu * cus, tiles);
+  const long by_cus = ceil_div(4L * cus, tiles);
   const long by_k = ceil_div(K, sgemm_tile_bk(tile)) * sgemm_tile_bk(tile) / 128;
   long s = by_cus < by_k ? by_cus : by_k;
   if (s > kMaxSplits) s = kMaxSplits;
@@ -97,12 +137,18 @@ bool tuned_config(int op, int M, int N, int K, int* tile, int* splits) {
 }
 
 SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_splits,
-                     size_t ws_floats) {
+                     size_t ws_floats, bool operands_ok) {
   int tuned_tile = -1, tuned_splits = -1;
-  const bool tuned = tuned_config(0, M, N, K, &tuned_tile, &tuned_splits) &&
-                     tuned_tile >= 0 && tuned_tile < kSgemmTileCount && tuned_splits >= 1;
+  bool tuned = tuned_config(0, M, N, K, &tuned_tile, &tuned_splits) && tuned_tile >= 0 &&
+               tuned_tile < kSgemmTileCount && tuned_splits >= 1;
+  // A table entry for a direct-to-LDS tile was measured with packed aligned
+  // operands; when the copies are not legal here, the rule chooses instead.
+  if (tuned && sgemm_resolve_tile(tuned_tile, M, N, K, tuned_splits, operands_ok) != tuned_tile)
+    tuned = false;
   SgemmPlan p;
-  p.tile = force_tile >= 0 ? force_tile : tuned ? tuned_tile : sgemm_rule_tile(M, N, K, cus);
+  p.tile = force_tile >= 0 ? force_tile
+           : tuned        ? tuned_tile
+                          : sgemm_rule_tile(M, N, K, cus, operands_ok);
   long s = force_splits > 0 ? force_splits
            : (tuned && force_tile < 0) ? tuned_splits
                                        : sgemm_rule_splits(M, N, K, p.tile, cus);
@@ -124,9 +170,9 @@ SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_spl
   }
   p.splits = (int)s;
   p.k_chunk = (int)chunk;
-  // Report what runs for 16-byte-aligned operands (the launch resolves again
-  // with the actual operands).
-  p.tile = sgemm_resolve_tile(p.tile, M, N, K, p.splits, true);
+  // What runs (the launch resolves again with the actual operands, to the same
+  // answer when `operands_ok` describes them).
+  p.tile = sgemm_resolve_tile(p.tile, M, N, K, p.splits, operands_ok);
   return p;
 }
 

@@ -72,16 +72,16 @@ struct SgemmPlan {
   int k_chunk;
 };
 
-// The plan for an M x N x K product on `cus` compute units.  force_tile /
-// force_splits < 0 let the shape decide (offline-tuned table, else the
-// built-in rule); the split count is then clamped to the K tiles there are and
-// to `ws_floats` of workspace.
+// The plan for an M x N x K product on `cus` compute units (`operands_ok`: lda
+// and ldb multiples of 4, A and B 16-byte aligned).  force_tile / force_splits
+// < 0 let the shape decide (offline-tuned table, else the built-in rule); the
+// split count is then clamped to the K tiles there are and to `ws_floats` of
+// workspace.
 SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_splits,
-                     size_t ws_floats);
+                     size_t ws_floats, bool operands_ok);
 // The FP32 configuration that actually runs for `tile` with `splits` K chunks:
-// the direct-to-LDS ones (7, 8, 9) become 4 when the shape or the operands
-// (`operands_ok`: lda, ldb multiples of 4, A and B 16-byte aligned) do not
-// suit them.
+// the direct-to-LDS ones (7, 8, 9) become 4 when N is not a multiple of 4 or
+// the operands (`operands_ok` as above) do not suit them.
 int sgemm_resolve_tile(int tile, int M, int N, int K, int splits, bool operands_ok);
 
 // Offline-tuned choice for (op, M, N, K) if the table has one for the shape's

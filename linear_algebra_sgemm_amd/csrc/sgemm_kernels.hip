@@ -390,20 +390,26 @@ struct SDmaTile {
 
 // Per-lane byte offsets of a wave's copies relative to the K tile's A or B base
 // (a_base(kt) = A + m0 lda + 16 kt, b_base(kt) = B + 16 kt ldb + n0, floats),
-// and the LDS slot of copy v inside one stage.
+// and the LDS slot of copy v inside one stage.  On a tile that crosses the
+// bottom or right edge, rows of A past M - 1 copy row M - 1 and 4-column chunks
+// of B past N - 4 copy the chunk at N - 4 (N is a multiple of 4), so every copy
+// reads inside the matrices; the values land in rows and columns of the tile
+// that the epilogue does not store.
 template <class T>
 struct SDmaPlan {
   uint32_t off[T::LOADS_PER_TILE];
-  __device__ __forceinline__ SDmaPlan(const SgemmArgs& p, int wave, int lane) {
+  __device__ __forceinline__ SDmaPlan(const SgemmArgs& p, int wave, int lane, int m0, int n0) {
 #pragma unroll
     for (int v = 0; v < T::LOADS_PER_TILE; ++v) {
       if (v < T::A_PER_WAVE) {
         const int r = (wave * T::A_PER_WAVE + v) * 16 + lane / 4;
         const int chunk = (lane % 4) ^ row64_swizzle(r);
-        off[v] = (uint32_t)(((size_t)r * p.lda + 4 * chunk) * 4);
+        const int rc = m0 + r < p.M ? r : p.M - 1 - m0;
+        off[v] = (uint32_t)(((size_t)rc * p.lda + 4 * chunk) * 4);
       } else {
         const int kr = wave * T::B_PER_WAVE + (v - T::A_PER_WAVE);
-        off[v] = (uint32_t)(((size_t)kr * p.ldb + 4 * lane) * 4);
+        const int cc = n0 + 4 * lane < p.N ? 4 * lane : p.N - 4 - n0;
+        off[v] = (uint32_t)(((size_t)kr * p.ldb + cc) * 4);
       }
     }
   }
@@ -530,7 +536,52 @@ __device__ __forceinline__ void sdma_tile(const SgemmArgs& p, f32x16 (&acc)[T::F
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <class T, bool SPLIT>
+// The last K - K % 32 < 32 values of k on a ragged K: both stages 0 and 1 are
+// filled with bounds-checked loads and plain LDS stores, in the layout the
+// copies produce (zeros for k >= K, clamped rows and columns as in SDmaPlan),
+// and the MFMAs of the two 16-wide K tiles follow.  Called by every wave after
+// the main loop.
+template <class T>
+__device__ __forceinline__ void sdma_k_tail(const SgemmArgs& p, f32x16 (&acc)[T::FM][T::FN],
+                                            uint8_t* lds, int k0, int m0, int n0, int wm, int wn,
+                                            int lane) {
+  lds_barrier();   // every wave is done reading the stages
+  const int tid = threadIdx.x;
+  // A: BM rows x 8 chunks of 4 k (two tiles of four chunks).
+  for (int c = tid; c < T::BM * 8; c += T::THREADS) {
+    const int r = c / 8, t = (c % 8) / 4, chunk = c % 4;
+    const int row = m0 + r < p.M ? m0 + r : p.M - 1;
+    const int k = k0 + 16 * t + 4 * chunk;
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = k + e < p.K ? p.A[(size_t)row * p.lda + k + e] : 0.0f;
+    *reinterpret_cast<f32x4*>(lds + t * T::STAGE_BYTES + r * 64 +
+                              16 * (chunk ^ row64_swizzle(r))) = v;
+  }
+  // B: 32 rows of k x BN / 4 chunks of 4 columns.
+  for (int c = tid; c < 32 * (T::BN / 4); c += T::THREADS) {
+    const int kr = c / (T::BN / 4), cc = 4 * (c % (T::BN / 4));
+    const int t = kr / 16;
+    const int k = k0 + kr;
+    const int col = n0 + cc < p.N ? n0 + cc : p.N - 4;
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (k < p.K) v = *reinterpret_cast<const f32x4*>(p.B + (size_t)k * p.ldb + col);
+    *reinterpret_cast<f32x4*>(lds + t * T::STAGE_BYTES + T::A_BYTES + (kr % 16) * T::B_ROW +
+                              4 * cc) = v;
+  }
+  lds_barrier();
+  SFrags<T> f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      sload_frags<T>(f, lds + t * T::STAGE_BYTES, g, wm, wn, lane);
+#pragma unroll
+      for (int x = 0; x < 4 * T::FM * T::FN; ++x) smfma<T>(acc, f, x);
+    }
+}
+
+template <class T, bool SPLIT, bool EDGE>
 __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(T::WAVES_PER_SIMD)))
 sgemm_dma_kernel(SgemmArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[T::STAGES * T::STAGE_BYTES];
@@ -568,12 +619,13 @@ sgemm_dma_kernel(SgemmArgs p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // Tile kt lives in stage kt % STAGES; its copies are issued during tile
-  // kt - STAGES + 1 (the prologue issues the first STAGES - 1).  K is a multiple
-  // of 2 BK, so the loop body covers two tiles and the fragment sets alternate.
-  const int ktiles = p.K / T::BK;
+  // kt - STAGES + 1 (the prologue issues the first STAGES - 1).  The loop covers
+  // the largest multiple of 2 BK in K, two tiles per trip, so the fragment sets
+  // alternate; on a ragged K (EDGE only) sdma_k_tail adds the rest.
+  const int ktiles = EDGE ? (p.K / (2 * T::BK)) * 2 : p.K / T::BK;
   const float* a_tile = p.A + (size_t)m0 * p.lda;
   const float* b_tile = p.B + n0;
-  const SDmaPlan<T> plan(p, wave, lane);
+  const SDmaPlan<T> plan(p, wave, lane, m0, n0);
   SFrags<T> f0, f1, f2, f3;
   if (ktiles > 0) {
 #pragma unroll
@@ -602,6 +654,9 @@ sgemm_dma_kernel(SgemmArgs p) {
     sdma_tile<T, false>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, plan, a_tile,
                         b_tile, wave, wm, wn, lane);
   }
+  if constexpr (EDGE) {
+    if (ktiles * T::BK < p.K) sdma_k_tail<T>(p, acc, lds, ktiles * T::BK, m0, n0, wm, wn, lane);
+  }
   if constexpr (SPLIT) {
     // Raw partial sums into this K chunk's slice of the workspace.
     float* W = p.ws + (size_t)blockIdx.y * p.M * p.N;
@@ -613,12 +668,15 @@ sgemm_dma_kernel(SgemmArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wm * T::WTM + i * 32 + mfma32_row(r, lane);
-          W[(size_t)row * p.N + col] = acc[i][j][r];
+          if (!EDGE || (row < p.M && col < p.N)) W[(size_t)row * p.N + col] = acc[i][j][r];
         }
       }
     return;
   }
-  sgemm_store<T, false>(p, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
+  if (EDGE && (m0 + T::BM > p.M || n0 + T::BN > p.N))
+    sgemm_store<T, true>(p, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
+  else
+    sgemm_store<T, false>(p, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
 }
 
 // Second half of split-K: C = alpha * (sum of the `splits` partials, added in
@@ -714,12 +772,35 @@ static hipError_t launch_tile(const SgemmCall& c, const SgemmPlan& plan, int gro
   return hipGetLastError();
 }
 
+// The direct-to-LDS kernels copy 16-byte chunks: rows of A and B must start on
+// 16-byte boundaries and N must be a multiple of 4 (a chunk of B never crosses
+// the matrix's right edge); the per-lane copy offsets are 32-bit.  Whole tiles
+// with K a multiple of 32 run the unchecked instantiation.
 template <class T>
 static bool sdma_fits(const SgemmCall& c) {
-  return c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % (2 * T::BK) == 0 && c.lda % 4 == 0 &&
-         c.ldb % 4 == 0 && aligned16(c.A) && aligned16(c.B) &&
+  return c.lda % 4 == 0 && c.ldb % 4 == 0 && c.N % 4 == 0 && aligned16(c.A) && aligned16(c.B) &&
          (int64_t)c.lda * T::BM * 4 < (int64_t(1) << 31) &&
          (int64_t)c.ldb * T::BK * 4 < (int64_t(1) << 31);
+}
+
+template <class T>
+static bool sdma_whole(const SgemmCall& c) {
+  return c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % (2 * T::BK) == 0;
+}
+
+template <class T, bool EDGE>
+static hipError_t launch_sdma_kernel(const SgemmCall& c, const SgemmPlan& plan, const SgemmArgs& p,
+                                     float* ws, hipStream_t s) {
+  if (plan.splits > 1) {
+    hipLaunchKernelGGL((sgemm_dma_kernel<T, true, EDGE>), dim3(p.tiles_m * p.tiles_n, plan.splits),
+                       dim3(T::THREADS), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_reduce(c, plan.splits, ws, s);
+  }
+  hipLaunchKernelGGL((sgemm_dma_kernel<T, false, EDGE>), dim3(p.tiles_m * p.tiles_n),
+                     dim3(T::THREADS), 0, s, p);
+  return hipGetLastError();
 }
 
 template <class T>
@@ -732,33 +813,23 @@ static hipError_t launch_sdma(const SgemmCall& c, const SgemmPlan& plan, int gro
   p.M = c.M; p.N = c.N; p.K = c.K;
   p.alpha = c.alpha; p.beta = c.beta;
   p.A = c.A; p.lda = c.lda; p.B = c.B; p.ldb = c.ldb; p.C = c.C; p.ldc = c.ldc;
-  p.tiles_m = c.M / T::BM;
-  p.tiles_n = c.N / T::BN;
+  p.tiles_m = (c.M + T::BM - 1) / T::BM;
+  p.tiles_n = (c.N + T::BN - 1) / T::BN;
   p.group_m = group_m;
   p.k_chunk = plan.splits > 1 ? plan.k_chunk : c.K;
   p.ws = ws;
   p.a_vec = p.b_vec = 1;
-  if (plan.splits > 1) {
-    hipLaunchKernelGGL((sgemm_dma_kernel<T, true>), dim3(p.tiles_m * p.tiles_n, plan.splits),
-                       dim3(T::THREADS), 0, s, p);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_reduce(c, plan.splits, ws, s);
-  }
-  hipLaunchKernelGGL((sgemm_dma_kernel<T, false>), dim3(p.tiles_m * p.tiles_n), dim3(T::THREADS), 0,
-                     s, p);
-  return hipGetLastError();
+  if (sdma_whole<T>(c)) return launch_sdma_kernel<T, false>(c, plan, p, ws, s);
+  return launch_sdma_kernel<T, true>(c, plan, p, ws, s);
 }
 
 int sgemm_resolve_tile(int tile, int M, int N, int K, int splits, bool operands_ok) {
-  // The direct-to-LDS kernels need whole tiles, K a multiple of 32 and aligned
-  // operands (K chunks of a split are multiples of 32 too); otherwise the
-  // register-staged 128 x 256 kernel (the best of those for large outputs) runs.
-  (void)splits;
-  const bool whole = operands_ok && N % 256 == 0 && K % 32 == 0;
-  if (tile == 7 && !(whole && M % 256 == 0)) return 4;
-  if (tile == 8 && !(whole && M % 128 == 0)) return 4;
-  if (tile == 9 && !(whole && M % 256 == 0)) return 4;
+  // The direct-to-LDS kernels need rows of A and B on 16-byte boundaries and N a
+  // multiple of 4 (any M, N and K otherwise: ragged edges and a ragged K run a
+  // bounds-checked instantiation); otherwise the register-staged 128 x 256
+  // kernel (the best of those for large outputs) runs.
+  (void)M; (void)K; (void)splits;
+  if (tile >= 7 && !(operands_ok && N % 4 == 0)) return 4;
   return tile;
 }
 

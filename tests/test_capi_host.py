@@ -148,7 +148,10 @@ def test_config_rule(so):
     cases = [
         (0, 4096, 4096, 4096, 256, (9, 1)),   # whole 256x256 tiles: direct-to-LDS kernel
         (0, 8192, 8192, 8192, 256, (9, 1)),
-        (0, 4096, 4096, 4008, 256, (4, 1)),   # K not a multiple of 32
+        (0, 4096, 4096, 4008, 256, (9, 1)),   # ragged K: the bounds-checked direct-to-LDS kernel
+        (0, 4000, 4000, 4000, 256, (9, 1)),   # ragged M, N, K likewise
+        (0, 4096, 4096, 4002, 256, (4, 1)),   # lda = 4002: rows of A not 16-byte aligned
+        (0, 4096, 4090, 4096, 256, (4, 1)),   # N not a multiple of 4
         (0, 256, 256, 256, 256, (2, 1)),      # K < 512: no split
         (0, 256, 256, 1024, 256, (2, 8)),     # 16 tiles; chunks of 128
         (0, 512, 512, 512, 256, (2, 4)),      # 64 tiles; chunks of 128
@@ -188,19 +191,23 @@ def test_config_rule(so):
 
 
 def test_sgemm_direct_tile_resolution(so):
-    """The FP32 direct-to-LDS tiles run only on whole tiles with K a multiple of 32."""
+    """The FP32 direct-to-LDS tiles take any M, N, K with N a multiple of 4 (ragged
+    edges and K run their bounds-checked instantiation); otherwise tile 4 runs."""
     try:
         assert lib.gemm_debug_force_tile(0, 7) == lib.STATUS_SUCCESS
         assert lib.gemm_debug_force_splits(0, 1) == lib.STATUS_SUCCESS
         assert pick(0, 4096, 4096, 4096) == (7, 1)
-        assert pick(0, 4096, 4096, 4008) == (4, 1)      # K not a multiple of 32
-        assert pick(0, 4000, 4096, 4096) == (4, 1)      # ragged M
+        assert pick(0, 4096, 4096, 4008) == (7, 1)      # K not a multiple of 32
+        assert pick(0, 4000, 4096, 4096) == (7, 1)      # ragged M
+        assert pick(0, 4096, 4090, 4096) == (4, 1)      # N not a multiple of 4
         assert lib.gemm_debug_force_splits(0, 4) == lib.STATUS_SUCCESS
         assert pick(0, 256, 256, 4096) == (7, 4)        # the direct-to-LDS tiles split too
+        assert pick(0, 300, 260, 1000) == (7, 4)        # chunks of 256, 256, 256, 232
         assert lib.gemm_debug_force_tile(0, 8) == lib.STATUS_SUCCESS
         assert lib.gemm_debug_force_splits(0, 1) == lib.STATUS_SUCCESS
         assert pick(0, 128, 256, 64) == (8, 1)
-        assert pick(0, 128, 200, 64) == (4, 1)
+        assert pick(0, 128, 200, 64) == (8, 1)
+        assert pick(0, 128, 201, 64) == (4, 1)
     finally:
         lib.gemm_debug_force_tile(0, -1)
         lib.gemm_debug_force_splits(0, -1)
