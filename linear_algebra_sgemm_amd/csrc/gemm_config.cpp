@@ -141,9 +141,11 @@ SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_spl
   int tuned_tile = -1, tuned_splits = -1;
   bool tuned = tuned_config(0, M, N, K, &tuned_tile, &tuned_splits) && tuned_tile >= 0 &&
                tuned_tile < kSgemmTileCount && tuned_splits >= 1;
-  // A table entry for a direct-to-LDS tile was measured with packed aligned
-  // operands; when the copies are not legal here, the rule chooses instead.
-  if (tuned && sgemm_resolve_tile(tuned_tile, M, N, K, tuned_splits, operands_ok) != tuned_tile)
+  // Table entries were measured on whole tiles with packed aligned operands;
+  // where the entry's tile would run bounds-checked here, the rule chooses
+  // instead (it knows the ragged shapes).
+  if (tuned && !(operands_ok && N % 4 == 0 && M % sgemm_tile_bm(tuned_tile) == 0 &&
+                 N % sgemm_tile_bn(tuned_tile) == 0 && K % sgemm_tile_bk(tuned_tile) == 0))
     tuned = false;
   SgemmPlan p;
   p.tile = force_tile >= 0 ? force_tile
@@ -180,20 +182,30 @@ namespace {
 
 int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   // Built-in rule (from the size sweep): 256x256 tiles once they give every CU
-  // one and K is at least 512 -- with direct-to-LDS copies when the shape and
-  // operands allow it: eight waves with the head/tail column split (tile 7, which
-  // runs as tile 6 where no split exists) for K >= 2048, four waves (tile 3) for
-  // shorter K, where the eight-wave tile lost up to 14 % -- else 128x128 tiles
-  // once they give every CU two, else 64x64 tiles, which spread small outputs
-  // over the most CUs.
+  // one and K is at least 512 -- with direct-to-LDS copies when the operands
+  // allow them (rows of A and B 16-byte aligned, N a multiple of 8): eight waves
+  // with the head/tail column split (tile 7, which runs as tile 6 where no split
+  // exists) for K >= 2048, four waves (tile 3) for shorter K, where the
+  // eight-wave tile lost up to 14 % -- else 128x128 tiles once they give every
+  // CU two, else 64x64 tiles, which spread small outputs over the most CUs.
+  // Where the copies are legal but the register-staged tile would have to run
+  // bounds-checked (ragged M, N or K), the direct-to-LDS tiles win by far at
+  // every size measured (3000^3: 652 TFLOP/s for the eight-wave tile vs 92 for
+  // the best register-staged one; 2000 x 7000 x 2000: 865 vs 136): the
+  // eight-wave 256x256 tile, or 128x256 where fewer than 64 256x256 tiles exist
+  // and K is below 2048 (1000^3: 68 vs 65; 1000 x 1000 x 4000: 75 vs 97).
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
+  const bool direct = operands_ok && N % 8 == 0;
   if (t_large >= cus && K >= 512) {
-    if (!(M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && operands_ok)) return 0;
+    if (!direct) return 0;
     return K >= 2048 ? 7 : 3;
   }
-  if (t_med >= 2L * cus) return 1;
-  return 2;
+  const int reg = t_med >= 2L * cus ? 1 : 2;
+  const int bm = half_tile_bm(reg);
+  const bool reg_whole = M % bm == 0 && N % bm == 0 && K % kHalfBK == 0;
+  if (direct && !reg_whole) return (t_large >= 64 || K >= 2048) ? 6 : 4;
+  return reg;
 }
 
 // Built-in split rule of the half products, as for FP32: split K (register-
@@ -215,8 +227,16 @@ int half_rule_splits(int M, int N, int K, int tile, int cus) {
 HalfPlan plan_half(int M, int N, int K, int cus, int force_tile, int force_splits,
                    size_t ws_floats, bool operands_ok) {
   int tuned_tile = -1, tuned_splits = -1;
-  const bool tuned = tuned_config(1, M, N, K, &tuned_tile, &tuned_splits) && tuned_tile >= 0 &&
-                     tuned_tile < kHgemmTileCount && tuned_splits >= 1;
+  bool tuned = tuned_config(1, M, N, K, &tuned_tile, &tuned_splits) && tuned_tile >= 0 &&
+               tuned_tile < kHgemmTileCount && tuned_splits >= 1;
+  // Table entries were measured on whole tiles with aligned operands; where the
+  // entry's tile would run bounds-checked here, the rule chooses instead.
+  if (tuned) {
+    const int bm = tuned_tile <= 2 ? half_tile_bm(tuned_tile) : tuned_tile == 4 ? 128 : 256;
+    const int bn = tuned_tile <= 2 ? bm : 256;
+    if (!(operands_ok && N % 8 == 0 && M % bm == 0 && N % bn == 0 && K % kHalfBK == 0))
+      tuned = false;
+  }
   HalfPlan p;
   p.tile = force_tile >= 0 ? force_tile
            : tuned         ? tuned_tile

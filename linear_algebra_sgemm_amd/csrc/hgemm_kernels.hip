@@ -374,11 +374,17 @@ __device__ __forceinline__ int a_swizzle(int r) {
 
 // Global address of the 16-byte chunk that lane `lane` of direct load `v` (0 ..
 // LOADS_PER_TILE - 1) of wave `wave` copies, and the offset of its LDS slot
-// inside one stage.
+// inside one stage.  Rows of A past M - 1 read row M - 1 and 8-column chunks of
+// B past N - 8 read the chunk at N - 8 (N is a multiple of 8), so on a tile that
+// crosses the bottom or right edge every copy stays inside the matrices; those
+// rows and columns of the tile are never stored.  `k_first` / `k_step` give the
+// k of element e of the chunk: k_first + k_step e (8 consecutive k of one A row,
+// or one k for the 8 columns of a B row).
 template <class T>
 __device__ __forceinline__ const uint16_t* hdma_source(const HgemmArgs& p, int m0, int n0, int k0,
                                                        int v, int wave, int lane,
-                                                       uint32_t& stage_offset) {
+                                                       uint32_t& stage_offset, int& k_first,
+                                                       int& k_step) {
   if (v < T::A_PER_WAVE) {
     // A stage: row-major rows of BK halves with the 16-byte chunks of row r
     // permuted by a_swizzle(r); one load = 1 KiB = whole rows, so every cache
@@ -388,7 +394,10 @@ __device__ __forceinline__ const uint16_t* hdma_source(const HgemmArgs& p, int m
     const int slot = lane % T::A_CHUNKS_PER_ROW;
     stage_offset = ia * 1024;
     const int chunk = slot ^ a_swizzle<T>(r);
-    return p.A + (size_t)(m0 + r) * p.lda + k0 + 8 * chunk;
+    const int row = m0 + r < p.M ? m0 + r : p.M - 1;
+    k_first = k0 + 8 * chunk;
+    k_step = 1;
+    return p.A + (size_t)row * p.lda + k0 + 8 * chunk;
   }
   const int ibb = wave * T::B_PER_WAVE + (v - T::A_PER_WAVE);   // = (s * 2 + t) * (BN / 64) + jp
   const int jp = ibb % (T::BN / 64);
@@ -399,7 +408,10 @@ __device__ __forceinline__ const uint16_t* hdma_source(const HgemmArgs& p, int m
   const int c2 = pidx & 1, q = (pidx >> 1) & 3, cg = (pidx >> 3) & 1, h = pidx >> 4;
   stage_offset = T::A_BYTES + ibb * 1024;
   const int row = k0 + 16 * s + 8 * h + 4 * t + q;
-  const int col = n0 + 32 * jb + 16 * cg + 8 * c2;
+  const int col0 = n0 + 32 * jb + 16 * cg + 8 * c2;
+  const int col = col0 <= p.N - 8 ? col0 : p.N - 8;
+  k_first = row;
+  k_step = 0;
   return p.B + (size_t)row * p.ldb + col;
 }
 
@@ -411,12 +423,14 @@ __device__ __forceinline__ const uint16_t* hdma_source(const HgemmArgs& p, int m
 template <class T>
 struct HDmaOffsets {
   uint32_t off[T::LOADS_PER_TILE];
-  __device__ __forceinline__ HDmaOffsets(const HgemmArgs& p, int wave, int lane) {
+  __device__ __forceinline__ HDmaOffsets(const HgemmArgs& p, int wave, int lane, int m0, int n0) {
 #pragma unroll
     for (int v = 0; v < T::LOADS_PER_TILE; ++v) {
-      uint32_t unused;
-      const uint16_t* src = hdma_source<T>(p, 0, 0, 0, v, wave, lane, unused);
-      const uint16_t* base = v < T::A_PER_WAVE ? p.A : p.B;
+      uint32_t unused_slot;
+      int unused_k, unused_step;
+      const uint16_t* src = hdma_source<T>(p, m0, n0, 0, v, wave, lane, unused_slot, unused_k,
+                                           unused_step);
+      const uint16_t* base = v < T::A_PER_WAVE ? p.A + (size_t)m0 * p.lda : p.B + n0;
       off[v] = (uint32_t)((src - base) * sizeof(uint16_t));
     }
   }
@@ -585,7 +599,42 @@ __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::F
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// The last K % (2 BK) values of k on a ragged K: stages 0 and 1 are filled with
+// bounds-checked loads and plain LDS stores, chunk for chunk where the copies
+// would put them (zeros for k >= K), and the MFMAs of those two K tiles follow.
+// Called by every wave after the main loop.
 template <class T>
+__device__ __forceinline__ void hdma_k_tail(const HgemmArgs& p, f32x16 (&acc)[T::FN][T::FM],
+                                            uint8_t* lds, int k0, int m0, int n0, int wave,
+                                            int wm, int wn, int lane) {
+  lds_barrier();   // every wave is done reading the stages
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int v = 0; v < T::LOADS_PER_TILE; ++v) {
+      uint32_t slot;
+      int k_first, k_step;
+      const uint16_t* src =
+          hdma_source<T>(p, m0, n0, k0 + t * T::BK, v, wave, lane, slot, k_first, k_step);
+      uint16_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = k_first + k_step * e < p.K ? src[e] : (uint16_t)0;
+      *reinterpret_cast<u32x4*>(lds + t * T::STAGE_BYTES + slot + 16 * lane) =
+          __builtin_bit_cast(u32x4, h);
+    }
+  lds_barrier();
+  HFrags<T> f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int st = 0; st < T::KSTEPS; ++st) {
+      hload_frags<T>(f, lds + t * T::STAGE_BYTES, st, wm, wn, lane);
+#pragma unroll
+      for (int x = 0; x < T::FM * T::FN; ++x) hmfma<T>(acc, f, x);
+    }
+}
+
+template <class T, bool EDGE>
 __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(T::WAVES_PER_SIMD)))
 hgemm_dma_kernel(HgemmArgs p) {
   static_assert(T::KSTEPS % 2 == 0, "fragments ping-pong between two register sets");
@@ -620,11 +669,13 @@ hgemm_dma_kernel(HgemmArgs p) {
   // wave has also finished with stage (kt - 1) % STAGES (its fragments were
   // consumed in tile kt - 1), which the direct loads of tile kt + STAGES - 1
   // then refill.  K is a multiple of 2 BK, so the loop body covers two tiles.
-  const int ktiles = p.K / T::BK;
+  // On a ragged K (EDGE only) the loop covers the largest multiple of 2 BK in K
+  // and hdma_k_tail adds the rest.
+  const int ktiles = EDGE ? (p.K / (2 * T::BK)) * 2 : p.K / T::BK;
   // Wave-uniform tile bases (k = 0) and the per-lane offsets of the direct loads.
   const uint16_t* a_tile = p.A + (size_t)m0 * p.lda;
   const uint16_t* b_tile = p.B + n0;
-  const HDmaOffsets<T> dma(p, wave, lane);
+  const HDmaOffsets<T> dma(p, wave, lane, m0, n0);
   HFrags<T> f0, f1, f2, f3;
   if (ktiles > 0) {
 #pragma unroll
@@ -652,6 +703,9 @@ hgemm_dma_kernel(HgemmArgs p) {
     hdma_tile<T, false>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, dma, a_tile,
                         b_tile, wave, wm, wn, lane);
   }
+  if constexpr (EDGE) {
+    if (ktiles * T::BK < p.K) hdma_k_tail<T>(p, acc, lds, ktiles * T::BK, m0, n0, wave, wm, wn, lane);
+  }
 
   // Epilogue.  Lane l holds, for n-block j, m-block i and q = 0..3, the four
   // columns n = 8 q + 4 (l / 32) + 0..3 of row m = l % 32.
@@ -678,7 +732,8 @@ hgemm_dma_kernel(HgemmArgs p) {
         float bias4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (p.bias != nullptr) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bias4[e] = p.bias[n0 + cl + e];
+          for (int e = 0; e < 4; ++e)
+            if (!EDGE || n0 + cl + e < p.N) bias4[e] = p.bias[n0 + cl + e];
         }
 #pragma unroll
         for (int i = 0; i < T::FM; ++i) {
@@ -702,6 +757,8 @@ hgemm_dma_kernel(HgemmArgs p) {
       const int chunk = lane % CPR;
       const u32x4 v = *reinterpret_cast<const u32x4*>(region + r * RB +
                                                       16 * (chunk ^ ((r / RPL) % CPR)));
+      // (N is a multiple of 8 on the ragged path: a chunk is wholly in or out)
+      if (EDGE && (m0 + wm * T::WTM + r >= p.M || n0 + wn * T::WTN + 8 * chunk >= p.N)) continue;
       *reinterpret_cast<u32x4*>(p.C + (size_t)(m0 + wm * T::WTM + r) * p.ldc + n0 +
                                 wn * T::WTN + 8 * chunk) = v;
     }
@@ -716,7 +773,8 @@ hgemm_dma_kernel(HgemmArgs p) {
       float bias4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (p.bias != nullptr) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bias4[e] = p.bias[col + e];
+        for (int e = 0; e < 4; ++e)
+          if (!EDGE || col + e < p.N) bias4[e] = p.bias[col + e];
       }
 #pragma unroll
       for (int i = 0; i < T::FM; ++i) {
@@ -729,11 +787,13 @@ hgemm_dma_kernel(HgemmArgs p) {
           h[e] = T::E::bits(x);
         }
         uint16_t* dst = p.C + (size_t)row * p.ldc + col;
-        if (vec_store) {
+        if (EDGE && (row >= p.M || col >= p.N)) continue;
+        if (vec_store && (!EDGE || col + 3 < p.N)) {
           *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, h);
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dst[e] = h[e];
+          for (int e = 0; e < 4; ++e)
+            if (!EDGE || col + e < p.N) dst[e] = h[e];
         }
       }
     }
@@ -816,13 +876,22 @@ static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s, i
   return hipGetLastError();
 }
 
+// The direct-to-LDS kernels copy 16-byte chunks: rows of A and B on 16-byte
+// boundaries, N a multiple of 8 (a chunk of B never crosses the right edge),
+// 32-bit per-lane copy offsets.  Whole tiles with K a multiple of 2 BK run the
+// unchecked instantiation.
 template <class T>
 static bool dma_fits(const HgemmCall& c) {
-  return c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % (2 * T::BK) == 0 && c.lda % 8 == 0 &&
-         c.ldb % 8 == 0 && (reinterpret_cast<uintptr_t>(c.A) & 15u) == 0 &&
+  return c.lda % 8 == 0 && c.ldb % 8 == 0 && c.N % 8 == 0 &&
+         (reinterpret_cast<uintptr_t>(c.A) & 15u) == 0 &&
          (reinterpret_cast<uintptr_t>(c.B) & 15u) == 0 &&
          (int64_t)c.lda * T::BM * 2 < (int64_t(1) << 31) &&
          (int64_t)c.ldb * T::BK * 2 < (int64_t(1) << 31);
+}
+
+template <class T>
+static bool dma_whole(const HgemmCall& c) {
+  return c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % (2 * T::BK) == 0;
 }
 
 template <class T>
@@ -833,11 +902,15 @@ static hipError_t launch_hdma(const HgemmCall& c, int group_m, hipStream_t s) {
   p.A = c.A; p.lda = c.lda; p.B = c.B; p.ldb = c.ldb;
   p.bias = c.bias; p.act = c.act;
   p.C = c.C; p.ldc = c.ldc;
-  p.tiles_m = c.M / T::BM;
-  p.tiles_n = c.N / T::BN;
+  p.tiles_m = (c.M + T::BM - 1) / T::BM;
+  p.tiles_n = (c.N + T::BN - 1) / T::BN;
   p.group_m = group_m;
-  hipLaunchKernelGGL((hgemm_dma_kernel<T>), dim3(p.tiles_m * p.tiles_n), dim3(T::THREADS), 0, s,
-                     p);
+  if (dma_whole<T>(c))
+    hipLaunchKernelGGL((hgemm_dma_kernel<T, false>), dim3(p.tiles_m * p.tiles_n),
+                       dim3(T::THREADS), 0, s, p);
+  else
+    hipLaunchKernelGGL((hgemm_dma_kernel<T, true>), dim3(p.tiles_m * p.tiles_n),
+                       dim3(T::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
@@ -865,13 +938,14 @@ int hgemm_tail_split(int M, int N, int cus) {
 }
 
 int hgemm_resolve_tile(int tile, int M, int N, int K, bool operands_ok, int cus) {
-  // The direct-to-LDS kernels need whole tiles and K a multiple of 64;
-  // otherwise the register-staged 256x256 kernel, which handles every shape, runs.
-  if ((tile == 3 || tile == 5 || tile == 6 || tile == 7) &&
-      !(operands_ok && M % 256 == 0 && N % 256 == 0 && K % 64 == 0))
-    return 0;
-  if (tile == 7 && hgemm_tail_split(M, N, cus) == 0) return 6;
-  if (tile == 4 && !(operands_ok && M % 128 == 0 && N % 256 == 0 && K % 64 == 0)) return 0;
+  // The direct-to-LDS kernels need rows of A and B on 16-byte boundaries and N a
+  // multiple of 8 (ragged M, N and K run their bounds-checked instantiation);
+  // otherwise the register-staged 256x256 kernel, which handles every shape,
+  // runs.  The head/tail column split needs whole 256x256 tiles, K a multiple of
+  // 64 and a split that fills the last round; else the eight-wave tile runs alone.
+  if (tile >= 3 && !(operands_ok && N % 8 == 0)) return 0;
+  if (tile == 7 && !(M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && hgemm_tail_split(M, N, cus) > 0))
+    return 6;
   return tile;
 }
 
@@ -926,7 +1000,8 @@ static hipError_t launch_half(const HgemmCall& c, const HalfPlan& plan, int cus,
       tail.B = c.B + n1;
       tail.C = c.C + n1;
       tail.bias = c.bias ? c.bias + n1 : nullptr;
-      if (n1 == 0 || !dma_fits<HDmaEight<E>>(head) || !dma_fits<HDmaHalfEight<E>>(tail))
+      if (n1 == 0 || !dma_fits<HDmaEight<E>>(head) || !dma_fits<HDmaHalfEight<E>>(tail) ||
+          !dma_whole<HDmaEight<E>>(head) || !dma_whole<HDmaHalfEight<E>>(tail))
         return hipErrorInvalidValue;
       const hipError_t e = launch_hdma<HDmaEight<E>>(head, 4, s);
       if (e != hipSuccess) return e;

@@ -167,8 +167,11 @@ def test_config_rule(so):
         (1, 4096, 14336, 4096, 256, (7, 1)),  # whole 256-tiles, long K: eight waves + tail split
         (1, 4096, 4096, 4096, 256, (6, 1)),   # no partial round: eight waves, no split
         (1, 4096, 4096, 1024, 256, (3, 1)),   # shorter K: four waves
-        (1, 4096, 4000, 4096, 256, (0, 1)),
-        (1, 2048, 2000, 4096, 256, (2, 1)),
+        (1, 4096, 4000, 4096, 256, (6, 1)),   # ragged N: eight waves, no column split
+        (1, 4096, 4004, 4096, 256, (0, 1)),   # N not a multiple of 8
+        (1, 2048, 2000, 4096, 256, (6, 1)),   # ragged N: 64x64 would run bounds-checked
+        (1, 1000, 1000, 1000, 256, (4, 1)),   # ragged, 16 tiles of 256x256: 128x256
+        (1, 1000, 1004, 1000, 256, (2, 1)),   # N not a multiple of 8: register-staged
         (1, 4096, 2048, 4096, 256, (1, 1)),   # 512 tiles of 128x128
         (1, 4096, 4096, 256, 256, (1, 1)),    # K < 512: not the 256x256 tiles
         (1, 300, 500, 4096, 256, (2, 22)),     # 40 tiles of 64x64: ~4 workgroups per CU
@@ -232,16 +235,19 @@ def test_half_split_legality(so):
 
 
 def test_half_tile_resolution(so):
-    """A forced direct-to-LDS tile that the shape does not suit is reported (and run)
-    as the register-staged 256x256 configuration."""
+    """A forced direct-to-LDS tile takes any M, N, K with N a multiple of 8 (ragged
+    edges and K run its bounds-checked instantiation); otherwise it is reported (and
+    run) as the register-staged 256x256 configuration."""
     try:
         assert lib.gemm_debug_force_tile(1, 3) == lib.STATUS_SUCCESS
         assert pick(1, 4096, 4096, 4096)[0] == 3
-        assert pick(1, 300, 512, 4096)[0] == 0
-        assert pick(1, 512, 512, 96)[0] == 0
+        assert pick(1, 300, 512, 4096)[0] == 3
+        assert pick(1, 512, 512, 96)[0] == 3
+        assert pick(1, 512, 516, 96)[0] == 0       # N not a multiple of 8
         assert lib.gemm_debug_force_tile(1, 4) == lib.STATUS_SUCCESS
         assert pick(1, 128, 256, 64)[0] == 4
-        assert pick(1, 128, 128, 64)[0] == 0
+        assert pick(1, 128, 128, 64)[0] == 4
+        assert pick(1, 128, 132, 64)[0] == 0
         assert lib.gemm_debug_force_tile(1, 1) == lib.STATUS_SUCCESS
         assert pick(1, 128, 128, 64)[0] == 1
         # tile 7 splits the columns only where whole rounds plus one short round exist
@@ -251,7 +257,8 @@ def test_half_tile_resolution(so):
         assert pick(1, 4096, 5120, 128)[0] == 7
         assert pick(1, 4096, 5120, 128, cus=128)[0] == 7   # 2 rounds + 128 half tiles
         assert pick(1, 4096, 5120, 128, cus=64)[0] == 6    # the tail would need 2 rounds
-        assert pick(1, 300, 5120, 128)[0] == 0
+        assert pick(1, 300, 5120, 128)[0] == 6     # ragged M: no split, the eight-wave tile
+        assert pick(1, 300, 5124, 128)[0] == 0
     finally:
         lib.gemm_debug_force_tile(1, -1)
 

@@ -149,3 +149,25 @@ def test_unaligned_operands_resolve_to_register_staged(forced):
     assert lib.gemm_debug_pick_config(0, 300, 258, 100, 256) == (4, 1)
     check(300, 258, 100, 1.0, 0.5, seed=971, label="N = 258")
     check(300, 256, 101, 1.0, 0.5, seed=972, label="lda = 101")
+
+
+@pytest.mark.parametrize("shape,want", [((4000, 4000, 4008), (9, 1)), ((6000, 6000, 6000), (8, 1)),
+                                        ((2800, 2800, 2800), (9, 2)),
+                                        ((4000, 2000, 3000), (9, 2))])
+def test_auto_choice_large_ragged(shape, want):
+    """Full-size ragged products on the configuration the library picks, checked on
+    sampled outputs (the four corners, the last row and column, and uniform picks)."""
+    import oracle
+    M, N, K = shape
+    assert lib.gemm_debug_pick_config(
+        0, M, N, K, torch.cuda.get_device_properties(0).multi_processor_count) == want
+    A, B, C = inputs.sgemm_inputs(M, N, K, 981 + M)
+    note("sgemm direct-to-LDS edge auto %dx%dx%d (expect tile %d x%d)" % (M, N, K, *want))
+    got = run_sgemm(M, N, K, 1.5, A, K, B, N, -0.25, C, N).cpu()
+    assert torch.isfinite(got).all()
+    rows, cols = inputs.sample_indices(M, N, 2048, M + N)
+    ref, den = oracle.sgemm_entries(K, 1.5, A.numpy(), K, B.numpy(), N, -0.25, C.numpy(), N,
+                                    rows, cols)
+    e = oracle.normalized_error(got.numpy()[rows, cols], ref, den)
+    assert float(e.max()) <= FP32_TOL, "max normalised error %.3g at sample %d" % (
+        e.max(), int(e.argmax()))
