@@ -55,6 +55,10 @@ typedef enum {
 /*
  * Initialise the library for the current HIP device.  Checks that the device
  * is gfx950 (else GEMM_STATUS_ARCH_MISMATCH) and records its compute-unit count.
+ * Allocates the library's device memory: a 64 MiB workspace for split-K
+ * partial sums and a 256 MiB buffer for packed copies of operands whose rows
+ * do not start on 16-byte boundaries (a call may copy such an operand there,
+ * with padded rows, so that its fastest kernels can read it).
  * Reference counted: each successful gemm_create needs one gemm_destroy.
  */
 int gemm_create(void);

@@ -18,8 +18,9 @@ extern "C" {
  * largest tile, 1 = medium, 2 = small; sgemm also has 3 = largest tile with a
  * K step of 32, 4 = 128 x 256 tiles at two workgroups per compute unit, 5
  * and 6 = tiles 0 and 4 built from 16 x 16 x 4 MFMA blocks, and 7 and 8 = tiles
- * 0 and 4 with direct-to-LDS copies (lda, ldb and N multiples of 4 and A, B
- * 16-byte aligned, else tile 4; ragged M, N or K run their bounds-checked
+ * 0 and 4 with direct-to-LDS copies (rows of A and B on 16-byte boundaries and
+ * N a multiple of 4, else the operands are packed when the copy is small next
+ * to the product, else tile 4 runs; ragged M, N or K run their bounds-checked
  * instantiation), 9 = tile 7 with eight waves; the
  * half products also have 3 = 256 x 256 and 4 = 128 x 256 direct-to-LDS kernels
  * 5 = the 256 x 256 one with a five-stage pipeline, 6 = the 256 x 256 one
@@ -54,13 +55,14 @@ int gemm_debug_use_tuned_table(int on);
 /*
  * The configuration the library would run for an M x N x K product on a device
  * with `cus` compute units, forced values included: *tile receives the tile
- * configuration, *splits the number of K chunks (1 = no split).  op 0 = sgemm
- * with packed operands (lda = K, ldb = N) on 16-byte-aligned bases; op 1 = the
- * half products with 16-byte-aligned
- * operands and lda, ldb multiples of 8 (a direct-to-LDS tile the shape does not
- * suit is reported as the tile that runs instead).  Returns GEMM_STATUS_INVALID_VALUE for an
- * unknown op, negative sizes, cus <= 0 or a null output pointer.  Pure host
- * computation: no HIP call, no library state needed.
+ * configuration, *splits the number of K chunks (1 = no split).  op 0 = sgemm,
+ * op 1 = the half products, both with packed operands (lda = K, ldb = N) on
+ * 16-byte-aligned bases; where those rows do not suit the direct-to-LDS
+ * kernels (K or N not a multiple of 4 for sgemm, of 8 for the half products),
+ * the call would pack them into the library's buffer when the copy is small
+ * next to the product, and the result says what then runs.  Returns GEMM_STATUS_INVALID_VALUE for an unknown op,
+ * negative sizes, cus <= 0 or a null output pointer.  Pure host computation:
+ * no HIP call, no library state needed.
  */
 int gemm_debug_pick_config(int op, int M, int N, int K, int cus, int* tile, int* splits);
 

@@ -28,14 +28,17 @@ struct LibraryState {
   int cus = 256;
 };
 
-// Split-K workspace: FP32 partials, allocated by gemm_create and shared by all
-// calls.  Calls on different streams take turns: each split-K call first
-// waits for the event recorded after the previous one (when that ran on
-// another stream), then records the event after its own reduction.
+// Workspace: FP32 split-K partials and the buffer for packed operand copies,
+// allocated by gemm_create and shared by all calls.  Calls on different
+// streams take turns: each call that uses them first waits for the event
+// recorded after the previous one (when that ran on another stream), then
+// records the event after its own kernels.
 struct Workspace {
   std::mutex mu;
   float* ptr = nullptr;
   size_t floats = 0;
+  void* pack = nullptr;
+  size_t pack_bytes = 0;
   hipEvent_t done = nullptr;
   hipStream_t last = nullptr;
   bool used = false;
@@ -60,24 +63,89 @@ int hip_failure(hipError_t e) {
 
 bool ld_ok(int ld, int cols) { return ld >= (cols > 1 ? cols : 1); }
 
-// Runs `launch(ws)` with the split-K workspace, ordered after the previous
+// Runs `launch(ws, pack)` with the workspace, ordered after the previous
 // workspace user when that ran on another stream, and records the event after it.
 template <class F>
 int with_workspace(hipStream_t stream, F launch) {
   std::lock_guard<std::mutex> wl(g_ws.mu);
-  if (g_ws.ptr == nullptr) return GEMM_STATUS_NOT_INITIALIZED;
+  if (g_ws.ptr == nullptr || g_ws.pack == nullptr) return GEMM_STATUS_NOT_INITIALIZED;
   hipError_t e;
   if (g_ws.used && g_ws.last != stream) {
     e = hipStreamWaitEvent(stream, g_ws.done, 0);
     if (e != hipSuccess) return hip_failure(e);
   }
-  e = launch(g_ws.ptr);
+  e = launch(g_ws.ptr, g_ws.pack);
   if (e != hipSuccess) return hip_failure(e);
   e = hipEventRecord(g_ws.done, stream);
   if (e != hipSuccess) return hip_failure(e);
   g_ws.last = stream;
   g_ws.used = true;
   return GEMM_STATUS_SUCCESS;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Operand packing.  The direct-to-LDS kernels copy 16-byte chunks, so they need
+// rows of A and B on 16-byte boundaries and B readable in whole chunks up to N;
+// the register-staged kernels read such rows with 16-byte loads too.  Where an
+// operand falls short, it is copied once per call into the library's pack
+// buffer, rows padded to a multiple of 16 bytes with zeros, and the product
+// reads the copy.  The copy costs a kernel launch and moves 2 x its bytes through HBM; it
+// is made only when it fits the buffer and is small next to the product:
+// 2 M N K of at least 2^28 FLOP (a few microseconds of work, the order of a
+// launch) and at least 64 FLOP per byte moved.
+struct Packing {
+  bool a = false, b = false;
+  int lda = 0, ldb = 0;    // leading dimensions of the copies (elements)
+  size_t b_offset = 0;     // byte offset of B's copy in the buffer
+};
+
+bool plan_packing(int M, int N, int K, bool a_ok, bool b_ok, size_t elem, size_t cap_bytes,
+                  Packing& pk) {
+  const size_t chunk = 16 / elem;
+  pk.a = !a_ok;
+  pk.b = !b_ok;
+  pk.lda = (int)round_up((size_t)K, chunk);
+  pk.ldb = (int)round_up((size_t)N, chunk);
+  const size_t a_bytes = pk.a ? round_up((size_t)M * pk.lda * elem, 256) : 0;
+  const size_t b_bytes = pk.b ? (size_t)K * pk.ldb * elem : 0;
+  pk.b_offset = a_bytes;
+  const double flops = 2.0 * M * N * K;
+  return a_bytes + b_bytes <= cap_bytes && flops >= (double)(1 << 28) &&
+         flops >= 64.0 * 2.0 * (double)(a_bytes + b_bytes);
+}
+
+// Direct-to-LDS operand conditions of the FP32 product (rows 16-byte aligned,
+// B readable in whole 4-float chunks, 32-bit copy offsets).
+bool sgemm_a_ok(const void* A, int lda) {
+  return lda % 4 == 0 && aligned16(A) && (int64_t)lda * 256 * 4 < (int64_t(1) << 31);
+}
+bool sgemm_b_ok(const void* B, int ldb, int N) {
+  return ldb % 4 == 0 && N % 4 == 0 && aligned16(B) && (int64_t)ldb * 16 * 4 < (int64_t(1) << 31);
+}
+// The same for the half products (8-half chunks).
+bool half_a_ok(const void* A, int lda) {
+  return lda % 8 == 0 && aligned16(A) && (int64_t)lda * 256 * 2 < (int64_t(1) << 31);
+}
+bool half_b_ok(const void* B, int ldb, int N) {
+  return ldb % 8 == 0 && N % 8 == 0 && aligned16(B) && (int64_t)ldb * 32 * 2 < (int64_t(1) << 31);
+}
+
+// The FP32 plan, and whether (and how) operands are packed for it.
+lasg::SgemmPlan decide_sgemm(int M, int N, int K, bool a_ok, bool b_ok, int cus, size_t ws_floats,
+                             size_t pack_bytes, Packing& pk, bool& pack) {
+  const int ft = g_force_sgemm_tile.load(), fs = g_force_sgemm_splits.load();
+  pack = !(a_ok && b_ok) && plan_packing(M, N, K, a_ok, b_ok, 4, pack_bytes, pk);
+  return lasg::plan_sgemm(M, N, K, cus, ft, fs, ws_floats, pack || (a_ok && b_ok));
+}
+
+lasg::HalfPlan decide_half(int M, int N, int K, bool a_ok, bool b_ok, int cus, size_t ws_floats,
+                           size_t pack_bytes, Packing& pk, bool& pack) {
+  const int ft = g_force_hgemm_tile.load(), fs = g_force_half_splits.load();
+  pack = K > 0 && !(a_ok && b_ok) && plan_packing(M, N, K, a_ok, b_ok, 2, pack_bytes, pk);
+  return lasg::plan_half(M, N, K, cus, ft, fs, ws_floats, pack || (a_ok && b_ok));
 }
 
 }  // namespace
@@ -106,14 +174,23 @@ int gemm_create(void) {
     void* ptr = nullptr;
     e = hipMalloc(&ptr, lasg::kWorkspaceBytes);
     if (e != hipSuccess) return hip_failure(e);
-    hipEvent_t ev = nullptr;
-    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    void* pack = nullptr;
+    e = hipMalloc(&pack, lasg::kPackBytes);
     if (e != hipSuccess) {
       (void)hipFree(ptr);
       return hip_failure(e);
     }
+    hipEvent_t ev = nullptr;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      (void)hipFree(ptr);
+      (void)hipFree(pack);
+      return hip_failure(e);
+    }
     g_ws.ptr = static_cast<float*>(ptr);
     g_ws.floats = lasg::kWorkspaceBytes / sizeof(float);
+    g_ws.pack = pack;
+    g_ws.pack_bytes = lasg::kPackBytes;
     g_ws.done = ev;
     g_ws.last = nullptr;
     g_ws.used = false;
@@ -137,8 +214,11 @@ int gemm_destroy(void) {
     hipError_t e = hipDeviceSynchronize();
     if (g_ws.done) (void)hipEventDestroy(g_ws.done);
     if (g_ws.ptr) (void)hipFree(g_ws.ptr);
+    if (g_ws.pack) (void)hipFree(g_ws.pack);
     g_ws.ptr = nullptr;
     g_ws.floats = 0;
+    g_ws.pack = nullptr;
+    g_ws.pack_bytes = 0;
     g_ws.done = nullptr;
     g_ws.used = false;
     if (e != hipSuccess) return hip_failure(e);
@@ -164,14 +244,31 @@ int sgemm(int M, int N, int K, float alpha, const float* A, int lda, const float
     e = lasg::launch_sgemm_scale(M, N, beta, C, ldc, stream);
   } else {
     lasg::SgemmCall c{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
-    const bool operands_ok = lda % 4 == 0 && ldb % 4 == 0 &&
-                             (reinterpret_cast<uintptr_t>(A) & 15u) == 0 &&
-                             (reinterpret_cast<uintptr_t>(B) & 15u) == 0;
+    Packing pk;
+    bool pack = false;
     const lasg::SgemmPlan plan =
-        lasg::plan_sgemm(M, N, K, g_cus.load(), g_force_sgemm_tile.load(),
-                         g_force_sgemm_splits.load(), g_ws.floats, operands_ok);
-    if (plan.splits > 1) {
-      return with_workspace(stream, [&](float* ws) { return lasg::launch_sgemm(c, plan, ws, stream); });
+        decide_sgemm(M, N, K, sgemm_a_ok(A, lda), sgemm_b_ok(B, ldb, N), g_cus.load(),
+                     g_ws.floats, g_ws.pack_bytes, pk, pack);
+    if (plan.splits > 1 || pack) {
+      return with_workspace(stream, [&](float* ws, void* pbuf) {
+        lasg::SgemmCall cc = c;
+        if (pack && pk.a) {
+          float* a = static_cast<float*>(pbuf);
+          const hipError_t pe = lasg::launch_pack_f32(A, M, K, lda, a, pk.lda, stream);
+          if (pe != hipSuccess) return pe;
+          cc.A = a;
+          cc.lda = pk.lda;
+        }
+        if (pack && pk.b) {
+          float* b = reinterpret_cast<float*>(static_cast<char*>(pbuf) + pk.b_offset);
+          const hipError_t pe = lasg::launch_pack_f32(B, K, N, ldb, b, pk.ldb, stream);
+          if (pe != hipSuccess) return pe;
+          cc.B = b;
+          cc.ldb = pk.ldb;
+          cc.nb = pk.ldb;
+        }
+        return lasg::launch_sgemm(cc, plan, ws, stream);
+      });
     } else {
       e = lasg::launch_sgemm(c, plan, nullptr, stream);
     }
@@ -197,14 +294,32 @@ int half_product(bool bf16, int M, int N, int K, float alpha, const uint16_t* A,
   // skips its K loop and still applies bias and activation.
   lasg::HgemmCall c{M, N, reads_ab ? K : 0, alpha, A, lda, B, ldb, bias, act, C, ldc};
   const int cus = g_cus.load();
-  const lasg::HalfPlan plan = lasg::plan_half_call(c, cus, g_force_hgemm_tile.load(),
-                                                   g_force_half_splits.load(), g_ws.floats);
-  auto launch = [&](float* ws) {
-    return bf16 ? lasg::launch_bgemm(c, plan, cus, ws, stream)
-                : lasg::launch_hgemm(c, plan, cus, ws, stream);
+  Packing pk;
+  bool pack = false;
+  const lasg::HalfPlan plan = decide_half(M, N, c.K, half_a_ok(A, lda), half_b_ok(B, ldb, N), cus,
+                                          g_ws.floats, g_ws.pack_bytes, pk, pack);
+  auto launch = [&](float* ws, void* pbuf) {
+    lasg::HgemmCall cc = c;
+    if (pack && pk.a) {
+      uint16_t* a = static_cast<uint16_t*>(pbuf);
+      const hipError_t pe = lasg::launch_pack_u16(A, M, K, lda, a, pk.lda, stream);
+      if (pe != hipSuccess) return pe;
+      cc.A = a;
+      cc.lda = pk.lda;
+    }
+    if (pack && pk.b) {
+      uint16_t* b = reinterpret_cast<uint16_t*>(static_cast<char*>(pbuf) + pk.b_offset);
+      const hipError_t pe = lasg::launch_pack_u16(B, K, N, ldb, b, pk.ldb, stream);
+      if (pe != hipSuccess) return pe;
+      cc.B = b;
+      cc.ldb = pk.ldb;
+      cc.nb = pk.ldb;
+    }
+    return bf16 ? lasg::launch_bgemm(cc, plan, cus, ws, stream)
+                : lasg::launch_hgemm(cc, plan, cus, ws, stream);
   };
-  if (plan.splits > 1) return with_workspace(stream, launch);
-  const hipError_t e = launch(nullptr);
+  if (plan.splits > 1 || pack) return with_workspace(stream, launch);
+  const hipError_t e = launch(nullptr, nullptr);
   return e == hipSuccess ? GEMM_STATUS_SUCCESS : hip_failure(e);
 }
 
@@ -261,17 +376,21 @@ int gemm_debug_pick_config(int op, int M, int N, int K, int cus, int* tile, int*
     return GEMM_STATUS_INVALID_VALUE;
   if (op == 0) {
     // Packed operands (lda = K, ldb = N) on 16-byte-aligned bases.
+    Packing pk;
+    bool pack = false;
     const lasg::SgemmPlan p =
-        lasg::plan_sgemm(M, N, K, cus, g_force_sgemm_tile.load(), g_force_sgemm_splits.load(),
-                         lasg::kWorkspaceBytes / sizeof(float), K % 4 == 0 && N % 4 == 0);
+        decide_sgemm(M, N, K, K % 4 == 0, N % 4 == 0, cus, lasg::kWorkspaceBytes / sizeof(float),
+                     lasg::kPackBytes, pk, pack);
     *tile = p.tile;
     *splits = p.splits;
     return GEMM_STATUS_SUCCESS;
   }
   if (op == 1) {
+    Packing pk;
+    bool pack = false;
     const lasg::HalfPlan p =
-        lasg::plan_half(M, N, K, cus, g_force_hgemm_tile.load(), g_force_half_splits.load(),
-                        lasg::kWorkspaceBytes / sizeof(float), true);
+        decide_half(M, N, K, K % 8 == 0, N % 8 == 0, cus, lasg::kWorkspaceBytes / sizeof(float),
+                    lasg::kPackBytes, pk, pack);
     *tile = p.tile;
     *splits = p.splits;
     return GEMM_STATUS_SUCCESS;

@@ -69,7 +69,8 @@ long round_use(long tiles, int cus, int per_cu) {
 // Built-in tile rule, measured on MI355X (the size sweep over powers of two and
 // a sweep of ragged shapes):
 //  * The direct-to-LDS kernels wherever their copies are legal (rows of A and B
-//    16-byte aligned, N a multiple of 4) and their 256x256 tiles cover the CUs:
+//    16-byte aligned, B readable in whole 4-float chunks: `operands_ok`, which
+//    holds after packing too) and their 256x256 tiles cover the CUs:
 //    eight waves of 256x256 (4096^3: 146 TFLOP/s, 8192^3: 149; ragged 4000^3:
 //    138 vs 111 for the best register-staged tile), or 128x256 at two per CU
 //    when that wastes less of the last round (6000^3: 116 vs 104; 7000 x 3000 x
@@ -89,7 +90,7 @@ int sgemm_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_tall = ceil_div(M, 128) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
-  const bool direct = operands_ok && N % 4 == 0;
+  const bool direct = operands_ok;
   const bool whole = M % 256 == 0 && N % 256 == 0 && K % 32 == 0;
   if (direct && t_large >= cus && (whole || K >= 384))
     return 89 * round_use(t_tall, cus, 2) > 93 * round_use(t_large, cus, 1) ? 8 : 9;
@@ -144,7 +145,7 @@ SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_spl
   // Table entries were measured on whole tiles with packed aligned operands;
   // where the entry's tile would run bounds-checked here, the rule chooses
   // instead (it knows the ragged shapes).
-  if (tuned && !(operands_ok && N % 4 == 0 && M % sgemm_tile_bm(tuned_tile) == 0 &&
+  if (tuned && !(operands_ok && M % sgemm_tile_bm(tuned_tile) == 0 &&
                  N % sgemm_tile_bn(tuned_tile) == 0 && K % sgemm_tile_bk(tuned_tile) == 0))
     tuned = false;
   SgemmPlan p;
@@ -183,7 +184,8 @@ namespace {
 int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   // Built-in rule (from the size sweep): 256x256 tiles once they give every CU
   // one and K is at least 512 -- with direct-to-LDS copies when the operands
-  // allow them (rows of A and B 16-byte aligned, N a multiple of 8): eight waves
+  // allow them (`operands_ok`: rows of A and B 16-byte aligned, B readable in
+  // whole 8-half chunks, as given or after packing): eight waves
   // with the head/tail column split (tile 7, which runs as tile 6 where no split
   // exists) for K >= 2048, four waves (tile 3) for shorter K, where the
   // eight-wave tile lost up to 14 % -- else 128x128 tiles once they give every
@@ -193,10 +195,12 @@ int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   // every size measured (3000^3: 652 TFLOP/s for the eight-wave tile vs 92 for
   // the best register-staged one; 2000 x 7000 x 2000: 865 vs 136): the
   // eight-wave 256x256 tile, or 128x256 where fewer than 64 256x256 tiles exist
-  // and K is below 2048 (1000^3: 68 vs 65; 1000 x 1000 x 4000: 75 vs 97).
+  // and K is below 2048 (1000^3: 68 vs 65; 1000 x 1000 x 4000: 75 vs 97) -- as
+  // long as there are 16 tiles of 128x256; below that the split 64x64 tile is
+  // ahead (504 x 504 x 8000: 33 vs 27).
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
-  const bool direct = operands_ok && N % 8 == 0;
+  const bool direct = operands_ok;
   if (t_large >= cus && K >= 512) {
     if (!direct) return 0;
     return K >= 2048 ? 7 : 3;
@@ -204,7 +208,8 @@ int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   const int reg = t_med >= 2L * cus ? 1 : 2;
   const int bm = half_tile_bm(reg);
   const bool reg_whole = M % bm == 0 && N % bm == 0 && K % kHalfBK == 0;
-  if (direct && !reg_whole) return (t_large >= 64 || K >= 2048) ? 6 : 4;
+  const long t_tall = ceil_div(M, 128) * ceil_div(N, 256);
+  if (direct && !reg_whole && t_tall >= 16) return (t_large >= 64 || K >= 2048) ? 6 : 4;
   return reg;
 }
 
@@ -234,7 +239,7 @@ HalfPlan plan_half(int M, int N, int K, int cus, int force_tile, int force_split
   if (tuned) {
     const int bm = tuned_tile <= 2 ? half_tile_bm(tuned_tile) : tuned_tile == 4 ? 128 : 256;
     const int bn = tuned_tile <= 2 ? bm : 256;
-    if (!(operands_ok && N % 8 == 0 && M % bm == 0 && N % bn == 0 && K % kHalfBK == 0))
+    if (!(operands_ok && M % bm == 0 && N % bn == 0 && K % kHalfBK == 0))
       tuned = false;
   }
   HalfPlan p;

@@ -17,6 +17,9 @@ struct SgemmCall {
   int ldb;
   float* C;
   int ldc;
+  // Columns of each row of B that may be read (at least N; more when B is a
+  // padded copy); 0 means N.
+  int nb = 0;
 };
 
 struct HgemmCall {
@@ -30,20 +33,27 @@ struct HgemmCall {
   int act;
   uint16_t* C;
   int ldc;
+  // Columns of each row of B that may be read (at least N; more when B is a
+  // padded copy); 0 means N.
+  int nb = 0;
 };
+
+inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 
 // Tile configurations.  SGEMM: 0 = 256x256 (K step 16), 1 = 128x128, 2 = 64x64,
 // 3 = 256x256 with K step 32, 4 = 128x256 at two workgroups per CU (all with
 // 32x32x2 MFMA blocks); 5 = 256x256 and 6 = 128x256 at two
 // workgroups per CU, both with 16x16x4 MFMA blocks; 7 = 256x256 and 8 = 128x256
 // at two workgroups per CU with direct-to-LDS copies into a multi-stage ring
-// (whole tiles only, else tile 4); 9 = tile 7 with eight waves, two per SIMD.
+// (rows of A and B 16-byte aligned and B readable in whole 4-float chunks, else
+// tile 4); 9 = tile 7 with eight waves, two per SIMD.
 // HGEMM: 0 = 256x256, 1 = 128x128, 2 = 64x64 (register-staged, K step 64),
 // 3 = 256x256 direct-to-LDS, 4 stages of K step 32, 4 = 128x256 direct-to-LDS,
 // 3 stages, two workgroups per CU, 5 = 256x256 direct-to-LDS, 5 stages, 6 = 256x256
 // direct-to-LDS with eight waves, 7 = tile 6 on the columns that fill whole
 // rounds of workgroups and 128 x 256 direct-to-LDS tiles on the rest (3 to 7 need
-// whole tiles and K a multiple of 64; other shapes fall back to 0).
+// rows of A and B 16-byte aligned and B readable in whole 8-half chunks, 7 also
+// whole tiles; other operands fall back to 0).
 constexpr int kSgemmTileCount = 10;
 constexpr int kHgemmTileCount = 8;
 
@@ -63,6 +73,9 @@ constexpr int kMaxSplits = 32;
 // Library-owned FP32 workspace for split-K partials (per device, allocated by
 // gemm_create): splits * M * N floats must fit.
 constexpr size_t kWorkspaceBytes = size_t(64) << 20;
+// Library-owned buffer for packed copies of operands whose rows are not 16-byte
+// aligned (allocated by gemm_create beside the workspace).
+constexpr size_t kPackBytes = size_t(256) << 20;
 
 // How one SGEMM call runs: tile configuration, number of K chunks (1 = no
 // split) and the chunk length in elements (a multiple of the tile's K step).
@@ -72,16 +85,17 @@ struct SgemmPlan {
   int k_chunk;
 };
 
-// The plan for an M x N x K product on `cus` compute units (`operands_ok`: lda
-// and ldb multiples of 4, A and B 16-byte aligned).  force_tile / force_splits
+// The plan for an M x N x K product on `cus` compute units (`operands_ok`: the
+// direct-to-LDS copies are legal: lda and ldb multiples of 4, A and B 16-byte
+// aligned, B readable in whole 4-float chunks).  force_tile / force_splits
 // < 0 let the shape decide (offline-tuned table, else the built-in rule); the
 // split count is then clamped to the K tiles there are and to `ws_floats` of
 // workspace.
 SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_splits,
                      size_t ws_floats, bool operands_ok);
 // The FP32 configuration that actually runs for `tile` with `splits` K chunks:
-// the direct-to-LDS ones (7, 8, 9) become 4 when N is not a multiple of 4 or
-// the operands (`operands_ok` as above) do not suit them.
+// the direct-to-LDS ones (7, 8, 9) become 4 when the operands (`operands_ok` as
+// above) do not suit them.
 int sgemm_resolve_tile(int tile, int M, int N, int K, int splits, bool operands_ok);
 
 // Offline-tuned choice for (op, M, N, K) if the table has one for the shape's
@@ -100,8 +114,8 @@ constexpr int half_tile_bm(int tile) { return tile == 0 ? 256 : tile == 1 ? 128 
 constexpr int kHalfBK = 64;
 
 // The plan for an M x N x K half product on `cus` compute units (`operands_ok`:
-// lda and ldb are multiples of 8 and A, B 16-byte aligned, as the direct-to-LDS
-// kernels need).  force_tile / force_splits < 0 let the shape decide (tuned
+// lda and ldb are multiples of 8, A, B 16-byte aligned and B readable in whole
+// 8-half chunks, as the direct-to-LDS kernels need).  force_tile / force_splits < 0 let the shape decide (tuned
 // table, else the built-in rule); the result is resolved to what runs and the
 // split count is clamped to the K tiles and to `ws_floats` of workspace.
 HalfPlan plan_half(int M, int N, int K, int cus, int force_tile, int force_splits,
@@ -126,6 +140,12 @@ void set_use_tuned(bool on);
 // `ws` holds at least plan.splits * M * N floats when plan.splits > 1.
 hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hipStream_t s);
 hipError_t launch_sgemm_scale(int M, int N, float beta, float* C, int ldc, hipStream_t s);
+// dst (rows x ldd, 16-byte aligned) = src (rows x cols, leading dimension lds)
+// with columns [cols, ldd) zero: the packed copy of an operand.
+hipError_t launch_pack_f32(const float* src, int rows, int cols, int lds, float* dst, int ldd,
+                           hipStream_t s);
+hipError_t launch_pack_u16(const uint16_t* src, int rows, int cols, int lds, uint16_t* dst,
+                           int ldd, hipStream_t s);
 
 // The half-precision product: binary16 (hgemm) or bfloat16 (bgemm) inputs and
 // output, FP32 accumulation; same kernels, tiles and tile choice.

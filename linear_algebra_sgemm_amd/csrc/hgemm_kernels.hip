@@ -88,6 +88,9 @@ struct HgemmArgs {
   uint16_t* C;
   int ldc;
   int tiles_m, tiles_n, group_m;
+  // Direct-to-LDS kernels: columns of each row of B that may be read (a multiple
+  // of 8, at least N).
+  int nb;
   // Split-K (register-staged kernel): workgroup row blockIdx.y covers K range
   // [y * k_chunk, min(K, (y + 1) * k_chunk)) and writes its raw FP32 partial to
   // ws + y * M * N (M x N, row stride N).
@@ -375,9 +378,9 @@ __device__ __forceinline__ int a_swizzle(int r) {
 // Global address of the 16-byte chunk that lane `lane` of direct load `v` (0 ..
 // LOADS_PER_TILE - 1) of wave `wave` copies, and the offset of its LDS slot
 // inside one stage.  Rows of A past M - 1 read row M - 1 and 8-column chunks of
-// B past N - 8 read the chunk at N - 8 (N is a multiple of 8), so on a tile that
-// crosses the bottom or right edge every copy stays inside the matrices; those
-// rows and columns of the tile are never stored.  `k_first` / `k_step` give the
+// B at or past nb (the readable width, a multiple of 8) read the chunk at
+// nb - 8, so on a tile that crosses the bottom or right edge every copy stays
+// inside the matrices; those rows and columns of the tile are never stored.  `k_first` / `k_step` give the
 // k of element e of the chunk: k_first + k_step e (8 consecutive k of one A row,
 // or one k for the 8 columns of a B row).
 template <class T>
@@ -409,7 +412,7 @@ __device__ __forceinline__ const uint16_t* hdma_source(const HgemmArgs& p, int m
   stage_offset = T::A_BYTES + ibb * 1024;
   const int row = k0 + 16 * s + 8 * h + 4 * t + q;
   const int col0 = n0 + 32 * jb + 16 * cg + 8 * c2;
-  const int col = col0 <= p.N - 8 ? col0 : p.N - 8;
+  const int col = col0 < p.nb ? col0 : p.nb - 8;
   k_first = row;
   k_step = 0;
   return p.B + (size_t)row * p.ldb + col;
@@ -711,7 +714,7 @@ hgemm_dma_kernel(HgemmArgs p) {
   // columns n = 8 q + 4 (l / 32) + 0..3 of row m = l % 32.
   const float alpha = p.alpha;
   const bool gelu = p.act == 1;
-  if (p.ldc % 8 == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15u) == 0) {
+  if (p.ldc % 8 == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15u) == 0 && (!EDGE || p.N % 8 == 0)) {
     // Through LDS, so that every store instruction writes whole rows: the wave
     // puts its finished WTM x WTN tile into its own region of the (now idle)
     // stages, then reads it back 16 bytes per lane along rows.  16-byte chunks
@@ -757,7 +760,7 @@ hgemm_dma_kernel(HgemmArgs p) {
       const int chunk = lane % CPR;
       const u32x4 v = *reinterpret_cast<const u32x4*>(region + r * RB +
                                                       16 * (chunk ^ ((r / RPL) % CPR)));
-      // (N is a multiple of 8 on the ragged path: a chunk is wholly in or out)
+      // (N is a multiple of 8 here: a chunk is wholly in or out)
       if (EDGE && (m0 + wm * T::WTM + r >= p.M || n0 + wn * T::WTN + 8 * chunk >= p.N)) continue;
       *reinterpret_cast<u32x4*>(p.C + (size_t)(m0 + wm * T::WTM + r) * p.ldc + n0 +
                                 wn * T::WTN + 8 * chunk) = v;
@@ -847,6 +850,7 @@ static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s, i
   p.tiles_n = (c.N + T::BN - 1) / T::BN;
   p.group_m = group_m;
   p.k_chunk = k_chunk;
+  p.nb = c.N;
   p.ws = ws;
   const bool fast = c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % T::BK == 0 &&
                     c.lda % 8 == 0 && c.ldb % 8 == 0 &&
@@ -877,16 +881,22 @@ static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s, i
 }
 
 // The direct-to-LDS kernels copy 16-byte chunks: rows of A and B on 16-byte
-// boundaries, N a multiple of 8 (a chunk of B never crosses the right edge),
-// 32-bit per-lane copy offsets.  Whole tiles with K a multiple of 2 BK run the
-// unchecked instantiation.
-template <class T>
-static bool dma_fits(const HgemmCall& c) {
-  return c.lda % 8 == 0 && c.ldb % 8 == 0 && c.N % 8 == 0 &&
+// boundaries, each row of B readable in whole chunks up to N (nb a multiple of
+// 8), 32-bit per-lane copy offsets (at most 256 rows of A or 32 of B).  Whole
+// tiles with K a multiple of 2 BK run the unchecked instantiation.
+static bool half_operands_ok(const HgemmCall& c) {
+  const int nb = readable_cols(c.nb, c.N);
+  return c.lda % 8 == 0 && c.ldb % 8 == 0 && nb % 8 == 0 && nb >= c.N && nb <= c.ldb &&
          (reinterpret_cast<uintptr_t>(c.A) & 15u) == 0 &&
          (reinterpret_cast<uintptr_t>(c.B) & 15u) == 0 &&
-         (int64_t)c.lda * T::BM * 2 < (int64_t(1) << 31) &&
-         (int64_t)c.ldb * T::BK * 2 < (int64_t(1) << 31);
+         (int64_t)c.lda * 256 * 2 < (int64_t(1) << 31) &&
+         (int64_t)c.ldb * 32 * 2 < (int64_t(1) << 31);
+}
+
+template <class T>
+static bool dma_fits(const HgemmCall& c) {
+  static_assert(T::BM <= 256 && T::BK == 32, "half_operands_ok's offset bounds");
+  return half_operands_ok(c);
 }
 
 template <class T>
@@ -905,6 +915,7 @@ static hipError_t launch_hdma(const HgemmCall& c, int group_m, hipStream_t s) {
   p.tiles_m = (c.M + T::BM - 1) / T::BM;
   p.tiles_n = (c.N + T::BN - 1) / T::BN;
   p.group_m = group_m;
+  p.nb = readable_cols(c.nb, c.N);
   if (dma_whole<T>(c))
     hipLaunchKernelGGL((hgemm_dma_kernel<T, false>), dim3(p.tiles_m * p.tiles_n),
                        dim3(T::THREADS), 0, s, p);
@@ -938,24 +949,16 @@ int hgemm_tail_split(int M, int N, int cus) {
 }
 
 int hgemm_resolve_tile(int tile, int M, int N, int K, bool operands_ok, int cus) {
-  // The direct-to-LDS kernels need rows of A and B on 16-byte boundaries and N a
-  // multiple of 8 (ragged M, N and K run their bounds-checked instantiation);
-  // otherwise the register-staged 256x256 kernel, which handles every shape,
-  // runs.  The head/tail column split needs whole 256x256 tiles, K a multiple of
-  // 64 and a split that fills the last round; else the eight-wave tile runs alone.
-  if (tile >= 3 && !(operands_ok && N % 8 == 0)) return 0;
+  // The direct-to-LDS kernels need rows of A and B on 16-byte boundaries and B
+  // readable in whole 8-half chunks (ragged M, N and K run their bounds-checked
+  // instantiation); otherwise the register-staged 256x256 kernel, which handles
+  // every shape, runs.  The head/tail column split needs whole 256x256 tiles, K
+  // a multiple of 64 and a split that fills the last round; else the eight-wave
+  // tile runs alone.
+  if (tile >= 3 && !operands_ok) return 0;
   if (tile == 7 && !(M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && hgemm_tail_split(M, N, cus) > 0))
     return 6;
   return tile;
-}
-
-static bool half_operands_ok(const HgemmCall& c) {
-  // The direct loads address A and B as a tile base plus a 32-bit byte offset
-  // of at most 256 rows of A or 32 rows of B.
-  return c.lda % 8 == 0 && c.ldb % 8 == 0 && (reinterpret_cast<uintptr_t>(c.A) & 15u) == 0 &&
-         (reinterpret_cast<uintptr_t>(c.B) & 15u) == 0 &&
-         (int64_t)c.lda * 256 * 2 < (int64_t(1) << 31) &&
-         (int64_t)c.ldb * 32 * 2 < (int64_t(1) << 31);
 }
 
 HalfPlan plan_half_call(const HgemmCall& c, int cus, int force_tile, int force_splits,
@@ -998,6 +1001,7 @@ static hipError_t launch_half(const HgemmCall& c, const HalfPlan& plan, int cus,
       head.N = n1;
       tail.N = c.N - n1;
       tail.B = c.B + n1;
+      if (c.nb > 0) tail.nb = c.nb - n1;
       tail.C = c.C + n1;
       tail.bias = c.bias ? c.bias + n1 : nullptr;
       if (n1 == 0 || !dma_fits<HDmaEight<E>>(head) || !dma_fits<HDmaHalfEight<E>>(tail) ||
@@ -1019,6 +1023,30 @@ hipError_t launch_hgemm(const HgemmCall& c, const HalfPlan& plan, int cus, float
 hipError_t launch_bgemm(const HgemmCall& c, const HalfPlan& plan, int cus, float* ws,
                         hipStream_t s) {
   return launch_half<EltBF16>(c, plan, cus, ws, s);
+}
+
+// Packed copy of an operand: dst (rows x ldd) = src (rows x cols, leading
+// dimension lds), columns [cols, ldd) zero.  Plain element copies, HBM-bound.
+__global__ void __launch_bounds__(256) pack_rows_u16_kernel(int rows, int cols,
+                                                            const uint16_t* src, int lds,
+                                                            uint16_t* dst, int ldd) {
+  const int64_t total = (int64_t)rows * ldd;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = t / ldd, c = t % ldd;
+    dst[t] = c < cols ? src[r * lds + c] : (uint16_t)0;
+  }
+}
+
+hipError_t launch_pack_u16(const uint16_t* src, int rows, int cols, int lds, uint16_t* dst,
+                           int ldd, hipStream_t s) {
+  const int64_t total = (int64_t)rows * ldd;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) return hipSuccess;
+  hipLaunchKernelGGL(pack_rows_u16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, rows, cols,
+                     src, lds, dst, ldd);
+  return hipGetLastError();
 }
 
 }  // namespace lasg

@@ -111,6 +111,9 @@ struct SgemmArgs {
   // Bounds-checked path: rows of A (B) are 16-byte aligned, so a 4-float chunk that
   // lies wholly inside the matrix may be read with one 16-byte load.
   int a_vec, b_vec;
+  // Direct-to-LDS kernels: columns of each row of B that may be read (a multiple
+  // of 4, at least N).
+  int nb;
 };
 
 // Global -> register staging of one K tile.  EDGE selects bounds-checked scalar
@@ -392,9 +395,9 @@ struct SDmaTile {
 // (a_base(kt) = A + m0 lda + 16 kt, b_base(kt) = B + 16 kt ldb + n0, floats),
 // and the LDS slot of copy v inside one stage.  On a tile that crosses the
 // bottom or right edge, rows of A past M - 1 copy row M - 1 and 4-column chunks
-// of B past N - 4 copy the chunk at N - 4 (N is a multiple of 4), so every copy
-// reads inside the matrices; the values land in rows and columns of the tile
-// that the epilogue does not store.
+// of B at or past nb (the readable width, a multiple of 4) copy the chunk at
+// nb - 4, so every copy reads inside the matrices; the values land in rows and
+// columns of the tile that the epilogue does not store.
 template <class T>
 struct SDmaPlan {
   uint32_t off[T::LOADS_PER_TILE];
@@ -408,7 +411,7 @@ struct SDmaPlan {
         off[v] = (uint32_t)(((size_t)rc * p.lda + 4 * chunk) * 4);
       } else {
         const int kr = wave * T::B_PER_WAVE + (v - T::A_PER_WAVE);
-        const int cc = n0 + 4 * lane < p.N ? 4 * lane : p.N - 4 - n0;
+        const int cc = n0 + 4 * lane < p.nb ? 4 * lane : p.nb - 4 - n0;
         off[v] = (uint32_t)(((size_t)kr * p.ldb + cc) * 4);
       }
     }
@@ -563,7 +566,7 @@ __device__ __forceinline__ void sdma_k_tail(const SgemmArgs& p, f32x16 (&acc)[T:
     const int kr = c / (T::BN / 4), cc = 4 * (c % (T::BN / 4));
     const int t = kr / 16;
     const int k = k0 + kr;
-    const int col = n0 + cc < p.N ? n0 + cc : p.N - 4;
+    const int col = n0 + cc < p.nb ? n0 + cc : p.nb - 4;
     f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
     if (k < p.K) v = *reinterpret_cast<const f32x4*>(p.B + (size_t)k * p.ldb + col);
     *reinterpret_cast<f32x4*>(lds + t * T::STAGE_BYTES + T::A_BYTES + (kr % 16) * T::B_ROW +
@@ -752,6 +755,7 @@ static hipError_t launch_tile(const SgemmCall& c, const SgemmPlan& plan, int gro
   p.ws = ws;
   p.a_vec = c.lda % 4 == 0 && aligned16(c.A);
   p.b_vec = c.ldb % 4 == 0 && aligned16(c.B);
+  p.nb = c.N;
   const bool edge = !(c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % T::BK == 0 &&
                       c.lda % 4 == 0 && c.ldb % 4 == 0 && aligned16(c.A) && aligned16(c.B));
   const bool split = plan.splits > 1;
@@ -773,14 +777,20 @@ static hipError_t launch_tile(const SgemmCall& c, const SgemmPlan& plan, int gro
 }
 
 // The direct-to-LDS kernels copy 16-byte chunks: rows of A and B must start on
-// 16-byte boundaries and N must be a multiple of 4 (a chunk of B never crosses
-// the matrix's right edge); the per-lane copy offsets are 32-bit.  Whole tiles
+// 16-byte boundaries and each row of B must be readable in whole chunks up to
+// N (nb a multiple of 4); the per-lane copy offsets are 32-bit.  Whole tiles
 // with K a multiple of 32 run the unchecked instantiation.
+static bool direct_operands_ok(const SgemmCall& c) {
+  const int nb = readable_cols(c.nb, c.N);
+  return c.lda % 4 == 0 && c.ldb % 4 == 0 && nb % 4 == 0 && nb >= c.N && nb <= c.ldb &&
+         aligned16(c.A) && aligned16(c.B) && (int64_t)c.lda * 256 * 4 < (int64_t(1) << 31) &&
+         (int64_t)c.ldb * 16 * 4 < (int64_t(1) << 31);
+}
+
 template <class T>
 static bool sdma_fits(const SgemmCall& c) {
-  return c.lda % 4 == 0 && c.ldb % 4 == 0 && c.N % 4 == 0 && aligned16(c.A) && aligned16(c.B) &&
-         (int64_t)c.lda * T::BM * 4 < (int64_t(1) << 31) &&
-         (int64_t)c.ldb * T::BK * 4 < (int64_t(1) << 31);
+  static_assert(T::BM <= 256 && T::BK == 16, "direct_operands_ok's offset bounds");
+  return direct_operands_ok(c);
 }
 
 template <class T>
@@ -819,26 +829,24 @@ static hipError_t launch_sdma(const SgemmCall& c, const SgemmPlan& plan, int gro
   p.k_chunk = plan.splits > 1 ? plan.k_chunk : c.K;
   p.ws = ws;
   p.a_vec = p.b_vec = 1;
+  p.nb = readable_cols(c.nb, c.N);
   if (sdma_whole<T>(c)) return launch_sdma_kernel<T, false>(c, plan, p, ws, s);
   return launch_sdma_kernel<T, true>(c, plan, p, ws, s);
 }
 
 int sgemm_resolve_tile(int tile, int M, int N, int K, int splits, bool operands_ok) {
-  // The direct-to-LDS kernels need rows of A and B on 16-byte boundaries and N a
-  // multiple of 4 (any M, N and K otherwise: ragged edges and a ragged K run a
-  // bounds-checked instantiation); otherwise the register-staged 128 x 256
-  // kernel (the best of those for large outputs) runs.
-  (void)M; (void)K; (void)splits;
-  if (tile >= 7 && !(operands_ok && N % 4 == 0)) return 4;
+  // The direct-to-LDS kernels need rows of A and B on 16-byte boundaries and B
+  // readable in whole 4-float chunks (any M, N and K otherwise: ragged edges and
+  // a ragged K run a bounds-checked instantiation); otherwise the
+  // register-staged 128 x 256 kernel (the best of those for large outputs) runs.
+  (void)M; (void)N; (void)K; (void)splits;
+  if (tile >= 7 && !operands_ok) return 4;
   return tile;
 }
 
 hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hipStream_t s) {
   if (plan.splits > 1 && ws == nullptr) return hipErrorInvalidValue;
-  const bool operands_ok = c.lda % 4 == 0 && c.ldb % 4 == 0 && aligned16(c.A) && aligned16(c.B) &&
-                           (int64_t)c.lda * 256 * 4 < (int64_t(1) << 31) &&
-                           (int64_t)c.ldb * 16 * 4 < (int64_t(1) << 31);
-  switch (sgemm_resolve_tile(plan.tile, c.M, c.N, c.K, plan.splits, operands_ok)) {
+  switch (sgemm_resolve_tile(plan.tile, c.M, c.N, c.K, plan.splits, direct_operands_ok(c))) {
     case 0: return launch_tile<TileLarge>(c, plan, 4, ws, s);
     case 1: return launch_tile<TileMedium>(c, plan, 8, ws, s);
     case 2: return launch_tile<TileSmall>(c, plan, 8, ws, s);
@@ -859,6 +867,29 @@ hipError_t launch_sgemm_scale(int M, int N, float beta, float* C, int ldc, hipSt
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(sgemm_scale_kernel, dim3((unsigned)blocks), dim3(256), 0, s, M, N, beta, C,
                      ldc);
+  return hipGetLastError();
+}
+
+// Packed copy of an operand: dst (rows x ldd) = src (rows x cols, leading
+// dimension lds), columns [cols, ldd) zero.  Plain element copies, HBM-bound.
+__global__ void __launch_bounds__(256) pack_rows_f32_kernel(int rows, int cols, const float* src,
+                                                            int lds, float* dst, int ldd) {
+  const int64_t total = (int64_t)rows * ldd;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = t / ldd, c = t % ldd;
+    dst[t] = c < cols ? src[r * lds + c] : 0.0f;
+  }
+}
+
+hipError_t launch_pack_f32(const float* src, int rows, int cols, int lds, float* dst, int ldd,
+                           hipStream_t s) {
+  const int64_t total = (int64_t)rows * ldd;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) return hipSuccess;
+  hipLaunchKernelGGL(pack_rows_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, rows, cols,
+                     src, lds, dst, ldd);
   return hipGetLastError();
 }
 

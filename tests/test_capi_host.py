@@ -150,8 +150,9 @@ def test_config_rule(so):
         (0, 8192, 8192, 8192, 256, (9, 1)),
         (0, 4096, 4096, 4008, 256, (9, 1)),   # ragged K: the bounds-checked direct-to-LDS kernel
         (0, 4000, 4000, 4000, 256, (9, 1)),   # ragged M, N, K likewise
-        (0, 4096, 4096, 4002, 256, (4, 1)),   # lda = 4002: rows of A not 16-byte aligned
-        (0, 4096, 4090, 4096, 256, (4, 1)),   # N not a multiple of 4
+        (0, 4096, 4096, 4002, 256, (9, 1)),   # lda = 4002: A packed to 16-byte rows first
+        (0, 4096, 4090, 4096, 256, (9, 1)),   # N not a multiple of 4: B packed first
+        (0, 64, 4090, 64, 256, (2, 1)),       # packing B would cost more than it saves
         (0, 256, 256, 256, 256, (2, 1)),      # K < 512: no split
         (0, 256, 256, 1024, 256, (2, 8)),     # 16 tiles; chunks of 128
         (0, 512, 512, 512, 256, (2, 4)),      # 64 tiles; chunks of 128
@@ -168,10 +169,10 @@ def test_config_rule(so):
         (1, 4096, 4096, 4096, 256, (6, 1)),   # no partial round: eight waves, no split
         (1, 4096, 4096, 1024, 256, (3, 1)),   # shorter K: four waves
         (1, 4096, 4000, 4096, 256, (6, 1)),   # ragged N: eight waves, no column split
-        (1, 4096, 4004, 4096, 256, (0, 1)),   # N not a multiple of 8
+        (1, 4096, 4004, 4096, 256, (6, 1)),   # N not a multiple of 8: B packed first
         (1, 2048, 2000, 4096, 256, (6, 1)),   # ragged N: 64x64 would run bounds-checked
         (1, 1000, 1000, 1000, 256, (4, 1)),   # ragged, 16 tiles of 256x256: 128x256
-        (1, 1000, 1004, 1000, 256, (2, 1)),   # N not a multiple of 8: register-staged
+        (1, 1000, 1004, 1000, 256, (4, 1)),   # N not a multiple of 8: B packed, as above
         (1, 4096, 2048, 4096, 256, (1, 1)),   # 512 tiles of 128x128
         (1, 4096, 4096, 256, 256, (1, 1)),    # K < 512: not the 256x256 tiles
         (1, 300, 500, 4096, 256, (2, 22)),     # 40 tiles of 64x64: ~4 workgroups per CU
@@ -202,7 +203,8 @@ def test_sgemm_direct_tile_resolution(so):
         assert pick(0, 4096, 4096, 4096) == (7, 1)
         assert pick(0, 4096, 4096, 4008) == (7, 1)      # K not a multiple of 32
         assert pick(0, 4000, 4096, 4096) == (7, 1)      # ragged M
-        assert pick(0, 4096, 4090, 4096) == (4, 1)      # N not a multiple of 4
+        assert pick(0, 4096, 4090, 4096) == (7, 1)      # N not a multiple of 4: B packed
+        assert pick(0, 64, 4090, 64) == (4, 1)          # packing costs more than it saves
         assert lib.gemm_debug_force_splits(0, 4) == lib.STATUS_SUCCESS
         assert pick(0, 256, 256, 4096) == (7, 4)        # the direct-to-LDS tiles split too
         assert pick(0, 300, 260, 1000) == (7, 4)        # chunks of 256, 256, 256, 232
@@ -243,7 +245,8 @@ def test_half_tile_resolution(so):
         assert pick(1, 4096, 4096, 4096)[0] == 3
         assert pick(1, 300, 512, 4096)[0] == 3
         assert pick(1, 512, 512, 96)[0] == 3
-        assert pick(1, 512, 516, 96)[0] == 0       # N not a multiple of 8
+        assert pick(1, 512, 516, 96)[0] == 0       # N not a multiple of 8, packing not worth it
+        assert pick(1, 1024, 1028, 1024)[0] == 3   # N not a multiple of 8: B packed
         assert lib.gemm_debug_force_tile(1, 4) == lib.STATUS_SUCCESS
         assert pick(1, 128, 256, 64)[0] == 4
         assert pick(1, 128, 128, 64)[0] == 4
@@ -258,7 +261,8 @@ def test_half_tile_resolution(so):
         assert pick(1, 4096, 5120, 128, cus=128)[0] == 7   # 2 rounds + 128 half tiles
         assert pick(1, 4096, 5120, 128, cus=64)[0] == 6    # the tail would need 2 rounds
         assert pick(1, 300, 5120, 128)[0] == 6     # ragged M: no split, the eight-wave tile
-        assert pick(1, 300, 5124, 128)[0] == 0
+        assert pick(1, 300, 5124, 128)[0] == 6     # N not a multiple of 8: B packed
+        assert pick(1, 64, 5124, 32)[0] == 0       # packing costs more than it saves
     finally:
         lib.gemm_debug_force_tile(1, -1)
 

@@ -72,7 +72,11 @@ def check(fmt, M, N, K, alpha, act, seed, label, with_bias=True, lda=None, ldb=N
 def test_ragged_shapes(fmt, tile, shape, forced):
     assert lib.gemm_debug_force_tile(1, tile) == lib.STATUS_SUCCESS
     M, N, K = shape
-    assert lib.gemm_debug_pick_config(1, M, N, K, 256) == (tile, 1)
+    # the configuration for packed operands (lda = K): with K % 8 != 0 the rows of A
+    # are packed first when that pays, else tile 0 runs; with lda padded to a
+    # multiple of 8, as here, the direct-to-LDS tile runs for every shape
+    t, s = lib.gemm_debug_pick_config(1, M, N, K, 256)
+    assert (t, s) == (tile, 1) or (K % 8 != 0 and t == 0)
     check(fmt, M, N, K, 1.25, lib.ACT_GELU_TANH, seed=1100 + tile + M + K, label="tile %d" % tile)
 
 
@@ -120,11 +124,16 @@ def test_guard_bands_untouched(tile, forced):
     assert err <= FP16_TOL, (err, where)
 
 
-def test_misaligned_operands_resolve_to_register_staged(forced):
+def test_misaligned_operands_are_packed(forced):
+    """N not a multiple of 8, or lda not a multiple of 8: the operand is copied into the
+    library's pack buffer with 16-byte rows and the direct-to-LDS tile reads the copy."""
     assert lib.gemm_debug_force_tile(1, 6) == lib.STATUS_SUCCESS
-    assert lib.gemm_debug_pick_config(1, 300, 260, 100, 256) == (0, 1)   # N % 8 != 0
-    check("f16", 300, 260, 100, 1.0, lib.ACT_GELU_TANH, seed=1161, label="N = 260")
-    check("f16", 300, 256, 100, 1.0, lib.ACT_GELU_TANH, seed=1162, label="lda = 100", lda=100)
+    assert lib.gemm_debug_pick_config(1, 600, 1028, 1000, 256) == (6, 1)
+    check("f16", 600, 1028, 1000, 1.0, lib.ACT_GELU_TANH, seed=1161, label="N = 1028")
+    check("f16", 600, 1024, 1000, 1.0, lib.ACT_GELU_TANH, seed=1162, label="lda = 1004", lda=1004)
+    # too small for the copy to pay: the register-staged tile runs on the operands as given
+    assert lib.gemm_debug_pick_config(1, 300, 260, 100, 256) == (0, 1)
+    check("f16", 300, 260, 100, 1.0, lib.ACT_GELU_TANH, seed=1163, label="N = 260, not packed")
 
 
 @pytest.mark.parametrize("fmt", list(FMTS))

@@ -1,0 +1,159 @@
+"""Operand packing on the GPU through the C ABI, against the CPU oracle.
+
+The direct-to-LDS kernels copy 16-byte chunks, so they need rows of A and B on
+16-byte boundaries and B readable in whole chunks up to N.  When an operand falls
+short (a leading dimension or N not a multiple of 4 floats / 8 halves, or a base
+address off a 16-byte boundary) and a direct-to-LDS tile is chosen, the call
+first copies that operand into the library's pack buffer with padded rows (zeros
+beyond the matrix) and the product reads the copy.  Same bars as the other
+parity tests; the caller's A, B and everything outside C's window are unchanged.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_algebra_sgemm_amd as lib
+import oracle
+from linear_algebra_sgemm_amd import inputs
+from tests.gpu_helpers import (FP16_TOL, FP32_TOL, f16_bits, hgemm_error, note, run_hgemm,
+                               run_sgemm, sgemm_error)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def library():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lib.gemm_create()
+    yield
+    for op in (0, 1):
+        lib.gemm_debug_force_tile(op, -1)
+        lib.gemm_debug_force_splits(op, -1)
+    torch.cuda.synchronize()
+    lib.gemm_destroy()
+
+
+@pytest.fixture
+def forced():
+    yield
+    for op in (0, 1):
+        lib.gemm_debug_force_tile(op, -1)
+        lib.gemm_debug_force_splits(op, -1)
+
+
+def force(op, tile, splits=-1):
+    assert lib.gemm_debug_force_tile(op, tile) == lib.STATUS_SUCCESS
+    assert lib.gemm_debug_force_splits(op, splits) == lib.STATUS_SUCCESS
+
+
+@pytest.mark.parametrize("tile", [7, 8, 9])
+@pytest.mark.parametrize("shape", [(400, 1026, 777), (600, 1026, 1001), (257, 1000, 1111),
+                                   (64, 2048, 2049)])
+def test_sgemm_packed_operands(tile, shape, forced):
+    force(0, tile, 1)
+    M, N, K = shape
+    assert lib.gemm_debug_pick_config(0, M, N, K, 256) == (tile, 1), "packing expected"
+    A, B, C = inputs.sgemm_inputs(M, N, K, 1200 + tile + M)
+    A0, B0 = A.clone(), B.clone()
+    note("sgemm packed tile %d M=%d N=%d K=%d" % (tile, M, N, K))
+    dA, dB, dC = A.cuda(), B.cuda(), C.cuda()
+    lib.sgemm(M, N, K, 1.25, dA, K, dB, N, -0.5, dC, N)
+    torch.cuda.synchronize()
+    err, where = sgemm_error(M, N, K, 1.25, A, K, B, N, -0.5, C, N, dC)
+    assert err <= FP32_TOL, (err, where)
+    assert torch.equal(dA.cpu(), A0) and torch.equal(dB.cpu(), B0), "operands must stay unchanged"
+
+
+def test_sgemm_workload_ragged_packs_a():
+    """1000 x 3000 x 777: lda = 777 keeps rows of A off 16-byte boundaries."""
+    w = inputs.WORKLOADS["sgemm_ragged"]
+    A, B, C = inputs.workload_inputs(w)
+    note("sgemm ragged workload")
+    got = run_sgemm(w.M, w.N, w.K, w.alpha, A, w.K, B, w.N, w.beta, C, w.N)
+    err, where = sgemm_error(w.M, w.N, w.K, w.alpha, A, w.K, B, w.N, w.beta, C, w.N, got)
+    assert err <= FP32_TOL, (err, where)
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+def test_sgemm_packed_with_split(splits, forced):
+    """Packing and split-K in one call: partials in the workspace, copies in the pack buffer."""
+    force(0, 9, splits)
+    M, N, K = 300, 264, 3999
+    assert lib.gemm_debug_pick_config(0, M, N, K, 256)[0] == 9, "packing expected"
+    A, B, C = inputs.sgemm_inputs(M, N, K, 1231 + splits)
+    note("sgemm packed + split x%d" % splits)
+    got = run_sgemm(M, N, K, 1.0, A, K, B, N, 0.25, C, N)
+    err, where = sgemm_error(M, N, K, 1.0, A, K, B, N, 0.25, C, N, got)
+    assert err <= FP32_TOL, (err, where)
+
+
+@pytest.mark.parametrize("tile", [7, 9])
+def test_sgemm_unaligned_bases(tile, forced):
+    """Bases 4 bytes past a 16-byte boundary, leading dimensions multiples of 4."""
+    force(0, tile, 1)
+    M, N, K = 512, 512, 1024
+    A, B, C = inputs.sgemm_inputs(M, N, K, 1241 + tile)
+    bufA = torch.zeros(M * K + 1)
+    bufA[1:] = A.reshape(-1)
+    bufB = torch.zeros(K * N + 1)
+    bufB[1:] = B.reshape(-1)
+    dA, dB, dC = bufA.cuda(), bufB.cuda(), C.cuda()
+    note("sgemm packed unaligned bases tile %d" % tile)
+    lib.sgemm(M, N, K, 1.0, dA.data_ptr() + 4, K, dB.data_ptr() + 4, N, -1.0, dC, N)
+    torch.cuda.synchronize()
+    err, where = sgemm_error(M, N, K, 1.0, A, K, B, N, -1.0, C, N, dC)
+    assert err <= FP32_TOL, (err, where)
+
+
+def test_packed_calls_on_two_streams_take_turns(forced):
+    """Calls that pack, on two streams, share the pack buffer; the library orders them."""
+    force(0, 9, 1)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    cases = []
+    for i in range(6):
+        M, N, K = 512 + 64 * i, 1026 + 4 * (i % 3), 1001 + 100 * i
+        assert lib.gemm_debug_pick_config(0, M, N, K, 256)[0] == 9, "packing expected"
+        A, B, C = inputs.sgemm_inputs(M, N, K, 1251 + i)
+        cases.append((M, N, K, A, B, C, A.cuda(), B.cuda(), C.cuda()))
+    torch.cuda.synchronize()
+    note("sgemm packed calls on two streams")
+    for i, (M, N, K, A, B, C, dA, dB, dC) in enumerate(cases):
+        lib.sgemm(M, N, K, 1.0, dA, K, dB, N, 1.0, dC, N, stream=(s1, s2)[i % 2])
+    torch.cuda.synchronize()
+    for (M, N, K, A, B, C, dA, dB, dC) in cases:
+        err, where = sgemm_error(M, N, K, 1.0, A, K, B, N, 1.0, C, N, dC)
+        assert err <= FP32_TOL, (M, N, K, err, where)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("tile", [3, 4, 6])
+@pytest.mark.parametrize("shape", [(520, 1028, 777), (300, 2060, 1001), (257, 1000, 1777)])
+def test_half_packed_operands(fmt, tile, shape, forced):
+    force(1, tile)
+    M, N, K = shape
+    assert lib.gemm_debug_pick_config(1, M, N, K, 256) == (tile, 1), "packing expected"
+    A, B, bias = inputs.hgemm_inputs(M, N, K, 1300 + tile + M, fmt=fmt)
+    dt = torch.bfloat16 if fmt == "bf16" else torch.float16
+    C = torch.full((M, N), float("nan"), dtype=dt)
+    note("half packed %s tile %d M=%d N=%d K=%d" % (fmt, tile, M, N, K))
+    got = run_hgemm(M, N, K, 1.0, A, K, B, N, bias, lib.ACT_GELU_TANH, C, N)
+    err, where = hgemm_error(M, N, K, 1.0, A, K, B, N, bias, lib.ACT_GELU_TANH, got, N)
+    assert err <= FP16_TOL, (err, where)
+
+
+def test_half_ffn_shape_with_odd_k_sampled():
+    """4096 x 14336 x 4095: rows of A (lda = 4095) packed, then the eight-wave tile."""
+    M, N, K = 4096, 14336, 4095
+    assert lib.gemm_debug_pick_config(1, M, N, K, torch.cuda.get_device_properties(
+        0).multi_processor_count) == (6, 1)
+    A, B, bias = inputs.hgemm_inputs(M, N, K, 1321)
+    C = torch.empty((M, N), dtype=torch.float16)
+    note("half packed ffn shape K = 4095")
+    got = run_hgemm(M, N, K, 1.0, A, K, B, N, bias, lib.ACT_GELU_TANH, C, N).cpu().float()
+    assert torch.isfinite(got).all()
+    rows, cols = inputs.sample_indices(M, N, 2048, K)
+    ref, den = oracle.hgemm_entries(K, 1.0, f16_bits(A), K, f16_bits(B), N, bias.numpy(),
+                                    oracle.ACT_GELU_TANH, rows, cols)
+    e = oracle.normalized_error(got.numpy()[rows, cols], ref, den)
+    assert float(e.max()) <= FP16_TOL, "max normalised error %.3g" % e.max()

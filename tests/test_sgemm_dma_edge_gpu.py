@@ -76,9 +76,11 @@ def lda_for(K):
 def test_ragged_shapes(tile, shape, forced):
     force(tile)
     M, N, K = shape
-    # the configuration for packed operands; with lda padded to a multiple of 4 the
-    # direct-to-LDS tile runs for every shape here
-    assert lib.gemm_debug_pick_config(0, M, N, K, 256) == ((tile, 1) if K % 4 == 0 else (4, 1))
+    # the configuration for packed operands (lda = K): with K % 4 != 0 the rows of A
+    # are packed first when that pays, else tile 4 runs; with lda padded to a
+    # multiple of 4, as here, the direct-to-LDS tile runs for every shape
+    t, s = lib.gemm_debug_pick_config(0, M, N, K, 256)
+    assert (t, s) == (tile, 1) or (K % 4 != 0 and t == 4)
     check(M, N, K, 1.25, -0.5, seed=900 + tile + M + K, label="tile %d" % tile, lda=lda_for(K))
 
 
@@ -143,12 +145,16 @@ def test_guard_bands_untouched(tile, forced):
     assert err <= FP32_TOL, (err, where)
 
 
-def test_unaligned_operands_resolve_to_register_staged(forced):
-    """N not a multiple of 4, or lda not a multiple of 4: tile 4 runs instead, same result."""
+def test_unaligned_operands_are_packed(forced):
+    """N not a multiple of 4, or lda not a multiple of 4: the operand is copied into the
+    library's pack buffer with 16-byte rows and the direct-to-LDS tile reads the copy."""
     force(9)
+    assert lib.gemm_debug_pick_config(0, 600, 1026, 1000, 256) == (9, 1)
+    check(600, 1026, 1000, 1.0, 0.5, seed=971, label="N = 1026")
+    check(600, 1024, 1001, 1.0, 0.5, seed=972, label="lda = 1001")
+    # too small for the copy to pay: the register-staged tile runs on the operands as given
     assert lib.gemm_debug_pick_config(0, 300, 258, 100, 256) == (4, 1)
-    check(300, 258, 100, 1.0, 0.5, seed=971, label="N = 258")
-    check(300, 256, 101, 1.0, 0.5, seed=972, label="lda = 101")
+    check(300, 258, 100, 1.0, 0.5, seed=973, label="N = 258, not packed")
 
 
 @pytest.mark.parametrize("shape,want", [((4000, 4000, 4008), (9, 1)), ((6000, 6000, 6000), (8, 1)),
