@@ -76,41 +76,51 @@ long round_use(long tiles, int cus, int per_cu) {
 //    when that wastes less of the last round (6000^3: 116 vs 104; 7000 x 3000 x
 //    2000: 109 vs 89) — weighed by their full-round rates, 89 vs 93 % of peak.
 //    On a ragged shape K must reach 384 (5000 x 5000 x 333: 64 vs 74 for 64x64).
+//  * Fewer 256x256 tiles than CUs: the 128x128 direct-to-LDS tile, unsplit
+//    once its tiles give every CU one and use at least 75 % of the last round
+//    of slots, two per CU (2048^3: 130 vs 114 for the split 256x256 tile;
+//    4096 x 2048 x 2048: 139 vs 125 for register-staged 128x128; 2800^3: 128 vs
+//    124; but 1536 x 3072 x 2048, 288 tiles in 512 slots: 80 vs 108 for 64x64),
+//    else with K split so that one round uses at least 70 % of the CUs, in two
+//    or more chunks of at least 384 (1024 x 1024 x 8192: 123 vs 117 for the
+//    256x256 tile in 16 chunks; 1024 x 2048 x 4096: 121 vs 116), as long as
+//    there are 32 tiles (512 x 512 x 8192 keeps 64x64 in 16 chunks: 82 vs 59).
 //  * Else the register-staged 128x256 tile at two per CU, then 128x128, where
 //    their tiles give every CU two (4096^3: 134 vs 130 for 256x256) — on shapes
 //    the direct-to-LDS kernel takes, only where they are whole (their
 //    bounds-checked form is slow: 3000^3 at 128x128: 77).
-//  * Else the 256x256 direct-to-LDS tile with K split so that one round uses at
-//    least 70 % of the CUs (2048^3: 114, 1024 x 1024 x 8192: 116 vs 81; ragged
-//    2500^3: 99 vs 90, 4000 x 2000 x 3000: 128 vs 105), or unsplit when its
-//    tiles alone fill 70 % (3500^3: 106 vs 104).
-//  * Else 64x64 tiles, which spread small outputs over more CUs (3000^3: 101 vs
-//    78 for 256x256 at 144 tiles; 1000x3000x777: 63 vs 50 for 128x128).
+//  * Else 64x64 tiles, which spread small outputs over more CUs (1024 x 3072 x
+//    768: 101 vs 92 for 128x128 direct at 192 tiles; 1000x3000x777: 68 vs 64).
 int sgemm_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_tall = ceil_div(M, 128) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
   const bool direct = operands_ok;
   const bool whole = M % 256 == 0 && N % 256 == 0 && K % 32 == 0;
-  if (direct && t_large >= cus && (whole || K >= 384))
-    return 89 * round_use(t_tall, cus, 2) > 93 * round_use(t_large, cus, 1) ? 8 : 9;
+  if (direct && (whole || K >= 384)) {
+    if (t_large >= cus)
+      return 89 * round_use(t_tall, cus, 2) > 93 * round_use(t_large, cus, 1) ? 8 : 9;
+    if (t_med >= cus) {
+      if (round_use(t_med, cus, 2) >= 75) return 10;
+    } else {
+      const long s = direct_splits(t_med, K, cus);
+      if (t_med >= 32 && s >= 2 && 10 * t_med * s >= 7L * cus) return 10;
+    }
+  }
   // (on shapes the direct-to-LDS kernel can take, only where these tiles are whole)
   if (t_tall >= 2L * cus && (!direct || (M % 128 == 0 && N % 256 == 0 && K % 16 == 0))) return 4;
   if (t_med >= 2L * cus && (!direct || (M % 128 == 0 && N % 128 == 0 && K % 16 == 0))) return 1;
-  if (direct && K >= 384 && t_large < cus) {
-    const long s = direct_splits(t_large, K, cus);
-    if (10 * t_large * s >= 7L * cus) return 9;
-  }
   return 2;
 }
 
-// Built-in split rule: the direct-to-LDS tiles as in direct_splits; for the
+// Built-in split rule: the direct-to-LDS tiles as in direct_splits (the
+// 128x128 one counted at one workgroup per CU, as measured best); for the
 // register-staged tiles (from the size sweep), when the output has fewer tiles
 // than there are CUs and K is at least 512, split K until there are about four
 // workgroups per CU (small tiles share a CU), keeping chunks of at least 128.
 int sgemm_rule_splits(int M, int N, int K, int tile, int cus) {
   const long tiles = ceil_div(M, sgemm_tile_bm(tile)) * ceil_div(N, sgemm_tile_bn(tile));
-  if (tile == 7 || tile == 9) return (int)direct_splits(tiles, K, cus);
+  if (tile == 7 || tile == 9 || tile == 10) return (int)direct_splits(tiles, K, cus);
   if (tile == 8) return (int)direct_splits((tiles + 1) / 2, K, cus);
   if (tiles >= cus || K < 512) return 1;
   const long by_cus = ceil_div(4L * cus, tiles);

@@ -356,9 +356,10 @@ __global__ void __launch_bounds__(256) sgemm_scale_kernel(int M, int N, float be
 //    row r permuted by row64_swizzle(r); one instruction copies 16 whole rows.
 //    A fragment read (chunk 2 g + l / 32 of 32 consecutive rows) is then free
 //    of bank conflicts.
-//  * B: one instruction per row of the tile (BN = 256 floats = 1 KiB), rows
-//    padded to 1056 bytes so that the two k-slots of a B read (rows 4 apart)
-//    fall on different halves of the 64 banks.
+//  * B: one instruction per 1 KiB of rows of the tile (one row of BN = 256
+//    floats, or two of BN = 128), each copy's 1 KiB padded (to 1056 or 1088
+//    bytes) so that the two k-slots of a B read (rows 4 apart) fall on
+//    different halves of the 64 banks.
 // ---------------------------------------------------------------------------
 template <int BM_, int BN_, int STAGES_, int WAVES_PER_SIMD_ = 1, int WAVES_M_ = 2,
           int WAVES_N_ = 2>
@@ -373,16 +374,24 @@ struct SDmaTile {
   static constexpr int BLK = 32;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int A_BYTES = BM * BK * 4;          // 64-byte rows
-  static constexpr int B_ROW = BN * 4 + 32;            // bytes per padded LDS row of B
-  static constexpr int B_BYTES = BK * B_ROW;
+  static constexpr int B_RPC = 1024 / (BN * 4);        // rows of B per copy
+  // Bytes per copy slot of B: rows r and r + 4 lie 4 / B_RPC slots apart, and
+  // (4 / B_RPC) * B_SLOT = 128 (mod 256) puts them on opposite halves of the banks.
+  static constexpr int B_SLOT = 1024 + 32 * B_RPC;
+  static constexpr int B_BYTES = (BK / B_RPC) * B_SLOT;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int A_INSTR = A_BYTES / 1024;       // 16 rows per copy
-  static constexpr int B_INSTR = BK;                   // one row per copy
+  static constexpr int B_INSTR = BK / B_RPC;
   static constexpr int A_PER_WAVE = A_INSTR / WAVES;
   static constexpr int B_PER_WAVE = B_INSTR / WAVES;
   static constexpr int LOADS_PER_TILE = A_PER_WAVE + B_PER_WAVE;
+  // Byte offset of row r (0 .. BK - 1) of B inside the stage's B region.
+  static __device__ __forceinline__ int b_row(int r) {
+    return (r / B_RPC) * B_SLOT + (r % B_RPC) * (BN * 4);
+  }
 
-  static_assert(BN * 4 == 1024, "one copy instruction per row of the B tile");
+  static_assert(BN * 4 == 1024 || BN * 4 == 512, "one or two rows of B per copy instruction");
+  static_assert(((4 / B_RPC) * B_SLOT) % 256 == 128, "k-slots of a B read on opposite bank halves");
   static_assert(A_INSTR % WAVES == 0 && B_INSTR % WAVES == 0, "copies split evenly over waves");
   static_assert(STAGE_BYTES % 16 == 0, "stages start on 16-byte boundaries");
   static_assert(STAGES >= 3 && STAGES * STAGE_BYTES * WG_PER_CU <= 160 * 1024,
@@ -410,15 +419,17 @@ struct SDmaPlan {
         const int rc = m0 + r < p.M ? r : p.M - 1 - m0;
         off[v] = (uint32_t)(((size_t)rc * p.lda + 4 * chunk) * 4);
       } else {
-        const int kr = wave * T::B_PER_WAVE + (v - T::A_PER_WAVE);
-        const int cc = n0 + 4 * lane < p.nb ? 4 * lane : p.nb - 4 - n0;
+        const int copy = wave * T::B_PER_WAVE + (v - T::A_PER_WAVE);
+        const int kr = copy * T::B_RPC + lane / (T::BN / 4);
+        const int c4 = 4 * (lane % (T::BN / 4));
+        const int cc = n0 + c4 < p.nb ? c4 : p.nb - 4 - n0;
         off[v] = (uint32_t)(((size_t)kr * p.ldb + cc) * 4);
       }
     }
   }
   static __device__ __forceinline__ uint32_t slot(int v, int wave) {
     if (v < T::A_PER_WAVE) return (wave * T::A_PER_WAVE + v) * 1024;
-    return T::A_BYTES + (wave * T::B_PER_WAVE + (v - T::A_PER_WAVE)) * T::B_ROW;
+    return T::A_BYTES + (wave * T::B_PER_WAVE + (v - T::A_PER_WAVE)) * T::B_SLOT;
   }
 };
 
@@ -454,7 +465,7 @@ __device__ __forceinline__ void sload_frags(SFrags<T>& f, const uint8_t* stage, 
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int j = 0; j < T::FN; ++j)
-      f.b[s][j] = *reinterpret_cast<const float*>(bs + (8 * g + 4 * h + s) * T::B_ROW +
+      f.b[s][j] = *reinterpret_cast<const float*>(bs + T::b_row(8 * g + 4 * h + s) +
                                                   4 * (wn * T::WTN + j * 32 + l32));
 }
 
@@ -569,7 +580,7 @@ __device__ __forceinline__ void sdma_k_tail(const SgemmArgs& p, f32x16 (&acc)[T:
     const int col = n0 + cc < p.nb ? n0 + cc : p.nb - 4;
     f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
     if (k < p.K) v = *reinterpret_cast<const f32x4*>(p.B + (size_t)k * p.ldb + col);
-    *reinterpret_cast<f32x4*>(lds + t * T::STAGE_BYTES + T::A_BYTES + (kr % 16) * T::B_ROW +
+    *reinterpret_cast<f32x4*>(lds + t * T::STAGE_BYTES + T::A_BYTES + T::b_row(kr % 16) +
                               4 * cc) = v;
   }
   lds_barrier();
@@ -716,6 +727,9 @@ using SDmaLarge = SDmaTile<256, 256, 4, 1>;
 using SDmaTall = SDmaTile<128, 256, 3, 2>;
 // 256 x 256 with eight waves (2 x 4, each 128 x 64), two per SIMD.
 using SDmaEight = SDmaTile<256, 256, 4, 2, 2, 4>;
+// 128 x 128 with four waves of 64 x 64, 4 stages of 16.5 KiB, two workgroups per CU:
+// outputs with too few 256 x 256 tiles to fill the CUs.
+using SDmaSmall = SDmaTile<128, 128, 4, 2, 2, 2>;
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -729,7 +743,8 @@ static_assert(TileLarge::BK == sgemm_tile_bk(0) && TileMedium::BK == sgemm_tile_
                   SDmaLarge::BM == sgemm_tile_bm(7) && SDmaLarge::BN == sgemm_tile_bn(7) &&
                   SDmaTall::BM == sgemm_tile_bm(8) && SDmaTall::BN == sgemm_tile_bn(8) &&
                   SDmaEight::BM == sgemm_tile_bm(9) && SDmaEight::BN == sgemm_tile_bn(9) &&
-                  2 * SDmaEight::BK == sgemm_tile_bk(9),
+                  2 * SDmaEight::BK == sgemm_tile_bk(9) && SDmaSmall::BM == sgemm_tile_bm(10) &&
+                  SDmaSmall::BN == sgemm_tile_bn(10) && 2 * SDmaSmall::BK == sgemm_tile_bk(10),
               "the host-side planner's K steps must match the tiles");
 
 static hipError_t launch_reduce(const SgemmCall& c, int splits, const float* ws, hipStream_t s) {
@@ -857,6 +872,7 @@ hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hi
     case 7: return launch_sdma<SDmaLarge>(c, plan, 4, ws, s);
     case 8: return launch_sdma<SDmaTall>(c, plan, 8, ws, s);
     case 9: return launch_sdma<SDmaEight>(c, plan, 4, ws, s);
+    case 10: return launch_sdma<SDmaSmall>(c, plan, 8, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -157,12 +157,15 @@ def test_config_rule(so):
         (0, 256, 256, 1024, 256, (2, 8)),     # 16 tiles; chunks of 128
         (0, 512, 512, 512, 256, (2, 4)),      # 64 tiles; chunks of 128
         (0, 1000, 3000, 777, 256, (2, 1)),    # 752 tiles
-        (0, 2048, 2048, 2048, 256, (9, 4)),   # 64 whole tiles: direct-to-LDS, 4 chunks of 512
-        (0, 2048, 2048, 8192, 256, (9, 4)),
-        (0, 1024, 2048, 4096, 256, (9, 8)),   # 32 whole tiles, 8 chunks of 512
-        (0, 1024, 1024, 4096, 256, (2, 1)),   # 16 whole tiles would need chunks under 512
-        (0, 1024, 1024, 8192, 256, (9, 16)),  # 16 whole tiles, 16 chunks of 512
-        (0, 2048, 4096, 1024, 256, (1, 1)),   # 512 tiles of 128x128 before a split
+        (0, 2048, 2048, 2048, 256, (10, 1)),  # 64 tiles of 256x256, 256 of 128x128: direct 128x128
+        (0, 2048, 2048, 8192, 256, (10, 1)),
+        (0, 1024, 2048, 4096, 256, (10, 2)),  # 128 tiles of 128x128, 2 chunks of 2048
+        (0, 1024, 1024, 4096, 256, (10, 4)),  # 64 tiles, 4 chunks of 1024
+        (0, 1024, 1024, 8192, 256, (10, 4)),
+        (0, 2048, 4096, 1024, 256, (10, 1)),  # 512 tiles of 128x128
+        (0, 512, 512, 8192, 256, (2, 16)),    # 16 tiles of 128x128 only: split 64x64
+        (0, 1024, 3072, 768, 256, (2, 1)),    # 192 tiles of 128x128 would need a split of 1
+        (0, 1536, 3072, 2048, 256, (2, 1)),   # 288 tiles of 128x128 fill 56 % of 512 slots
         (0, 4096, 4096, 4096, 64, (9, 1)),
         (0, 128, 128, 16384, 256, (2, 32)),   # 4 tiles; 256 chunks by CUs, capped at 32
         (1, 4096, 14336, 4096, 256, (7, 1)),  # whole 256-tiles, long K: eight waves + tail split
@@ -297,13 +300,13 @@ def test_split_legality(so):
             M, N = rng.randint(1, 3000), rng.randint(1, 3000)
             K = rng.choice([1, 15, 16, 17, 100, 777, 4096, 20000])
             want = rng.choice([1, 2, 3, 5, 8, 16, 32])
-            tile = rng.choice([-1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
+            tile = rng.choice([-1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
             assert lib.gemm_debug_force_tile(0, tile) == lib.STATUS_SUCCESS
             assert lib.gemm_debug_force_splits(0, want) == lib.STATUS_SUCCESS
             t, s = pick(0, M, N, K)
             if tile >= 0:
                 # direct-to-LDS tiles (7, 8) run as 0 / 4 unless the shape is whole and unsplit
-                assert t == tile or (tile, t) in ((7, 4), (8, 4), (9, 4))
+                assert t == tile or (tile, t) in ((7, 4), (8, 4), (9, 4), (10, 4))
                 if t != tile:
                     assert s > 1 or M % (128 if tile == 8 else 256) or N % 256 or K % 32
             # the chunks are planned in the K granularity of the tile asked for (the
@@ -354,7 +357,7 @@ def test_forced_splits(so):
 
 
 def test_force_tile_values(so):
-    assert lib.gemm_debug_force_tile(0, 10) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(0, 11) == lib.STATUS_INVALID_VALUE
     assert lib.gemm_debug_force_tile(0, 9) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(1, 8) == lib.STATUS_INVALID_VALUE
     assert lib.gemm_debug_force_tile(1, 7) == lib.STATUS_SUCCESS
@@ -364,3 +367,16 @@ def test_force_tile_values(so):
     assert lib.gemm_debug_force_tile(0, 4) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(5, 0) == lib.STATUS_INVALID_VALUE
     assert lib.gemm_debug_force_tile(0, -1) == lib.STATUS_SUCCESS
+
+
+def test_tuner_covers_every_tile(so):
+    """The tuner times (and names in its report) exactly the tile configurations the
+    library accepts."""
+    from linear_algebra_sgemm_amd import tune
+    try:
+        for op, tiles in ((0, tune.SGEMM_TILES), (1, tune.HALF_TILES)):
+            valid = {t for t in range(32) if lib.gemm_debug_force_tile(op, t) == lib.STATUS_SUCCESS}
+            assert valid == set(tiles) == set(tune.TILE_NAMES[op]), (op, valid, tiles)
+    finally:
+        lib.gemm_debug_force_tile(0, -1)
+        lib.gemm_debug_force_tile(1, -1)

@@ -1,7 +1,7 @@
 """The FP32 direct-to-LDS kernels on ragged shapes, on the GPU through the C ABI,
 against the CPU oracle.
 
-Tiles 7, 8 and 9 copy 16-byte chunks of A and B straight into LDS.  When M or N
+Tiles 7, 8, 9 and 10 copy 16-byte chunks of A and B straight into LDS.  When M or N
 is not a multiple of the tile, or K not a multiple of 32, they run a
 bounds-checked instantiation: copies of rows past M - 1 (columns past N - 4)
 repeat the last row (chunk) inside the matrix, the last K % 32 values of k go
@@ -20,7 +20,7 @@ from tests.gpu_helpers import FP32_TOL, note, run_sgemm, sgemm_error
 
 pytestmark = pytest.mark.gpu
 
-DMA_TILES = (7, 8, 9)
+DMA_TILES = (7, 8, 9, 10)
 # (M, N, K): ragged M and N, K below 32, K % 32 in 1..31, K a multiple of 32 on ragged M / N,
 # tiles smaller than one block, several tiles with a ragged last row and column
 SHAPES = [(300, 520, 100), (257, 260, 33), (64, 64, 16), (1, 4, 1), (129, 132, 31),
@@ -158,8 +158,8 @@ def test_unaligned_operands_are_packed(forced):
 
 
 @pytest.mark.parametrize("shape,want", [((4000, 4000, 4008), (9, 1)), ((6000, 6000, 6000), (8, 1)),
-                                        ((2800, 2800, 2800), (9, 2)),
-                                        ((4000, 2000, 3000), (9, 2))])
+                                        ((2800, 2800, 2800), (10, 1)),
+                                        ((4000, 2000, 3000), (10, 1)), ((3000, 3000, 3000), (10, 1))])
 def test_auto_choice_large_ragged(shape, want):
     """Full-size ragged products on the configuration the library picks, checked on
     sampled outputs (the four corners, the last row and column, and uniform picks)."""
