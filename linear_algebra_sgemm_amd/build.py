@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgemm.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["gemm_capi.cpp", "gemm_config.cpp", "sgemm_kernels.hip", "hgemm_kernels.hip"]
+SOURCES = ["gemm_capi.cpp", "gemm_config.cpp", "sgemm_kernels.hip", "hgemm_kernels.hip",
+           "pack_kernels.hip"]
 ARCH = "gfx950"
 
 DEVICE_FLAGS = [

@@ -100,6 +100,11 @@ struct Packing {
   bool a = false, b = false;
   int lda = 0, ldb = 0;    // leading dimensions of the copies (elements)
   size_t b_offset = 0;     // byte offset of B's copy in the buffer
+  // Padded copies (register-staged FP32 tiles on ragged shapes): A copied to
+  // `rows_a` rows and B to `k` rows, both zero-filled past the product, so the
+  // kernel loads without bounds checks over K' = `k`.
+  bool padded = false;
+  int rows_a = 0, k = 0;
 };
 
 bool plan_packing(int M, int N, int K, bool a_ok, bool b_ok, size_t elem, size_t cap_bytes,
@@ -115,6 +120,75 @@ bool plan_packing(int M, int N, int K, bool a_ok, bool b_ok, size_t elem, size_t
   const double flops = 2.0 * M * N * K;
   return a_bytes + b_bytes <= cap_bytes && flops >= (double)(1 << 28) &&
          flops >= 64.0 * 2.0 * (double)(a_bytes + b_bytes);
+}
+
+// Padded copies for a register-staged FP32 tile that would otherwise run its
+// bounds-checked instantiation (M, N or K off the tile, or rows of A or B off
+// 16-byte boundaries): A to ceil(M / BM) BM rows of K' = ceil(K / BK) BK
+// columns, B to K' rows of ceil(N / BN) BN columns.  Extra zeros add exact
+// zeros to every sum.  Same cost test as the plain copies, on the padded bytes.
+bool plan_padding(int M, int N, int K, int tile, bool operands_aligned, size_t cap_bytes,
+                  Packing& pk) {
+  if (tile < 0 || tile > 6) return false;
+  const int bm = lasg::sgemm_tile_bm(tile), bn = lasg::sgemm_tile_bn(tile);
+  const int bk = lasg::sgemm_tile_bk(tile);
+  if (operands_aligned && M % bm == 0 && N % bn == 0 && K % bk == 0) return false;
+  Packing q;
+  q.a = q.b = q.padded = true;
+  q.rows_a = (int)round_up((size_t)M, bm);
+  q.k = (int)round_up((size_t)K, bk);
+  q.lda = q.k;
+  q.ldb = (int)round_up((size_t)N, bn);
+  const size_t a_bytes = round_up((size_t)q.rows_a * q.lda * 4, 256);
+  const size_t b_bytes = (size_t)q.k * q.ldb * 4;
+  q.b_offset = a_bytes;
+  const double flops = 2.0 * M * N * K;
+  if (!(a_bytes + b_bytes <= cap_bytes && flops >= (double)(1 << 28) &&
+        flops >= 64.0 * 2.0 * (double)(a_bytes + b_bytes)))
+    return false;
+  pk = q;
+  return true;
+}
+
+// Makes the copies `pk` asks for (elements of `elem` bytes) in the pack buffer,
+// in one launch, and points the operands (`a` / `lda`, `b` / `ldb`, holding the
+// caller's on entry) at them.
+hipError_t pack_operands(const Packing& pk, int M, int N, int K, int elem, void* pbuf,
+                         hipStream_t s, const void*& a, int& lda, const void*& b, int& ldb) {
+  lasg::PackJob jobs[2];
+  int n = 0;
+  if (pk.a) {
+    lasg::PackJob& j = jobs[n++];
+    j.src = a;
+    j.rows = M;
+    j.cols = K;
+    j.lds = lda;
+    j.dst = pbuf;
+    j.dst_rows = pk.padded ? pk.rows_a : M;
+    j.ldd = pk.lda;
+  }
+  if (pk.b) {
+    lasg::PackJob& j = jobs[n++];
+    j.src = b;
+    j.rows = K;
+    j.cols = N;
+    j.lds = ldb;
+    j.dst = static_cast<char*>(pbuf) + pk.b_offset;
+    j.dst_rows = pk.padded ? pk.k : K;
+    j.ldd = pk.ldb;
+  }
+  if (n == 0) return hipSuccess;
+  const hipError_t e = lasg::launch_pack(jobs, n, elem, s);
+  if (e != hipSuccess) return e;
+  if (pk.a) {
+    a = jobs[0].dst;
+    lda = pk.lda;
+  }
+  if (pk.b) {
+    b = jobs[n - 1].dst;
+    ldb = pk.ldb;
+  }
+  return hipSuccess;
 }
 
 // Direct-to-LDS operand conditions of the FP32 product (rows 16-byte aligned,
@@ -138,7 +212,10 @@ lasg::SgemmPlan decide_sgemm(int M, int N, int K, bool a_ok, bool b_ok, int cus,
                              size_t pack_bytes, Packing& pk, bool& pack) {
   const int ft = g_force_sgemm_tile.load(), fs = g_force_sgemm_splits.load();
   pack = !(a_ok && b_ok) && plan_packing(M, N, K, a_ok, b_ok, 4, pack_bytes, pk);
-  return lasg::plan_sgemm(M, N, K, cus, ft, fs, ws_floats, pack || (a_ok && b_ok));
+  const lasg::SgemmPlan plan =
+      lasg::plan_sgemm(M, N, K, cus, ft, fs, ws_floats, pack || (a_ok && b_ok));
+  if (plan_padding(M, N, K, plan.tile, a_ok && b_ok, pack_bytes, pk)) pack = true;
+  return plan;
 }
 
 lasg::HalfPlan decide_half(int M, int N, int K, bool a_ok, bool b_ok, int cus, size_t ws_floats,
@@ -252,20 +329,17 @@ int sgemm(int M, int N, int K, float alpha, const float* A, int lda, const float
     if (plan.splits > 1 || pack) {
       return with_workspace(stream, [&](float* ws, void* pbuf) {
         lasg::SgemmCall cc = c;
-        if (pack && pk.a) {
-          float* a = static_cast<float*>(pbuf);
-          const hipError_t pe = lasg::launch_pack_f32(A, M, K, lda, a, pk.lda, stream);
+        if (pack) {
+          const void *a = A, *b = B;
+          const hipError_t pe = pack_operands(pk, M, N, K, 4, pbuf, stream, a, cc.lda, b, cc.ldb);
           if (pe != hipSuccess) return pe;
-          cc.A = a;
-          cc.lda = pk.lda;
-        }
-        if (pack && pk.b) {
-          float* b = reinterpret_cast<float*>(static_cast<char*>(pbuf) + pk.b_offset);
-          const hipError_t pe = lasg::launch_pack_f32(B, K, N, ldb, b, pk.ldb, stream);
-          if (pe != hipSuccess) return pe;
-          cc.B = b;
-          cc.ldb = pk.ldb;
-          cc.nb = pk.ldb;
+          cc.A = static_cast<const float*>(a);
+          cc.B = static_cast<const float*>(b);
+          if (pk.b) cc.nb = pk.ldb;
+          if (pk.padded) {
+            cc.K = pk.k;
+            cc.padded = true;
+          }
         }
         return lasg::launch_sgemm(cc, plan, ws, stream);
       });
@@ -300,20 +374,13 @@ int half_product(bool bf16, int M, int N, int K, float alpha, const uint16_t* A,
                                           g_ws.floats, g_ws.pack_bytes, pk, pack);
   auto launch = [&](float* ws, void* pbuf) {
     lasg::HgemmCall cc = c;
-    if (pack && pk.a) {
-      uint16_t* a = static_cast<uint16_t*>(pbuf);
-      const hipError_t pe = lasg::launch_pack_u16(A, M, K, lda, a, pk.lda, stream);
+    if (pack) {
+      const void *a = A, *b = B;
+      const hipError_t pe = pack_operands(pk, M, N, K, 2, pbuf, stream, a, cc.lda, b, cc.ldb);
       if (pe != hipSuccess) return pe;
-      cc.A = a;
-      cc.lda = pk.lda;
-    }
-    if (pack && pk.b) {
-      uint16_t* b = reinterpret_cast<uint16_t*>(static_cast<char*>(pbuf) + pk.b_offset);
-      const hipError_t pe = lasg::launch_pack_u16(B, K, N, ldb, b, pk.ldb, stream);
-      if (pe != hipSuccess) return pe;
-      cc.B = b;
-      cc.ldb = pk.ldb;
-      cc.nb = pk.ldb;
+      cc.A = static_cast<const uint16_t*>(a);
+      cc.B = static_cast<const uint16_t*>(b);
+      if (pk.b) cc.nb = pk.ldb;
     }
     return bf16 ? lasg::launch_bgemm(cc, plan, cus, ws, stream)
                 : lasg::launch_hgemm(cc, plan, cus, ws, stream);

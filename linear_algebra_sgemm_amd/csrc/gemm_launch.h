@@ -20,6 +20,11 @@ struct SgemmCall {
   // Columns of each row of B that may be read (at least N; more when B is a
   // padded copy); 0 means N.
   int nb = 0;
+  // A and B are copies zero-padded to whole tiles of the configuration that
+  // runs (register-staged tiles): A has ceil(M / BM) BM rows, B ceil(N / BN) BN
+  // columns, and K is a multiple of the tile's K step; only the stores of C are
+  // bounds-checked.
+  bool padded = false;
 };
 
 struct HgemmCall {
@@ -141,12 +146,17 @@ void set_use_tuned(bool on);
 // `ws` holds at least plan.splits * M * N floats when plan.splits > 1.
 hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hipStream_t s);
 hipError_t launch_sgemm_scale(int M, int N, float beta, float* C, int ldc, hipStream_t s);
-// dst (rows x ldd, 16-byte aligned) = src (rows x cols, leading dimension lds)
-// with columns [cols, ldd) zero: the packed copy of an operand.
-hipError_t launch_pack_f32(const float* src, int rows, int cols, int lds, float* dst, int ldd,
-                           hipStream_t s);
-hipError_t launch_pack_u16(const uint16_t* src, int rows, int cols, int lds, uint16_t* dst,
-                           int ldd, hipStream_t s);
+
+// One operand copy (counts in elements): dst (dst_rows x ldd) = src (rows x
+// cols, leading dimension lds) with columns [cols, ldd) and rows [rows,
+// dst_rows) zero.  dst 16-byte aligned, ldd a multiple of 16 bytes.
+struct PackJob {
+  const void* src = nullptr;
+  void* dst = nullptr;
+  int rows = 0, cols = 0, lds = 0, dst_rows = 0, ldd = 0;
+};
+// One or two copies of 4-byte or 2-byte elements in one launch.
+hipError_t launch_pack(const PackJob* jobs, int count, int elem_bytes, hipStream_t s);
 
 // The half-precision product: binary16 (hgemm) or bfloat16 (bgemm) inputs and
 // output, FP32 accumulation; same kernels, tiles and tile choice.

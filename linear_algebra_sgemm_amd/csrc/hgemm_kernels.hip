@@ -1025,28 +1025,4 @@ hipError_t launch_bgemm(const HgemmCall& c, const HalfPlan& plan, int cus, float
   return launch_half<EltBF16>(c, plan, cus, ws, s);
 }
 
-// Packed copy of an operand: dst (rows x ldd) = src (rows x cols, leading
-// dimension lds), columns [cols, ldd) zero.  Plain element copies, HBM-bound.
-__global__ void __launch_bounds__(256) pack_rows_u16_kernel(int rows, int cols,
-                                                            const uint16_t* src, int lds,
-                                                            uint16_t* dst, int ldd) {
-  const int64_t total = (int64_t)rows * ldd;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = t / ldd, c = t % ldd;
-    dst[t] = c < cols ? src[r * lds + c] : (uint16_t)0;
-  }
-}
-
-hipError_t launch_pack_u16(const uint16_t* src, int rows, int cols, int lds, uint16_t* dst,
-                           int ldd, hipStream_t s) {
-  const int64_t total = (int64_t)rows * ldd;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL(pack_rows_u16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, rows, cols,
-                     src, lds, dst, ldd);
-  return hipGetLastError();
-}
-
 }  // namespace lasg

@@ -225,7 +225,9 @@ __device__ __forceinline__ void sgemm_store(const SgemmArgs& p, const ACC& acc, 
   }
 }
 
-template <class T, bool EDGE, bool SPLIT>
+// EDGE: bounds-checked loads and stores; STORE_EDGE alone: operands padded to
+// whole tiles (SgemmCall::padded), loads unchecked, stores of C checked.
+template <class T, bool EDGE, bool SPLIT, bool STORE_EDGE = EDGE>
 __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(T::WAVES_PER_SIMD)))
 sgemm_mfma_kernel(SgemmArgs p) {
   if constexpr (SPLIT) {
@@ -318,14 +320,14 @@ sgemm_mfma_kernel(SgemmArgs p) {
 #pragma unroll
         for (int r = 0; r < MF::ACC; ++r) {
           const int row = m0 + wm * T::WTM + i * T::BLK + MF::row(r, lane);
-          if (EDGE && (row >= p.M || col >= p.N)) continue;
+          if (STORE_EDGE && (row >= p.M || col >= p.N)) continue;
           W[(size_t)row * p.N + col] = acc[i][j][r];
         }
       }
     return;
   }
 
-  sgemm_store<T, EDGE>(p, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
+  sgemm_store<T, STORE_EDGE>(p, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
 }
 
 // C = beta * C (C = 0 when beta == 0, without reading C): the alpha == 0 / K == 0 case.
@@ -771,10 +773,24 @@ static hipError_t launch_tile(const SgemmCall& c, const SgemmPlan& plan, int gro
   p.a_vec = c.lda % 4 == 0 && aligned16(c.A);
   p.b_vec = c.ldb % 4 == 0 && aligned16(c.B);
   p.nb = c.N;
-  const bool edge = !(c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % T::BK == 0 &&
-                      c.lda % 4 == 0 && c.ldb % 4 == 0 && aligned16(c.A) && aligned16(c.B));
   const bool split = plan.splits > 1;
   const dim3 grid(p.tiles_m * p.tiles_n, split ? plan.splits : 1), block(T::THREADS);
+  if (c.padded) {
+    // Copies padded to whole tiles: every load is in range, only C is checked.
+    if (c.K % T::BK != 0 || c.lda % 4 != 0 || c.ldb % 4 != 0 || !aligned16(c.A) ||
+        !aligned16(c.B) || c.ldb < p.tiles_n * T::BN || c.lda < c.K)
+      return hipErrorInvalidValue;
+    if (split) {
+      hipLaunchKernelGGL((sgemm_mfma_kernel<T, false, true, true>), grid, block, 0, s, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_reduce(c, plan.splits, ws, s);
+    }
+    hipLaunchKernelGGL((sgemm_mfma_kernel<T, false, false, true>), grid, block, 0, s, p);
+    return hipGetLastError();
+  }
+  const bool edge = !(c.M % T::BM == 0 && c.N % T::BN == 0 && c.K % T::BK == 0 &&
+                      c.lda % 4 == 0 && c.ldb % 4 == 0 && aligned16(c.A) && aligned16(c.B));
   if (split) {
     if (edge)
       hipLaunchKernelGGL((sgemm_mfma_kernel<T, true, true>), grid, block, 0, s, p);
@@ -883,29 +899,6 @@ hipError_t launch_sgemm_scale(int M, int N, float beta, float* C, int ldc, hipSt
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(sgemm_scale_kernel, dim3((unsigned)blocks), dim3(256), 0, s, M, N, beta, C,
                      ldc);
-  return hipGetLastError();
-}
-
-// Packed copy of an operand: dst (rows x ldd) = src (rows x cols, leading
-// dimension lds), columns [cols, ldd) zero.  Plain element copies, HBM-bound.
-__global__ void __launch_bounds__(256) pack_rows_f32_kernel(int rows, int cols, const float* src,
-                                                            int lds, float* dst, int ldd) {
-  const int64_t total = (int64_t)rows * ldd;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = t / ldd, c = t % ldd;
-    dst[t] = c < cols ? src[r * lds + c] : 0.0f;
-  }
-}
-
-hipError_t launch_pack_f32(const float* src, int rows, int cols, int lds, float* dst, int ldd,
-                           hipStream_t s) {
-  const int64_t total = (int64_t)rows * ldd;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL(pack_rows_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, rows, cols,
-                     src, lds, dst, ldd);
   return hipGetLastError();
 }
 

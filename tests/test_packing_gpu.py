@@ -157,3 +157,74 @@ def test_half_ffn_shape_with_odd_k_sampled():
                                     oracle.ACT_GELU_TANH, rows, cols)
     e = oracle.normalized_error(got.numpy()[rows, cols], ref, den)
     assert float(e.max()) <= FP16_TOL, "max normalised error %.3g" % e.max()
+
+
+# Register-staged FP32 tiles (0-6) on ragged shapes: when the copy pays, both
+# operands are copied zero-padded to whole tiles (A to ceil(M/BM) BM rows, K to
+# a multiple of the tile's K step, B to ceil(N/BN) BN columns) and the kernel
+# runs with unchecked loads and bounds-checked stores of C.
+REG_TILES = (0, 1, 2, 3, 4, 5, 6)
+
+
+@pytest.mark.parametrize("tile", REG_TILES)
+@pytest.mark.parametrize("shape", [(1000, 3000, 777), (700, 900, 777), (257, 1030, 1111),
+                                   (513, 520, 1024)])
+def test_sgemm_padded_register_tiles(tile, shape, forced):
+    force(0, tile, 1)
+    M, N, K = shape
+    assert lib.gemm_debug_pick_config(0, M, N, K, 256) == (tile, 1)
+    A, B, C = inputs.sgemm_inputs(M, N, K, 1300 + tile + M, ldc=N + 3)
+    ldc = C.shape[1]
+    A0, B0 = A.clone(), B.clone()
+    note("sgemm padded register tile %d M=%d N=%d K=%d ldc=%d" % (tile, M, N, K, ldc))
+    dA, dB, dC = A.cuda(), B.cuda(), C.cuda()
+    lib.sgemm(M, N, K, 0.75, dA, K, dB, N, 1.5, dC, ldc)
+    torch.cuda.synchronize()
+    got = dC.cpu()
+    err, where = sgemm_error(M, N, K, 0.75, A, K, B, N, 1.5, C, ldc, got)
+    assert err <= FP32_TOL, (err, where)
+    assert torch.isnan(got[:, N:]).all(), "wrote outside the N columns"
+    assert torch.equal(dA.cpu(), A0) and torch.equal(dB.cpu(), B0), "operands must stay unchanged"
+
+
+@pytest.mark.parametrize("tile", (1, 2, 4))
+@pytest.mark.parametrize("splits", [3, 7])
+def test_sgemm_padded_with_split(tile, splits, forced):
+    """Padded copies and split-K together: the last K chunk ends at the padded K."""
+    force(0, tile, splits)
+    M, N, K = 300, 650, 2001
+    t, s = lib.gemm_debug_pick_config(0, M, N, K, 256)
+    assert t == tile and 1 < s <= splits
+    A, B, C = inputs.sgemm_inputs(M, N, K, 1350 + tile + splits)
+    note("sgemm padded split tile %d x%d M=%d N=%d K=%d" % (tile, s, M, N, K))
+    got = run_sgemm(M, N, K, 1.0, A, K, B, N, -0.25, C, N)
+    err, where = sgemm_error(M, N, K, 1.0, A, K, B, N, -0.25, C, N, got)
+    assert err <= FP32_TOL, (err, where)
+
+
+@pytest.mark.parametrize("tile", (0, 2, 4))
+def test_sgemm_padded_exact_and_guard_bands(tile, forced):
+    """Small integers stay exact through the padded copies; nothing around C's
+    window changes."""
+    force(0, tile, 1)
+    M, N, K = 530, 1030, 523
+    g = torch.Generator().manual_seed(1370 + tile)
+    Ai = torch.randint(-7, 8, (M, K), generator=g)
+    Bi = torch.randint(-7, 8, (K, N), generator=g)
+    Ci = torch.randint(-7, 8, (M, N), generator=g)
+    want = (3 * (Ai.long() @ Bi.long()) - 2 * Ci.long()).float()
+    ldc = N + 2
+    guard = 2 * ldc
+    buf = torch.full((guard + M * ldc + guard,), 777.0)
+    body = buf[guard:guard + M * ldc].view(M, ldc)
+    body[:, :N] = Ci.float()
+    body[:, N:] = float("nan")
+    dA, dB, dbuf = Ai.float().cuda(), Bi.float().cuda(), buf.cuda()
+    note("sgemm padded exact tile %d" % tile)
+    lib.sgemm(M, N, K, 3.0, dA, K, dB, N, -2.0, dbuf.data_ptr() + guard * 4, ldc)
+    torch.cuda.synchronize()
+    out = dbuf.cpu()
+    assert torch.all(out[:guard] == 777.0) and torch.all(out[guard + M * ldc:] == 777.0)
+    res = out[guard:guard + M * ldc].view(M, ldc)
+    assert torch.isnan(res[:, N:]).all()
+    assert torch.equal(res[:, :N], want)
