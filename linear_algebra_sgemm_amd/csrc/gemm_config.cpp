@@ -89,8 +89,11 @@ long round_use(long tiles, int cus, int per_cu) {
 //    their tiles give every CU two (4096^3: 134 vs 130 for 256x256) — on shapes
 //    the direct-to-LDS kernel takes, only where they are whole (their
 //    bounds-checked form is slow: 3000^3 at 128x128: 77).
-//  * Else 64x64 tiles, which spread small outputs over more CUs (1024 x 3072 x
-//    768: 101 vs 92 for 128x128 direct at 192 tiles; 1000x3000x777: 68 vs 64).
+//  * Else 64x64 tiles, which spread small outputs over more CUs: direct-to-LDS
+//    where the copies are legal (1024 x 3072 x 768: 118 vs 103 for the
+//    register-staged 64x64 tile and 94 for 128x128 direct at 192 tiles;
+//    1000 x 3000 x 777: 83 vs 69; 1500^3: 89 vs 73 for the best register-staged
+//    tile; 256^3: 4.8 vs 3.8), else register-staged.
 int sgemm_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_tall = ceil_div(M, 128) * ceil_div(N, 256);
@@ -110,7 +113,7 @@ int sgemm_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   // (on shapes the direct-to-LDS kernel can take, only where these tiles are whole)
   if (t_tall >= 2L * cus && (!direct || (M % 128 == 0 && N % 256 == 0 && K % 16 == 0))) return 4;
   if (t_med >= 2L * cus && (!direct || (M % 128 == 0 && N % 128 == 0 && K % 16 == 0))) return 1;
-  return 2;
+  return direct ? 11 : 2;
 }
 
 // Built-in split rule: the direct-to-LDS tiles as in direct_splits (the
@@ -121,6 +124,17 @@ int sgemm_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
 int sgemm_rule_splits(int M, int N, int K, int tile, int cus) {
   const long tiles = ceil_div(M, sgemm_tile_bm(tile)) * ceil_div(N, sgemm_tile_bn(tile));
   if (tile == 7 || tile == 9 || tile == 10) return (int)direct_splits(tiles, K, cus);
+  if (tile == 11) {
+    // Up to four workgroups share a CU: split only outputs of at most half as
+    // many tiles as CUs, to about two workgroups per CU, in chunks of at least
+    // 512 (600 x 600 x 5000, 100 tiles: 39 unsplit, 66 in 2, 72 in 4; 700 x 900
+    // x 777, 165 tiles: 35 unsplit, 33 in 2).
+    if (2 * tiles > cus) return 1;
+    long s = 2L * cus / tiles;
+    if (s > K / 512) s = K / 512;
+    if (s > 16) s = 16;
+    return s < 1 ? 1 : (int)s;
+  }
   if (tile == 8) return (int)direct_splits((tiles + 1) / 2, K, cus);
   if (tiles >= cus || K < 512) return 1;
   const long by_cus = ceil_div(4L * cus, tiles);

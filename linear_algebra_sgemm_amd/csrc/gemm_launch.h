@@ -52,7 +52,8 @@ inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 // at two workgroups per CU with direct-to-LDS copies into a multi-stage ring
 // (rows of A and B 16-byte aligned and B readable in whole 4-float chunks, else
 // tile 4); 9 = tile 7 with eight waves, two per SIMD; 10 = 128x128 with
-// direct-to-LDS copies at two workgroups per CU.
+// direct-to-LDS copies at two workgroups per CU; 11 = 64x64 with direct-to-LDS
+// copies at up to four workgroups per CU (else tile 2).
 // HGEMM: 0 = 256x256, 1 = 128x128, 2 = 64x64 (register-staged, K step 64),
 // 3 = 256x256 direct-to-LDS, 4 stages of K step 32, 4 = 128x256 direct-to-LDS,
 // 3 stages, two workgroups per CU, 5 = 256x256 direct-to-LDS, 5 stages, 6 = 256x256
@@ -60,7 +61,7 @@ inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 // rounds of workgroups and 128 x 256 direct-to-LDS tiles on the rest (3 to 7 need
 // rows of A and B 16-byte aligned and B readable in whole 8-half chunks, 7 also
 // whole tiles; other operands fall back to 0).
-constexpr int kSgemmTileCount = 11;
+constexpr int kSgemmTileCount = 12;
 constexpr int kHgemmTileCount = 8;
 
 // K granularity of each SGEMM tile configuration: the K step, or for the
@@ -68,10 +69,12 @@ constexpr int kHgemmTileCount = 8;
 constexpr int sgemm_tile_bk(int tile) { return tile == 3 || tile >= 7 ? 32 : 16; }
 // Output tile of each SGEMM configuration.
 constexpr int sgemm_tile_bm(int tile) {
-  return tile == 0 || tile == 3 || tile == 5 || tile == 7 || tile == 9 ? 256 : tile == 2 ? 64 : 128;
+  return tile == 0 || tile == 3 || tile == 5 || tile == 7 || tile == 9 ? 256
+         : tile == 2 || tile == 11                                      ? 64
+                                                                        : 128;
 }
 constexpr int sgemm_tile_bn(int tile) {
-  return tile == 1 || tile == 10 ? 128 : tile == 2 ? 64 : 256;
+  return tile == 1 || tile == 10 ? 128 : tile == 2 || tile == 11 ? 64 : 256;
 }
 
 // Split-K: at most this many K chunks per output tile.

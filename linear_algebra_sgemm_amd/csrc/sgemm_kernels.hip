@@ -392,7 +392,8 @@ struct SDmaTile {
     return (r / B_RPC) * B_SLOT + (r % B_RPC) * (BN * 4);
   }
 
-  static_assert(BN * 4 == 1024 || BN * 4 == 512, "one or two rows of B per copy instruction");
+  static_assert(BN * 4 == 1024 || BN * 4 == 512 || BN * 4 == 256,
+                "one, two or four rows of B per copy instruction");
   static_assert(((4 / B_RPC) * B_SLOT) % 256 == 128, "k-slots of a B read on opposite bank halves");
   static_assert(A_INSTR % WAVES == 0 && B_INSTR % WAVES == 0, "copies split evenly over waves");
   static_assert(STAGE_BYTES % 16 == 0, "stages start on 16-byte boundaries");
@@ -732,6 +733,9 @@ using SDmaEight = SDmaTile<256, 256, 4, 2, 2, 4>;
 // 128 x 128 with four waves of 64 x 64, 4 stages of 16.5 KiB, two workgroups per CU:
 // outputs with too few 256 x 256 tiles to fill the CUs.
 using SDmaSmall = SDmaTile<128, 128, 4, 2, 2, 2>;
+// 64 x 64 with four waves of 32 x 32, 4 stages of 8.5 KiB, up to four workgroups
+// per CU: small and mid-size outputs (about 100 to 1000 tiles), spread evenly.
+using SDmaMini = SDmaTile<64, 64, 4, 4, 2, 2>;
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -746,7 +750,9 @@ static_assert(TileLarge::BK == sgemm_tile_bk(0) && TileMedium::BK == sgemm_tile_
                   SDmaTall::BM == sgemm_tile_bm(8) && SDmaTall::BN == sgemm_tile_bn(8) &&
                   SDmaEight::BM == sgemm_tile_bm(9) && SDmaEight::BN == sgemm_tile_bn(9) &&
                   2 * SDmaEight::BK == sgemm_tile_bk(9) && SDmaSmall::BM == sgemm_tile_bm(10) &&
-                  SDmaSmall::BN == sgemm_tile_bn(10) && 2 * SDmaSmall::BK == sgemm_tile_bk(10),
+                  SDmaSmall::BN == sgemm_tile_bn(10) && 2 * SDmaSmall::BK == sgemm_tile_bk(10) &&
+                  SDmaMini::BM == sgemm_tile_bm(11) && SDmaMini::BN == sgemm_tile_bn(11) &&
+                  2 * SDmaMini::BK == sgemm_tile_bk(11),
               "the host-side planner's K steps must match the tiles");
 
 static hipError_t launch_reduce(const SgemmCall& c, int splits, const float* ws, hipStream_t s) {
@@ -869,9 +875,10 @@ int sgemm_resolve_tile(int tile, int M, int N, int K, int splits, bool operands_
   // The direct-to-LDS kernels need rows of A and B on 16-byte boundaries and B
   // readable in whole 4-float chunks (any M, N and K otherwise: ragged edges and
   // a ragged K run a bounds-checked instantiation); otherwise the
-  // register-staged 128 x 256 kernel (the best of those for large outputs) runs.
+  // register-staged 128 x 256 kernel (the best of those for large outputs) runs,
+  // or for the 64 x 64 tile its register-staged twin.
   (void)M; (void)N; (void)K; (void)splits;
-  if (tile >= 7 && !operands_ok) return 4;
+  if (tile >= 7 && !operands_ok) return tile == 11 ? 2 : 4;
   return tile;
 }
 
@@ -889,6 +896,7 @@ hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hi
     case 8: return launch_sdma<SDmaTall>(c, plan, 8, ws, s);
     case 9: return launch_sdma<SDmaEight>(c, plan, 4, ws, s);
     case 10: return launch_sdma<SDmaSmall>(c, plan, 8, ws, s);
+    case 11: return launch_sdma<SDmaMini>(c, plan, 8, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -153,21 +153,25 @@ def test_config_rule(so):
         (0, 4096, 4096, 4002, 256, (9, 1)),   # lda = 4002: A packed to 16-byte rows first
         (0, 4096, 4090, 4096, 256, (9, 1)),   # N not a multiple of 4: B packed first
         (0, 64, 4090, 64, 256, (2, 1)),       # packing B would cost more than it saves
-        (0, 256, 256, 256, 256, (2, 1)),      # K < 512: no split
-        (0, 256, 256, 1024, 256, (2, 8)),     # 16 tiles; chunks of 128
-        (0, 512, 512, 512, 256, (2, 4)),      # 64 tiles; chunks of 128
-        (0, 1000, 3000, 777, 256, (2, 1)),    # 752 tiles
+        (0, 256, 256, 256, 256, (11, 1)),     # 64x64 direct-to-LDS; K < 1024: no split
+        (0, 256, 256, 1024, 256, (11, 2)),    # 16 tiles; chunks of at least 512
+        (0, 512, 512, 512, 256, (11, 1)),     # 64 tiles, K < 1024
+        (0, 1000, 3000, 777, 256, (11, 1)),   # 752 tiles
         (0, 2048, 2048, 2048, 256, (10, 1)),  # 64 tiles of 256x256, 256 of 128x128: direct 128x128
         (0, 2048, 2048, 8192, 256, (10, 1)),
         (0, 1024, 2048, 4096, 256, (10, 2)),  # 128 tiles of 128x128, 2 chunks of 2048
         (0, 1024, 1024, 4096, 256, (10, 4)),  # 64 tiles, 4 chunks of 1024
         (0, 1024, 1024, 8192, 256, (10, 4)),
         (0, 2048, 4096, 1024, 256, (10, 1)),  # 512 tiles of 128x128
-        (0, 512, 512, 8192, 256, (2, 16)),    # 16 tiles of 128x128 only: split 64x64
-        (0, 1024, 3072, 768, 256, (2, 1)),    # 192 tiles of 128x128 would need a split of 1
-        (0, 1536, 3072, 2048, 256, (2, 1)),   # 288 tiles of 128x128 fill 56 % of 512 slots
+        (0, 512, 512, 8192, 256, (11, 8)),    # 16 tiles of 128x128 only: 64 of 64x64, 8 chunks
+        (0, 1024, 3072, 768, 256, (11, 1)),   # 192 tiles of 128x128 would need a split of 1
+        (0, 1536, 3072, 2048, 256, (11, 1)),  # 288 tiles of 128x128 fill 56 % of 512 slots
+        (0, 1000, 1000, 1000, 256, (11, 1)),  # 256 tiles of 64x64: no split
+        (0, 600, 600, 5000, 256, (11, 5)),    # 100 tiles: about two workgroups per CU
         (0, 4096, 4096, 4096, 64, (9, 1)),
-        (0, 128, 128, 16384, 256, (2, 32)),   # 4 tiles; 256 chunks by CUs, capped at 32
+        (0, 128, 128, 16384, 256, (11, 16)),  # 4 tiles; 128 chunks by CUs, capped at 16
+        (0, 300, 520, 100, 256, (11, 1)),     # ragged and small: the bounds-checked 64x64 copies
+        (0, 300, 521, 100, 256, (2, 1)),      # N odd and too small to pack: register-staged
         (1, 4096, 14336, 4096, 256, (7, 1)),  # whole 256-tiles, long K: eight waves + tail split
         (1, 4096, 4096, 4096, 256, (6, 1)),   # no partial round: eight waves, no split
         (1, 4096, 4096, 1024, 256, (3, 1)),   # shorter K: four waves
@@ -300,15 +304,16 @@ def test_split_legality(so):
             M, N = rng.randint(1, 3000), rng.randint(1, 3000)
             K = rng.choice([1, 15, 16, 17, 100, 777, 4096, 20000])
             want = rng.choice([1, 2, 3, 5, 8, 16, 32])
-            tile = rng.choice([-1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
+            tile = rng.choice([-1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11])
             assert lib.gemm_debug_force_tile(0, tile) == lib.STATUS_SUCCESS
             assert lib.gemm_debug_force_splits(0, want) == lib.STATUS_SUCCESS
             t, s = pick(0, M, N, K)
             if tile >= 0:
-                # direct-to-LDS tiles (7, 8) run as 0 / 4 unless the shape is whole and unsplit
-                assert t == tile or (tile, t) in ((7, 4), (8, 4), (9, 4), (10, 4))
+                # direct-to-LDS tiles (7-11) run as their register-staged twin (4, or 2
+                # for 11) where the operands do not allow copies (N % 4 != 0 and no packing)
+                assert t == tile or (tile, t) in ((7, 4), (8, 4), (9, 4), (10, 4), (11, 2))
                 if t != tile:
-                    assert s > 1 or M % (128 if tile == 8 else 256) or N % 256 or K % 32
+                    assert N % 4 != 0 or K % 4 != 0
             # the chunks are planned in the K granularity of the tile asked for (the
             # tuned or forced one) before a direct-to-LDS tile resolves to tile 4
             ok = False
@@ -357,7 +362,8 @@ def test_forced_splits(so):
 
 
 def test_force_tile_values(so):
-    assert lib.gemm_debug_force_tile(0, 11) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(0, 12) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(0, 11) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(0, 9) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(1, 8) == lib.STATUS_INVALID_VALUE
     assert lib.gemm_debug_force_tile(1, 7) == lib.STATUS_SUCCESS

@@ -47,7 +47,7 @@ def force(op, tile, splits=-1):
     assert lib.gemm_debug_force_splits(op, splits) == lib.STATUS_SUCCESS
 
 
-@pytest.mark.parametrize("tile", [7, 8, 9, 10])
+@pytest.mark.parametrize("tile", [7, 8, 9, 10, 11])
 @pytest.mark.parametrize("shape", [(400, 1026, 777), (600, 1026, 1001), (257, 1000, 1111),
                                    (64, 2048, 2049)])
 def test_sgemm_packed_operands(tile, shape, forced):
