@@ -528,8 +528,13 @@ __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::F
   constexpr int NR = T::FM + 2 * T::FN;              // LDS reads per k step
   constexpr int PRE = 2;                             // MFMAs issued before the barrier
   constexpr int R0 = (NR + NM - PRE - 1) / (NM - PRE);          // reads per MFMA, step 0
-  constexpr int TAIL = NM - T::LOADS_PER_TILE;                  // MFMAs before the direct loads
-  static_assert(NM > PRE && TAIL >= 1 && T::LOADS_PER_TILE <= NM, "enough MFMAs to hide behind");
+  // Direct loads issued at the end of step 0 (L0) and among step 1's MFMAs (L1):
+  // all in step 1 unless a wave has as many loads as MFMAs per k step (a
+  // 128x128 tile), then half in each.
+  constexpr int L0 = NM - T::LOADS_PER_TILE >= 1 ? 0 : T::LOADS_PER_TILE / 2;
+  constexpr int L1 = T::LOADS_PER_TILE - L0;
+  constexpr int TAIL = NM - L1;                                 // MFMAs before the direct loads
+  static_assert(NM > PRE && TAIL >= 1 && L1 <= NM, "enough MFMAs to hide behind");
   constexpr int R1 = (NR + TAIL - 1) / TAIL;                    // reads per MFMA, step 1
   // Two MFMAs first, so the matrix unit has work queued while the waves meet.
   hmfma<T>(acc, x0, 0);
@@ -553,16 +558,24 @@ __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::F
     __builtin_amdgcn_sched_group_barrier(0x100, R0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // Step 1: the reads of the next tile's second k step with the first MFMAs, then
-  // the direct loads of tile kt + STAGES - 1 with the rest.  Reading first leaves
-  // the last LDS reads of the tile several MFMAs before its end, so they have
-  // landed when the next tile waits for its fragments (the compiler's wait at the
-  // top of the K loop is for all of them).
   const int kt_issue = kt + T::STAGES - 1;
   const bool issue = STEADY || kt_issue < ktiles;
   const uint32_t st_issue = lds_base + (kt_issue % T::STAGES) * T::STAGE_BYTES;
   const uint16_t* a_issue = a_tile + kt_issue * T::BK;
   const uint16_t* b_issue = b_tile + (size_t)kt_issue * T::BK * p.ldb;
+  if constexpr (L0 > 0) {
+#pragma unroll
+    for (int x = 0; x < L0; ++x)
+      if (issue)
+        dma16_sbase(x < T::A_PER_WAVE ? a_issue : b_issue, dma.off[x],
+                    st_issue + hdma_lds_slot<T>(x, wave));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Step 1: the reads of the next tile's second k step with the first MFMAs, then
+  // the direct loads of tile kt + STAGES - 1 with the rest.  Reading first leaves
+  // the last LDS reads of the tile several MFMAs before its end, so they have
+  // landed when the next tile waits for its fragments (the compiler's wait at the
+  // top of the K loop is for all of them).
   if constexpr (2 * TAIL >= NR) {
     hload_frags<T>(y1, next, 1, wm, wn, lane);
 #pragma unroll
@@ -574,8 +587,8 @@ __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::F
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int x = 0; x < T::LOADS_PER_TILE; ++x) {
-      hmfma<T>(acc, x1, TAIL + x);
+    for (int x = L0; x < T::LOADS_PER_TILE; ++x) {
+      hmfma<T>(acc, x1, TAIL + x - L0);
       if (issue)
         dma16_sbase(x < T::A_PER_WAVE ? a_issue : b_issue, dma.off[x],
                     st_issue + hdma_lds_slot<T>(x, wave));
@@ -584,15 +597,15 @@ __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::F
     // Few MFMAs per k step (the 128 x 256 tile): loads first, so the reads are
     // not crowded into the last MFMAs' registers.
 #pragma unroll
-    for (int x = 0; x < T::LOADS_PER_TILE; ++x) {
-      hmfma<T>(acc, x1, x);
+    for (int x = L0; x < T::LOADS_PER_TILE; ++x) {
+      hmfma<T>(acc, x1, x - L0);
       if (issue)
         dma16_sbase(x < T::A_PER_WAVE ? a_issue : b_issue, dma.off[x],
                     st_issue + hdma_lds_slot<T>(x, wave));
     }
     hload_frags<T>(y1, next, 1, wm, wn, lane);
 #pragma unroll
-    for (int x = T::LOADS_PER_TILE; x < NM; ++x) hmfma<T>(acc, x1, x);
+    for (int x = L1; x < NM; ++x) hmfma<T>(acc, x1, x);
 #pragma unroll
     for (int x = 0; x < TAIL; ++x) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
