@@ -221,7 +221,13 @@ int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   // eight-wave 256x256 tile, or 128x256 where fewer than 64 256x256 tiles exist
   // and K is below 2048 (1000^3: 68 vs 65; 1000 x 1000 x 4000: 75 vs 97) -- as
   // long as there are 16 tiles of 128x256; below that the split 64x64 tile is
-  // ahead (504 x 504 x 8000: 33 vs 27).
+  // ahead (504 x 504 x 8000: 33 vs 27).  Between those, where the copies are
+  // legal and the 128x128 tiles number a quarter to twice the CUs (one round
+  // at two per CU), the 128x128 direct-to-LDS tile beats them all (2048^3:
+  // 640 vs 404 for 64x64; 1024 x 4096 x 4096: 776 vs 528 for 128x128
+  // register-staged; 2048 x 2048 x 8192: 823 vs 641; 1000^3: 129 vs 68 for
+  // 128x256 direct; 1024^3: 185 vs 155) -- but not once there are more
+  // (3000^3: 494 vs 642 for the eight-wave tile).
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
   const bool direct = operands_ok;
@@ -229,6 +235,7 @@ int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
     if (!direct) return 0;
     return K >= 2048 ? 7 : 3;
   }
+  if (direct && 4 * t_med >= cus && t_med <= 2L * cus) return 8;
   const int reg = t_med >= 2L * cus ? 1 : 2;
   const int bm = half_tile_bm(reg);
   const bool reg_whole = M % bm == 0 && N % bm == 0 && K % kHalfBK == 0;
@@ -261,8 +268,8 @@ HalfPlan plan_half(int M, int N, int K, int cus, int force_tile, int force_split
   // Table entries were measured on whole tiles with aligned operands; where the
   // entry's tile would run bounds-checked here, the rule chooses instead.
   if (tuned) {
-    const int bm = tuned_tile <= 2 ? half_tile_bm(tuned_tile) : tuned_tile == 4 ? 128 : 256;
-    const int bn = tuned_tile <= 2 ? bm : 256;
+    const int bm = half_tile_rows(tuned_tile);
+    const int bn = half_tile_cols(tuned_tile);
     if (!(operands_ok && M % bm == 0 && N % bn == 0 && K % kHalfBK == 0))
       tuned = false;
   }

@@ -60,9 +60,10 @@ inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 // direct-to-LDS with eight waves, 7 = tile 6 on the columns that fill whole
 // rounds of workgroups and 128 x 256 direct-to-LDS tiles on the rest (3 to 7 need
 // rows of A and B 16-byte aligned and B readable in whole 8-half chunks, 7 also
-// whole tiles; other operands fall back to 0).
+// whole tiles; other operands fall back to 0); 8 = 128x128 direct-to-LDS, 4
+// stages, two workgroups per CU (other operands fall back to 1).
 constexpr int kSgemmTileCount = 12;
-constexpr int kHgemmTileCount = 8;
+constexpr int kHgemmTileCount = 9;
 
 // K granularity of each SGEMM tile configuration: the K step, or for the
 // direct-to-LDS tiles (7-10) their two-tile loop body (checked against the kernels).
@@ -121,6 +122,13 @@ struct HalfPlan {
 // Output tile of the register-staged half configurations 0-2 (K step 64).
 constexpr int half_tile_bm(int tile) { return tile == 0 ? 256 : tile == 1 ? 128 : 64; }
 constexpr int kHalfBK = 64;
+// Output tile of every half configuration (rows, columns).
+constexpr int half_tile_rows(int tile) {
+  return tile <= 2 ? half_tile_bm(tile) : tile == 4 || tile == 8 ? 128 : 256;
+}
+constexpr int half_tile_cols(int tile) {
+  return tile <= 2 ? half_tile_bm(tile) : tile == 8 ? 128 : 256;
+}
 
 // The plan for an M x N x K half product on `cus` compute units (`operands_ok`:
 // lda and ldb are multiples of 8, A, B 16-byte aligned and B readable in whole

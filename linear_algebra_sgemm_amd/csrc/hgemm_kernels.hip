@@ -830,6 +830,10 @@ template <class E> using HDmaEight = HDmaTile<E, 256, 256, 32, 4, 2, 2, 4>;
 // 128 x 256 with eight waves of 64 x 64 and four stages: 96 KiB of LDS, so each
 // CU holds one workgroup and a round of them spreads over every CU.
 template <class E> using HDmaHalfEight = HDmaTile<E, 128, 256, 32, 4, 2, 2, 4>;
+// 128 x 128 with four waves of 64 x 64, four stages of 16 KiB, two workgroups per
+// CU: outputs of a quarter to twice as many such tiles as CUs.  A wave has as
+// many direct loads as MFMAs per k step, so half go out in each step.
+template <class E> using HDmaSquare = HDmaTile<E, 128, 128, 32, 4, 2, 2, 2>;
 
 // Second half of split-K: C = act(alpha * (sum of the `splits` partials, added
 // in order 0, 1, ...) + bias[col]), rounded to the 16-bit format.
@@ -944,7 +948,10 @@ static_assert(HDmaLarge<EltF16>::BM == 256 && HDmaLarge<EltF16>::BN == 256 &&
                   HDmaEight<EltF16>::BM == 256 && HDmaEight<EltF16>::BN == 256 &&
                   2 * HDmaEight<EltF16>::BK == 64 &&
                   2 * HDmaLarge<EltF16>::BK == 64 && 2 * HDmaTall<EltF16>::BK == 64 &&
-                  2 * HDmaDeep<EltF16>::BK == 64,
+                  2 * HDmaDeep<EltF16>::BK == 64 && HDmaSquare<EltF16>::BM == half_tile_rows(8) &&
+                  HDmaSquare<EltF16>::BN == half_tile_cols(8) && 2 * HDmaSquare<EltF16>::BK == 64 &&
+                  HDmaTall<EltF16>::BM == half_tile_rows(4) &&
+                  HDmaTall<EltF16>::BN == half_tile_cols(4),
               "hgemm_resolve_tile's shape conditions must match the direct-to-LDS tiles");
 
 int hgemm_tail_split(int M, int N, int cus) {
@@ -967,8 +974,9 @@ int hgemm_resolve_tile(int tile, int M, int N, int K, bool operands_ok, int cus)
   // instantiation); otherwise the register-staged 256x256 kernel, which handles
   // every shape, runs.  The head/tail column split needs whole 256x256 tiles, K
   // a multiple of 64 and a split that fills the last round; else the eight-wave
-  // tile runs alone.
-  if (tile >= 3 && !operands_ok) return 0;
+  // tile runs alone.  The 128x128 direct-to-LDS tile falls back to its
+  // register-staged twin.
+  if (tile >= 3 && !operands_ok) return tile == 8 ? 1 : 0;
   if (tile == 7 && !(M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && hgemm_tail_split(M, N, cus) > 0))
     return 6;
   return tile;
@@ -1006,6 +1014,9 @@ static hipError_t launch_half(const HgemmCall& c, const HalfPlan& plan, int cus,
     case 6:
       if (!dma_fits<HDmaEight<E>>(c)) return hipErrorInvalidValue;
       return launch_hdma<HDmaEight<E>>(c, 4, s);
+    case 8:
+      if (!dma_fits<HDmaSquare<E>>(c)) return hipErrorInvalidValue;
+      return launch_hdma<HDmaSquare<E>>(c, 8, s);
     case 7: {
       // Columns [0, n1): eight-wave 256 x 256 tiles in whole rounds; the rest:
       // 128 x 256 tiles, twice as many half-size tiles in the last round.

@@ -17,7 +17,7 @@ from tests.gpu_helpers import FP16_TOL, f16_bits, hgemm_error, note, run_hgemm
 
 pytestmark = pytest.mark.gpu
 
-TILES = (0, 1, 2, 3, 4, 5, 6, 7)
+TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8)
 
 
 @pytest.fixture(scope="module", autouse=True)

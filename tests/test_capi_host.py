@@ -177,13 +177,15 @@ def test_config_rule(so):
         (1, 4096, 4096, 1024, 256, (3, 1)),   # shorter K: four waves
         (1, 4096, 4000, 4096, 256, (6, 1)),   # ragged N: eight waves, no column split
         (1, 4096, 4004, 4096, 256, (6, 1)),   # N not a multiple of 8: B packed first
-        (1, 2048, 2000, 4096, 256, (6, 1)),   # ragged N: 64x64 would run bounds-checked
-        (1, 1000, 1000, 1000, 256, (4, 1)),   # ragged, 16 tiles of 256x256: 128x256
-        (1, 1000, 1004, 1000, 256, (4, 1)),   # N not a multiple of 8: B packed, as above
-        (1, 4096, 2048, 4096, 256, (1, 1)),   # 512 tiles of 128x128
+        (1, 2048, 2000, 4096, 256, (8, 1)),   # ragged N, 256 tiles of 128x128: direct 128x128
+        (1, 1000, 1000, 1000, 256, (8, 1)),   # ragged, 64 tiles of 128x128
+        (1, 1000, 1004, 1000, 256, (8, 1)),   # N not a multiple of 8: B packed, as above
+        (1, 3000, 3000, 3000, 256, (6, 1)),   # 576 tiles of 128x128: more than one round
+        (1, 4096, 2048, 4096, 256, (8, 1)),   # 512 tiles of 128x128: one round at two per CU
         (1, 4096, 4096, 256, 256, (1, 1)),    # K < 512: not the 256x256 tiles
         (1, 300, 500, 4096, 256, (2, 22)),     # 40 tiles of 64x64: ~4 workgroups per CU
-        (1, 1024, 1024, 4096, 256, (2, 1)),    # 256 tiles of 64x64 cover the CUs
+        (1, 1024, 1024, 4096, 256, (8, 1)),    # 64 tiles of 128x128: direct 128x128
+        (1, 1024, 1024, 4095, 256, (8, 1)),    # the same with K ragged (A packed)
         (1, 512, 512, 4096, 256, (2, 16)),     # 64 tiles; 16 chunks of 256
         (1, 512, 512, 256, 256, (2, 1)),       # K < 512: no split
     ]
@@ -365,7 +367,8 @@ def test_force_tile_values(so):
     assert lib.gemm_debug_force_tile(0, 12) == lib.STATUS_INVALID_VALUE
     assert lib.gemm_debug_force_tile(0, 11) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(0, 9) == lib.STATUS_SUCCESS
-    assert lib.gemm_debug_force_tile(1, 8) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(1, 9) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(1, 8) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(1, 7) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(1, 5) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(1, 3) == lib.STATUS_SUCCESS

@@ -1,7 +1,7 @@
 """The half-precision direct-to-LDS kernels (binary16 and bfloat16) on ragged shapes,
 on the GPU through the C ABI, against the CPU oracle.
 
-Tiles 3-6 copy 16-byte chunks of A and B straight into LDS.  When M or N is not
+Tiles 3-6 and 8 copy 16-byte chunks of A and B straight into LDS.  When M or N is not
 a multiple of the tile, or K not a multiple of 64, they run a bounds-checked
 instantiation: copies of rows past M - 1 (8-column chunks past N - 8) repeat the
 last row (chunk) inside the matrix, the last K % 64 values of k go through one
@@ -22,7 +22,7 @@ from tests.gpu_helpers import FP16_TOL, hgemm_error, note, run_hgemm
 pytestmark = pytest.mark.gpu
 
 FMTS = {"f16": torch.float16, "bf16": torch.bfloat16}
-DMA_TILES = (3, 4, 5, 6)
+DMA_TILES = (3, 4, 5, 6, 8)
 SHAPES = [(300, 520, 100), (257, 264, 33), (64, 64, 16), (1, 8, 1), (129, 136, 31),
           (511, 520, 64), (700, 904, 777), (256, 256, 40), (1000, 1000, 1000), (260, 8, 4100)]
 
@@ -76,7 +76,7 @@ def test_ragged_shapes(fmt, tile, shape, forced):
     # are packed first when that pays, else tile 0 runs; with lda padded to a
     # multiple of 8, as here, the direct-to-LDS tile runs for every shape
     t, s = lib.gemm_debug_pick_config(1, M, N, K, 256)
-    assert (t, s) == (tile, 1) or (K % 8 != 0 and t == 0)
+    assert (t, s) == (tile, 1) or (K % 8 != 0 and t == (1 if tile == 8 else 0))
     check(fmt, M, N, K, 1.25, lib.ACT_GELU_TANH, seed=1100 + tile + M + K, label="tile %d" % tile)
 
 
@@ -138,7 +138,7 @@ def test_misaligned_operands_are_packed(forced):
 
 @pytest.mark.parametrize("fmt", list(FMTS))
 @pytest.mark.parametrize("shape,want", [((4000, 14000, 4000), (6, 1)), ((3000, 3000, 3000), (6, 1)),
-                                        ((1000, 1000, 1000), (4, 1))])
+                                        ((1000, 1000, 1000), (8, 1)), ((2000, 2000, 2000), (8, 1))])
 def test_auto_choice_ragged_sampled(fmt, shape, want):
     """Ragged products on the configuration the library picks, checked on sampled
     outputs (the four corners, the last row and column, and uniform picks)."""

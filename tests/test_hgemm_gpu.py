@@ -19,8 +19,8 @@ from tests.gpu_helpers import FP16_TOL, f16_bits, hgemm_error, note, run_hgemm
 
 pytestmark = pytest.mark.gpu
 
-TILES = (0, 1, 2, 3, 4, 5, 6, 7)   # register-staged 256, 128, 64; direct-to-LDS 256x256,
-#                           128x256, 256x256 5-stage, 256x256 eight waves, eight waves + tail
+TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8)   # register-staged 256, 128, 64; direct-to-LDS 256x256,
+#      128x256, 256x256 5-stage, 256x256 eight waves, eight waves + tail, 128x128
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -88,16 +88,16 @@ def test_edge_grid(M, N, K):
 
 
 @pytest.mark.parametrize("K", [32, 64, 128, 192, 256, 1024])
-@pytest.mark.parametrize("tile", [3, 4, 5, 6])
+@pytest.mark.parametrize("tile", [3, 4, 5, 6, 8])
 def test_direct_to_lds_pipeline_depths(K, tile, tile_forced):
     """Whole tiles with K a multiple of 64 take the direct-to-LDS kernels; K from 2 to 32
     tiles of 32 exercises every prologue / drain case of their 4-, 3- and 5-stage pipelines
-    (K = 32 falls back to the register-staged kernel)."""
+    (K = 32 is one bounds-checked tail step)."""
     lib.gemm_debug_force_tile(1, tile)
     check_full(512, 256, K, 1.0, lib.ACT_GELU_TANH, seed=K, label="dma%d K=%d" % (tile, K))
 
 
-@pytest.mark.parametrize("tile", [3, 4, 5, 6])
+@pytest.mark.parametrize("tile", [3, 4, 5, 6, 8])
 def test_direct_to_lds_unaligned_ldc(tile, tile_forced):
     lib.gemm_debug_force_tile(1, tile)
     check_full(256, 512, 64, 0.5, lib.ACT_GELU_TANH, seed=77, ldc=515, label="dma ldc=515")
@@ -114,7 +114,7 @@ def test_padded_leading_dimensions():
 def test_exact_identity_and_permutation(tile, tile_forced):
     lib.gemm_debug_force_tile(1, tile)
     g = torch.Generator().manual_seed(17)
-    M, N = 256, (512 if tile in (3, 4, 5, 6) else 320)
+    M, N = 256, (512 if tile in (3, 4, 5, 6, 8) else 320)
     B = (torch.randn((M, N), generator=g)).half()
     C = torch.zeros((M, N), dtype=torch.float16)
     note("hgemm identity tile=%d" % tile)
