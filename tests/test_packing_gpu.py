@@ -106,6 +106,31 @@ def test_sgemm_unaligned_bases(tile, forced):
     assert err <= FP32_TOL, (err, where)
 
 
+def test_second_stream_while_a_packed_call_runs(forced):
+    """A long packed call on the current stream is still running when a packed call
+    on another stream is enqueued: the second call's copies must not overwrite the
+    pack buffer under the first (the library orders the first use of a second
+    stream after all queued work)."""
+    force(0, 9, 1)
+    M, N, K = 3000, 4002, 3001          # lda = 3001 and N = 4002: both operands packed
+    A, B, C = inputs.sgemm_inputs(M, N, K, 1241)
+    m, n, k = 600, 1026, 1001
+    a, b, c = inputs.sgemm_inputs(m, n, k, 1242)
+    dA, dB, dC, da, db, dc = A.cuda(), B.cuda(), C.cuda(), a.cuda(), b.cuda(), c.cuda()
+    torch.cuda.synchronize()
+    s2 = torch.cuda.Stream()
+    note("sgemm packed call, then a second stream")
+    lib.sgemm(M, N, K, 1.0, dA, K, dB, N, 0.5, dC, N, stream=torch.cuda.current_stream())
+    lib.sgemm(m, n, k, 1.0, da, k, db, n, 0.5, dc, n, stream=s2)
+    torch.cuda.synchronize()
+    err, where = sgemm_error(m, n, k, 1.0, a, k, b, n, 0.5, c, n, dc)
+    assert err <= FP32_TOL, ("second stream", err, where)
+    rows, cols = inputs.sample_indices(M, N, 2048, 1241)
+    ref, den = oracle.sgemm_entries(K, 1.0, A.numpy(), K, B.numpy(), N, 0.5, C.numpy(), N, rows, cols)
+    e = oracle.normalized_error(dC.cpu().numpy()[rows, cols], ref, den)
+    assert float(e.max()) <= FP32_TOL, ("first stream", float(e.max()))
+
+
 def test_packed_calls_on_two_streams_take_turns(forced):
     """Calls that pack, on two streams, share the pack buffer; the library orders them."""
     force(0, 9, 1)
