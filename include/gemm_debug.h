@@ -18,10 +18,10 @@ extern "C" {
  * largest tile, 1 = medium, 2 = small; sgemm also has 3 = largest tile with a
  * K step of 32, 4 = 128 x 256 tiles at two workgroups per compute unit, 5
  * and 6 = tiles 0 and 4 built from 16 x 16 x 4 MFMA blocks, and 7 and 8 = tiles
- * 0 and 4 with direct-to-LDS copies (rows of A and B on 16-byte boundaries and
- * N a multiple of 4, else the operands are packed when the copy is small next
- * to the product, else tile 4 runs; ragged M, N or K run their bounds-checked
- * instantiation), 9 = tile 7 with eight waves, 10 = 128 x 128 direct-to-LDS
+ * 0 and 4 with direct-to-LDS copies (rows of B on 16-byte boundaries and N a
+ * multiple of 4, else B is packed when the copy is small next to the product,
+ * else tile 4 runs; rows of A off 16-byte boundaries are copied 4 bytes at a
+ * time; ragged M, N or K run their bounds-checked instantiation), 9 = tile 7 with eight waves, 10 = 128 x 128 direct-to-LDS
  * tiles at two workgroups per compute unit, 11 = 64 x 64 direct-to-LDS tiles
  * at up to four workgroups per compute unit (tile 2 where the operands do not
  * allow direct copies); the
@@ -63,9 +63,11 @@ int gemm_debug_use_tuned_table(int on);
  * configuration, *splits the number of K chunks (1 = no split).  op 0 = sgemm,
  * op 1 = the half products, both with packed operands (lda = K, ldb = N) on
  * 16-byte-aligned bases; where those rows do not suit the direct-to-LDS
- * kernels (K or N not a multiple of 4 for sgemm, of 8 for the half products),
- * the call would pack them into the library's buffer when the copy is small
- * next to the product, and the result says what then runs.  Returns GEMM_STATUS_INVALID_VALUE for an unknown op,
+ * kernels (N not a multiple of 4 for sgemm; K or N not a multiple of 8 for the
+ * half products), the call would pack them into the library's buffer when the
+ * copy is small next to the product, and the result says what then runs (the
+ * FP32 direct-to-LDS kernels copy rows of A with K not a multiple of 4 4 bytes
+ * at a time).  Returns GEMM_STATUS_INVALID_VALUE for an unknown op,
  * negative sizes, cus <= 0 or a null output pointer.  Pure host computation:
  * no HIP call, no library state needed.
  */

@@ -49,6 +49,12 @@ __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t offset, u
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :: "s"(lds_base), "v"(offset), "s"(base) : "memory", "m0");
 }
+// The same with 4 bytes per lane (lane l writes LDS bytes [lds_base + 4 l, +4)):
+// for sources whose rows are only 4-byte aligned.
+__device__ __forceinline__ void dma4_sbase(const void* base, uint32_t offset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds_base), "v"(offset), "s"(base) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {

@@ -212,10 +212,15 @@ hipError_t pack_operands(const Packing& pk, int M, int N, int K, int elem, void*
   return hipSuccess;
 }
 
-// Direct-to-LDS operand conditions of the FP32 product (rows 16-byte aligned,
-// B readable in whole 4-float chunks, 32-bit copy offsets).
+// Operand conditions of the FP32 product.  A's rows on 16-byte boundaries (the
+// register-staged tiles' 16-byte loads); A's rows on 4-byte boundaries with
+// 32-bit copy offsets (the direct-to-LDS tiles, which copy A 4 bytes at a time
+// where its rows are not 16-byte aligned); B's rows 16-byte aligned and
+// readable in whole 4-float chunks, 32-bit copy offsets.
+bool sgemm_a_rows16(const void* A, int lda) { return lda % 4 == 0 && aligned16(A); }
 bool sgemm_a_ok(const void* A, int lda) {
-  return lda % 4 == 0 && aligned16(A) && (int64_t)lda * 256 * 4 < (int64_t(1) << 31);
+  return (reinterpret_cast<uintptr_t>(A) & 3u) == 0 &&
+         (int64_t)lda * 256 * 4 < (int64_t(1) << 31);
 }
 bool sgemm_b_ok(const void* B, int ldb, int N) {
   return ldb % 4 == 0 && N % 4 == 0 && aligned16(B) && (int64_t)ldb * 16 * 4 < (int64_t(1) << 31);
@@ -228,14 +233,15 @@ bool half_b_ok(const void* B, int ldb, int N) {
   return ldb % 8 == 0 && N % 8 == 0 && aligned16(B) && (int64_t)ldb * 32 * 2 < (int64_t(1) << 31);
 }
 
-// The FP32 plan, and whether (and how) operands are packed for it.
-lasg::SgemmPlan decide_sgemm(int M, int N, int K, bool a_ok, bool b_ok, int cus, size_t ws_floats,
-                             size_t pack_bytes, Packing& pk, bool& pack) {
+// The FP32 plan, and whether (and how) operands are packed for it: `a16`,
+// `a_ok`, `b_ok` as above.
+lasg::SgemmPlan decide_sgemm(int M, int N, int K, bool a16, bool a_ok, bool b_ok, int cus,
+                             size_t ws_floats, size_t pack_bytes, Packing& pk, bool& pack) {
   const int ft = g_force_sgemm_tile.load(), fs = g_force_sgemm_splits.load();
   pack = !(a_ok && b_ok) && plan_packing(M, N, K, a_ok, b_ok, 4, pack_bytes, pk);
   const lasg::SgemmPlan plan =
       lasg::plan_sgemm(M, N, K, cus, ft, fs, ws_floats, pack || (a_ok && b_ok));
-  if (plan_padding(M, N, K, plan.tile, a_ok && b_ok, pack_bytes, pk)) pack = true;
+  if (plan_padding(M, N, K, plan.tile, a16 && b_ok, pack_bytes, pk)) pack = true;
   return plan;
 }
 
@@ -350,8 +356,8 @@ int sgemm(int M, int N, int K, float alpha, const float* A, int lda, const float
     Packing pk;
     bool pack = false;
     const lasg::SgemmPlan plan =
-        decide_sgemm(M, N, K, sgemm_a_ok(A, lda), sgemm_b_ok(B, ldb, N), g_cus.load(),
-                     g_ws.floats, g_ws.pack_bytes, pk, pack);
+        decide_sgemm(M, N, K, sgemm_a_rows16(A, lda), sgemm_a_ok(A, lda), sgemm_b_ok(B, ldb, N),
+                     g_cus.load(), g_ws.floats, g_ws.pack_bytes, pk, pack);
     if (plan.splits > 1 || pack) {
       return with_workspace(stream, [&](float* ws, void* pbuf) {
         lasg::SgemmCall cc = c;
@@ -472,8 +478,8 @@ int gemm_debug_pick_config(int op, int M, int N, int K, int cus, int* tile, int*
     Packing pk;
     bool pack = false;
     const lasg::SgemmPlan p =
-        decide_sgemm(M, N, K, K % 4 == 0, N % 4 == 0, cus, lasg::kWorkspaceBytes / sizeof(float),
-                     lasg::kPackBytes, pk, pack);
+        decide_sgemm(M, N, K, K % 4 == 0, (int64_t)K * 256 * 4 < (int64_t(1) << 31), N % 4 == 0,
+                     cus, lasg::kWorkspaceBytes / sizeof(float), lasg::kPackBytes, pk, pack);
     *tile = p.tile;
     *splits = p.splits;
     return GEMM_STATUS_SUCCESS;

@@ -355,7 +355,9 @@ __global__ void __launch_bounds__(256) sgemm_scale_kernel(int M, int N, float be
 // made deeper).  Each copy instruction chooses the global chunk of every LDS
 // slot, which sets the layout:
 //  * A: 64-byte rows (one row of a 16-wide K tile), the four 16-byte chunks of
-//    row r permuted by row64_swizzle(r); one instruction copies 16 whole rows.
+//    row r permuted by row64_swizzle(r); one instruction copies 16 whole rows
+//    (A_DW: rows of A only 4-byte aligned, lda not a multiple of 4: 4-byte
+//    copies, one instruction per 4 rows, the same LDS layout).
 //    A fragment read (chunk 2 g + l / 32 of 32 consecutive rows) is then free
 //    of bank conflicts.
 //  * B: one instruction per 1 KiB of rows of the tile (one row of BN = 256
@@ -364,10 +366,13 @@ __global__ void __launch_bounds__(256) sgemm_scale_kernel(int M, int N, float be
 //    different halves of the 64 banks.
 // ---------------------------------------------------------------------------
 template <int BM_, int BN_, int STAGES_, int WAVES_PER_SIMD_ = 1, int WAVES_M_ = 2,
-          int WAVES_N_ = 2>
+          int WAVES_N_ = 2, bool A_DW_ = false>
 struct SDmaTile {
   using MF = MfmaF32x32;
   static constexpr int BM = BM_, BN = BN_, BK = 16, STAGES = STAGES_;
+  static constexpr bool A_DW = A_DW_;
+  // The same tile copying A with 4-byte copies.
+  using WithADw = SDmaTile<BM_, BN_, STAGES_, WAVES_PER_SIMD_, WAVES_M_, WAVES_N_, true>;
   static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M * WAVES_N;
   static constexpr int WG_PER_CU = WAVES_PER_SIMD * 4 / WAVES;
@@ -382,7 +387,8 @@ struct SDmaTile {
   static constexpr int B_SLOT = 1024 + 32 * B_RPC;
   static constexpr int B_BYTES = (BK / B_RPC) * B_SLOT;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int A_INSTR = A_BYTES / 1024;       // 16 rows per copy
+  static constexpr int A_COPY = A_DW ? 256 : 1024;      // bytes of A per copy instruction
+  static constexpr int A_INSTR = A_BYTES / A_COPY;       // 4 or 16 rows per copy
   static constexpr int B_INSTR = BK / B_RPC;
   static constexpr int A_PER_WAVE = A_INSTR / WAVES;
   static constexpr int B_PER_WAVE = B_INSTR / WAVES;
@@ -417,10 +423,20 @@ struct SDmaPlan {
 #pragma unroll
     for (int v = 0; v < T::LOADS_PER_TILE; ++v) {
       if (v < T::A_PER_WAVE) {
-        const int r = (wave * T::A_PER_WAVE + v) * 16 + lane / 4;
-        const int chunk = (lane % 4) ^ row64_swizzle(r);
-        const int rc = m0 + r < p.M ? r : p.M - 1 - m0;
-        off[v] = (uint32_t)(((size_t)rc * p.lda + 4 * chunk) * 4);
+        if constexpr (T::A_DW) {
+          // lane l fills byte 4 (l % 16) of row l / 16 of the copy: position
+          // (l % 16) / 4, element l % 4, so it reads that element of the chunk
+          // the permutation puts there.
+          const int r = (wave * T::A_PER_WAVE + v) * 4 + lane / 16;
+          const int chunk = ((lane % 16) / 4) ^ row64_swizzle(r);
+          const int rc = m0 + r < p.M ? r : p.M - 1 - m0;
+          off[v] = (uint32_t)(((size_t)rc * p.lda + 4 * chunk + lane % 4) * 4);
+        } else {
+          const int r = (wave * T::A_PER_WAVE + v) * 16 + lane / 4;
+          const int chunk = (lane % 4) ^ row64_swizzle(r);
+          const int rc = m0 + r < p.M ? r : p.M - 1 - m0;
+          off[v] = (uint32_t)(((size_t)rc * p.lda + 4 * chunk) * 4);
+        }
       } else {
         const int copy = wave * T::B_PER_WAVE + (v - T::A_PER_WAVE);
         const int kr = copy * T::B_RPC + lane / (T::BN / 4);
@@ -431,7 +447,7 @@ struct SDmaPlan {
     }
   }
   static __device__ __forceinline__ uint32_t slot(int v, int wave) {
-    if (v < T::A_PER_WAVE) return (wave * T::A_PER_WAVE + v) * 1024;
+    if (v < T::A_PER_WAVE) return (wave * T::A_PER_WAVE + v) * T::A_COPY;
     return T::A_BYTES + (wave * T::B_PER_WAVE + (v - T::A_PER_WAVE)) * T::B_SLOT;
   }
 };
@@ -442,7 +458,10 @@ __device__ __forceinline__ void sdma_issue(const SgemmArgs& p, const SDmaPlan<T>
                                            uint32_t stage, int wave, int x) {
   const float* base = x < T::A_PER_WAVE ? a_tile + kt * T::BK
                                         : b_tile + (size_t)kt * T::BK * p.ldb;
-  dma16_sbase(base, plan.off[x], stage + SDmaPlan<T>::slot(x, wave));
+  if (T::A_DW && x < T::A_PER_WAVE)
+    dma4_sbase(base, plan.off[x], stage + SDmaPlan<T>::slot(x, wave));
+  else
+    dma16_sbase(base, plan.off[x], stage + SDmaPlan<T>::slot(x, wave));
 }
 
 // Fragments of one group of 8 k (four MFMA steps): a[i] holds A[row][8 g + 4 h
@@ -510,7 +529,11 @@ __device__ __forceinline__ void sdma_tile(const SgemmArgs& p, f32x16 (&acc)[T::F
   constexpr int NR = T::FM + 4 * T::FN;            // LDS reads per group
   constexpr int PRE = 2;
   constexpr int R0 = (NR + NM - PRE - 1) / (NM - PRE);
-  constexpr int TAIL = NM - T::LOADS_PER_TILE;
+  // The copies go out one per MFMA at the end of group 1 -- or, where a wave
+  // has too many of them for that (the 64x64 tile copying A 4 bytes at a
+  // time), all together after group 1's MFMAs (BURST).
+  constexpr bool BURST = !(NM - T::LOADS_PER_TILE >= NR / 2 && NM - T::LOADS_PER_TILE >= 1);
+  constexpr int TAIL = BURST ? NM : NM - T::LOADS_PER_TILE;
   constexpr int R1 = (NR + TAIL - 1) / TAIL;
   static_assert(TAIL >= NR / 2 && TAIL >= 1, "enough MFMAs to spread the reads over");
   smfma<T>(acc, x0, 0);
@@ -545,10 +568,16 @@ __device__ __forceinline__ void sdma_tile(const SgemmArgs& p, f32x16 (&acc)[T::F
     __builtin_amdgcn_sched_group_barrier(0x100, R1, 1);
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (BURST) {
 #pragma unroll
-  for (int x = 0; x < T::LOADS_PER_TILE; ++x) {
-    smfma<T>(acc, x1, TAIL + x);
-    if (issue) sdma_issue<T>(p, plan, a_tile, b_tile, kt_issue, st_issue, wave, x);
+    for (int x = 0; x < T::LOADS_PER_TILE; ++x)
+      if (issue) sdma_issue<T>(p, plan, a_tile, b_tile, kt_issue, st_issue, wave, x);
+  } else {
+#pragma unroll
+    for (int x = 0; x < T::LOADS_PER_TILE; ++x) {
+      smfma<T>(acc, x1, TAIL + x);
+      if (issue) sdma_issue<T>(p, plan, a_tile, b_tile, kt_issue, st_issue, wave, x);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -813,14 +842,18 @@ static hipError_t launch_tile(const SgemmCall& c, const SgemmPlan& plan, int gro
   return hipGetLastError();
 }
 
-// The direct-to-LDS kernels copy 16-byte chunks: rows of A and B must start on
-// 16-byte boundaries and each row of B must be readable in whole chunks up to
-// N (nb a multiple of 4); the per-lane copy offsets are 32-bit.  Whole tiles
-// with K a multiple of 32 run the unchecked instantiation.
+// The direct-to-LDS kernels copy 16-byte chunks of B, so rows of B must start
+// on 16-byte boundaries and each row of B must be readable in whole chunks up
+// to N (nb a multiple of 4); A is copied in 16-byte chunks where its rows start
+// on 16-byte boundaries, else 4 bytes at a time (rows of A on 4-byte
+// boundaries).  The per-lane copy offsets are 32-bit.  Whole tiles with K a
+// multiple of 32 run the unchecked instantiation.
+static bool a_rows16(const SgemmCall& c) { return c.lda % 4 == 0 && aligned16(c.A); }
 static bool direct_operands_ok(const SgemmCall& c) {
   const int nb = readable_cols(c.nb, c.N);
-  return c.lda % 4 == 0 && c.ldb % 4 == 0 && nb % 4 == 0 && nb >= c.N && nb <= c.ldb &&
-         aligned16(c.A) && aligned16(c.B) && (int64_t)c.lda * 256 * 4 < (int64_t(1) << 31) &&
+  return (reinterpret_cast<uintptr_t>(c.A) & 3u) == 0 && c.ldb % 4 == 0 && nb % 4 == 0 &&
+         nb >= c.N && nb <= c.ldb && aligned16(c.B) &&
+         (int64_t)c.lda * 256 * 4 < (int64_t(1) << 31) &&
          (int64_t)c.ldb * 16 * 4 < (int64_t(1) << 31);
 }
 
@@ -851,8 +884,8 @@ static hipError_t launch_sdma_kernel(const SgemmCall& c, const SgemmPlan& plan, 
 }
 
 template <class T>
-static hipError_t launch_sdma(const SgemmCall& c, const SgemmPlan& plan, int group_m, float* ws,
-                              hipStream_t s) {
+static hipError_t launch_sdma_as(const SgemmCall& c, const SgemmPlan& plan, int group_m,
+                                 float* ws, hipStream_t s) {
   if (!sdma_fits<T>(c)) return hipErrorInvalidValue;
   if (plan.splits > 1 && (ws == nullptr || plan.k_chunk % (2 * T::BK) != 0))
     return hipErrorInvalidValue;
@@ -871,9 +904,17 @@ static hipError_t launch_sdma(const SgemmCall& c, const SgemmPlan& plan, int gro
   return launch_sdma_kernel<T, true>(c, plan, p, ws, s);
 }
 
+// Tile T, copying A 4 bytes at a time where its rows are not 16-byte aligned.
+template <class T>
+static hipError_t launch_sdma(const SgemmCall& c, const SgemmPlan& plan, int group_m, float* ws,
+                              hipStream_t s) {
+  if (a_rows16(c)) return launch_sdma_as<T>(c, plan, group_m, ws, s);
+  return launch_sdma_as<typename T::WithADw>(c, plan, group_m, ws, s);
+}
+
 int sgemm_resolve_tile(int tile, int M, int N, int K, int splits, bool operands_ok) {
-  // The direct-to-LDS kernels need rows of A and B on 16-byte boundaries and B
-  // readable in whole 4-float chunks (any M, N and K otherwise: ragged edges and
+  // The direct-to-LDS kernels need rows of B on 16-byte boundaries (A on 4-byte
+  // ones) and B readable in whole 4-float chunks (any M, N and K otherwise: ragged edges and
   // a ragged K run a bounds-checked instantiation); otherwise the
   // register-staged 128 x 256 kernel (the best of those for large outputs) runs,
   // or for the 64 x 64 tile its register-staged twin.

@@ -117,11 +117,15 @@ def test_exact_small_integers(tile, forced):
     Ci = torch.randint(-9, 10, (M, N), generator=g)
     want = (2 * (Ai.long() @ Bi.long()) - 3 * Ci.long()).float()
     note("sgemm direct-to-LDS edge small integers tile %d" % tile)
-    # lda = 77 is not a multiple of 4: pad A to 80 columns so the direct path runs
+    # lda = 80: rows of A on 16-byte boundaries, copied 16 bytes at a time
     Ap = torch.zeros((M, 80))
     Ap[:, :K] = Ai.float()
     got = run_sgemm(M, N, K, 2.0, Ap, 80, Bi.float(), N, -3.0, Ci.float(), N).cpu()
     assert torch.equal(got, want), "small-integer products must be exact on ragged tiles"
+    # lda = 77: rows of A only 4-byte aligned, copied 4 bytes at a time into the same layout
+    got = run_sgemm(M, N, K, 2.0, Ai.float().contiguous(), K, Bi.float(), N, -3.0, Ci.float(),
+                    N).cpu()
+    assert torch.equal(got, want), "4-byte copies of A must give the same exact result"
 
 
 @pytest.mark.parametrize("tile", DMA_TILES)
@@ -146,9 +150,31 @@ def test_guard_bands_untouched(tile, forced):
     assert err <= FP32_TOL, (err, where)
 
 
+@pytest.mark.parametrize("tile", DMA_TILES)
+@pytest.mark.parametrize("shape", [(300, 520, 101), (513, 260, 777), (256, 256, 255), (64, 128, 33)])
+def test_four_byte_copies_of_a(tile, shape, forced):
+    """lda not a multiple of 4 and A's base 4 bytes past a 16-byte boundary: the
+    direct-to-LDS tile copies A 4 bytes at a time, with no packing."""
+    force(tile)
+    M, N, K = shape
+    lda = K if K % 4 else K + 1
+    A, B, C = inputs.sgemm_inputs(M, N, K, 1010 + tile + M, lda=lda, ldc=N + 2)
+    ldc = C.shape[1]
+    buf = torch.zeros(M * lda + 1)
+    buf[1:] = A.reshape(-1)
+    dbuf, dB, dC = buf.cuda(), B.cuda(), C.cuda()
+    note("sgemm direct-to-LDS 4-byte A copies tile %d M=%d N=%d K=%d lda=%d" % (tile, M, N, K, lda))
+    lib.sgemm(M, N, K, 0.75, dbuf.data_ptr() + 4, lda, dB, N, 0.5, dC, ldc)
+    torch.cuda.synchronize()
+    err, where = sgemm_error(M, N, K, 0.75, A, lda, B, N, 0.5, C, ldc, dC)
+    assert err <= FP32_TOL, (err, where)
+    assert torch.isnan(dC.cpu()[:, N:]).all(), "wrote outside the N columns"
+
+
 def test_unaligned_operands_are_packed(forced):
-    """N not a multiple of 4, or lda not a multiple of 4: the operand is copied into the
-    library's pack buffer with 16-byte rows and the direct-to-LDS tile reads the copy."""
+    """N not a multiple of 4: B is copied into the library's pack buffer with 16-byte
+    rows and the direct-to-LDS tile reads the copy; lda not a multiple of 4: A is read
+    4 bytes at a time."""
     force(9)
     assert lib.gemm_debug_pick_config(0, 600, 1026, 1000, 256) == (9, 1)
     check(600, 1026, 1000, 1.0, 0.5, seed=971, label="N = 1026")
