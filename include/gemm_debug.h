@@ -24,7 +24,8 @@ extern "C" {
  * time; ragged M, N or K run their bounds-checked instantiation), 9 = tile 7 with eight waves, 10 = 128 x 128 direct-to-LDS
  * tiles at two workgroups per compute unit, 11 = 64 x 64 direct-to-LDS tiles
  * at up to four workgroups per compute unit (tile 2 where the operands do not
- * allow direct copies); the
+ * allow direct copies), 12 = 32 x 32 tiles built from 16 x 16 x 4 MFMA blocks
+ * with a K step of 32 (small outputs); the
  * half products also have 3 = 256 x 256 and 4 = 128 x 256 direct-to-LDS kernels
  * 5 = the 256 x 256 one with a five-stage pipeline, 6 = the 256 x 256 one
  * with eight waves and 7 = tile 6 on the columns that fill whole rounds of

@@ -150,7 +150,7 @@ bool plan_packing(int M, int N, int K, bool a_ok, bool b_ok, size_t elem, size_t
 // zeros to every sum.  Same cost test as the plain copies, on the padded bytes.
 bool plan_padding(int M, int N, int K, int tile, bool operands_aligned, size_t cap_bytes,
                   Packing& pk) {
-  if (tile < 0 || tile > 6) return false;
+  if (tile < 0 || (tile > 6 && tile != 12)) return false;   // the register-staged tiles
   const int bm = lasg::sgemm_tile_bm(tile), bn = lasg::sgemm_tile_bn(tile);
   const int bk = lasg::sgemm_tile_bk(tile);
   if (operands_aligned && M % bm == 0 && N % bn == 0 && K % bk == 0) return false;

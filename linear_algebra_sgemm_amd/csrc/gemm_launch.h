@@ -53,7 +53,8 @@ inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 // (rows of A and B 16-byte aligned and B readable in whole 4-float chunks, else
 // tile 4); 9 = tile 7 with eight waves, two per SIMD; 10 = 128x128 with
 // direct-to-LDS copies at two workgroups per CU; 11 = 64x64 with direct-to-LDS
-// copies at up to four workgroups per CU (else tile 2).
+// copies at up to four workgroups per CU (else tile 2); 12 = 32x32
+// register-staged from 16x16x4 MFMA blocks, K step 32 (small outputs).
 // HGEMM: 0 = 256x256, 1 = 128x128, 2 = 64x64 (register-staged, K step 64),
 // 3 = 256x256 direct-to-LDS, 4 stages of K step 32, 4 = 128x256 direct-to-LDS,
 // 3 stages, two workgroups per CU, 5 = 256x256 direct-to-LDS, 5 stages, 6 = 256x256
@@ -62,20 +63,21 @@ inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 // rows of A and B 16-byte aligned and B readable in whole 8-half chunks, 7 also
 // whole tiles; other operands fall back to 0); 8 = 128x128 direct-to-LDS, 4
 // stages, two workgroups per CU (other operands fall back to 1).
-constexpr int kSgemmTileCount = 12;
+constexpr int kSgemmTileCount = 13;
 constexpr int kHgemmTileCount = 9;
 
 // K granularity of each SGEMM tile configuration: the K step, or for the
-// direct-to-LDS tiles (7-10) their two-tile loop body (checked against the kernels).
+// direct-to-LDS tiles (7-11) their two-tile loop body (checked against the kernels).
 constexpr int sgemm_tile_bk(int tile) { return tile == 3 || tile >= 7 ? 32 : 16; }
 // Output tile of each SGEMM configuration.
 constexpr int sgemm_tile_bm(int tile) {
   return tile == 0 || tile == 3 || tile == 5 || tile == 7 || tile == 9 ? 256
          : tile == 2 || tile == 11                                      ? 64
+         : tile == 12                                                   ? 32
                                                                         : 128;
 }
 constexpr int sgemm_tile_bn(int tile) {
-  return tile == 1 || tile == 10 ? 128 : tile == 2 || tile == 11 ? 64 : 256;
+  return tile == 1 || tile == 10 ? 128 : tile == 2 || tile == 11 ? 64 : tile == 12 ? 32 : 256;
 }
 
 // Split-K: at most this many K chunks per output tile.

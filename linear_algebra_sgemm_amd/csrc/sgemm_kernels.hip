@@ -748,6 +748,9 @@ __global__ void __launch_bounds__(256) sgemm_splitk_reduce_kernel(int M, int N, 
 using TileLarge = SgemmTile<256, 256, 16, 2, 2>;     // 4 waves, 128 x 128 each, 1 wave/SIMD
 using TileMedium = SgemmTile<128, 128, 16, 2, 2>;    // 4 waves, 64 x 64 each
 using TileSmall = SgemmTile<64, 64, 16, 2, 2>;       // 4 waves, 32 x 32 each
+// 32 x 32 from 16x16x4 MFMA blocks, 4 waves of 16 x 16, K step 32: small outputs,
+// where the per-wave MFMA chain (K / 4 blocks) sets the time.
+using TileTiny = SgemmTile<32, 32, 32, 2, 2, 2, MfmaF16x16>;
 using TileLargeK32 = SgemmTile<256, 256, 32, 2, 2>;  // as TileLarge, half the barriers
 using TileTall = SgemmTile<128, 256, 16, 2, 2, 2>;   // 4 waves, 64 x 128 each, 2 workgroups/CU
 // The same two shapes built from 16x16x4 MFMA blocks.
@@ -770,6 +773,8 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 static_assert(TileLarge::BK == sgemm_tile_bk(0) && TileMedium::BK == sgemm_tile_bk(1) &&
                   TileSmall::BK == sgemm_tile_bk(2) && TileLargeK32::BK == sgemm_tile_bk(3) &&
+                  TileTiny::BK == sgemm_tile_bk(12) && TileTiny::BM == sgemm_tile_bm(12) &&
+                  TileTiny::BN == sgemm_tile_bn(12) &&
                   TileTall::BK == sgemm_tile_bk(4) && TileLarge16::BK == sgemm_tile_bk(5) &&
                   TileTall16::BK == sgemm_tile_bk(6) && TileLarge16::BM == sgemm_tile_bm(5) &&
                   TileLarge16::BN == sgemm_tile_bn(5) && TileTall16::BM == sgemm_tile_bm(6) &&
@@ -919,7 +924,7 @@ int sgemm_resolve_tile(int tile, int M, int N, int K, int splits, bool operands_
   // register-staged 128 x 256 kernel (the best of those for large outputs) runs,
   // or for the 64 x 64 tile its register-staged twin.
   (void)M; (void)N; (void)K; (void)splits;
-  if (tile >= 7 && !operands_ok) return tile == 11 ? 2 : 4;
+  if (tile >= 7 && tile <= 11 && !operands_ok) return tile == 11 ? 2 : 4;
   return tile;
 }
 
@@ -938,6 +943,7 @@ hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hi
     case 9: return launch_sdma<SDmaEight>(c, plan, 4, ws, s);
     case 10: return launch_sdma<SDmaSmall>(c, plan, 8, ws, s);
     case 11: return launch_sdma<SDmaMini>(c, plan, 8, ws, s);
+    case 12: return launch_tile<TileTiny>(c, plan, 8, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -153,9 +153,12 @@ def test_config_rule(so):
         (0, 4096, 4096, 4002, 256, (9, 1)),   # lda = 4002: A packed to 16-byte rows first
         (0, 4096, 4090, 4096, 256, (9, 1)),   # N not a multiple of 4: B packed first
         (0, 64, 4090, 64, 256, (2, 1)),       # packing B would cost more than it saves
-        (0, 256, 256, 256, 256, (11, 1)),     # 64x64 direct-to-LDS; K < 1024: no split
-        (0, 256, 256, 1024, 256, (11, 2)),    # 16 tiles; chunks of at least 512
-        (0, 512, 512, 512, 256, (11, 1)),     # 64 tiles, K < 1024
+        (0, 256, 256, 256, 256, (12, 1)),     # 16 tiles of 64x64: the 32x32 tile, unsplit
+        (0, 256, 256, 1024, 256, (12, 1)),
+        (0, 512, 512, 512, 256, (12, 1)),     # 64 tiles of 64x64
+        (0, 512, 512, 480, 256, (12, 1)),
+        (0, 512, 512, 500, 256, (11, 1)),     # K not a multiple of 32: 64x64 direct-to-LDS
+        (0, 512, 576, 512, 256, (11, 1)),     # 72 tiles of 64x64
         (0, 1000, 3000, 777, 256, (11, 1)),   # 752 tiles
         (0, 2048, 2048, 2048, 256, (10, 1)),  # 64 tiles of 256x256, 256 of 128x128: direct 128x128
         (0, 2048, 2048, 8192, 256, (10, 1)),
@@ -306,7 +309,7 @@ def test_split_legality(so):
             M, N = rng.randint(1, 3000), rng.randint(1, 3000)
             K = rng.choice([1, 15, 16, 17, 100, 777, 4096, 20000])
             want = rng.choice([1, 2, 3, 5, 8, 16, 32])
-            tile = rng.choice([-1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11])
+            tile = rng.choice([-1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12])
             assert lib.gemm_debug_force_tile(0, tile) == lib.STATUS_SUCCESS
             assert lib.gemm_debug_force_splits(0, want) == lib.STATUS_SUCCESS
             t, s = pick(0, M, N, K)
@@ -364,7 +367,8 @@ def test_forced_splits(so):
 
 
 def test_force_tile_values(so):
-    assert lib.gemm_debug_force_tile(0, 12) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(0, 13) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(0, 12) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(0, 11) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(0, 9) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(1, 9) == lib.STATUS_INVALID_VALUE

@@ -188,7 +188,7 @@ def test_half_ffn_shape_with_odd_k_sampled():
 # operands are copied zero-padded to whole tiles (A to ceil(M/BM) BM rows, K to
 # a multiple of the tile's K step, B to ceil(N/BN) BN columns) and the kernel
 # runs with unchecked loads and bounds-checked stores of C.
-REG_TILES = (0, 1, 2, 3, 4, 5, 6)
+REG_TILES = (0, 1, 2, 3, 4, 5, 6, 12)
 
 
 @pytest.mark.parametrize("tile", REG_TILES)

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 # 256x256, 128x128, 64x64, 256x256 (K step 32), 128x256; 5, 6: 256x256 and 128x256 with
 # 16x16x4 MFMA blocks; 7, 8: 256x256 and 128x256 with direct-to-LDS copies
-TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11)   # 9: tile 7 with eight waves; 10, 11: 128x128, 64x64 direct
+TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12)   # 9: tile 7 with eight waves; 10, 11: 128x128, 64x64 direct; 12: 32x32
 
 
 @pytest.fixture(scope="module", autouse=True)

@@ -15,7 +15,7 @@ from tests.gpu_helpers import FP32_TOL, note, run_sgemm, sgemm_error
 
 pytestmark = pytest.mark.gpu
 
-TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11)
+TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12)
 RESOLVED = {7: 4, 8: 4, 9: 4, 10: 4, 11: 2}   # direct-to-LDS tiles fall back to their register-staged twin off whole tiles
 
 
