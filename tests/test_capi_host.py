@@ -150,7 +150,7 @@ def test_config_rule(so):
         (0, 8192, 8192, 8192, 256, (9, 1)),
         (0, 4096, 4096, 4008, 256, (9, 1)),   # ragged K: the bounds-checked direct-to-LDS kernel
         (0, 4000, 4000, 4000, 256, (9, 1)),   # ragged M, N, K likewise
-        (0, 4096, 4096, 4002, 256, (9, 1)),   # lda = 4002: A packed to 16-byte rows first
+        (0, 4096, 4096, 4002, 256, (9, 1)),   # lda = 4002: A copied 4 bytes at a time
         (0, 4096, 4090, 4096, 256, (9, 1)),   # N not a multiple of 4: B packed first
         (0, 64, 4090, 64, 256, (2, 1)),       # packing B would cost more than it saves
         (0, 256, 256, 256, 256, (12, 1)),     # 16 tiles of 64x64: the 32x32 tile, unsplit
@@ -188,7 +188,7 @@ def test_config_rule(so):
         (1, 4096, 4096, 256, 256, (1, 1)),    # K < 512: not the 256x256 tiles
         (1, 300, 500, 4096, 256, (2, 22)),     # 40 tiles of 64x64: ~4 workgroups per CU
         (1, 1024, 1024, 4096, 256, (8, 1)),    # 64 tiles of 128x128: direct 128x128
-        (1, 1024, 1024, 4095, 256, (8, 1)),    # the same with K ragged (A packed)
+        (1, 1024, 1024, 4095, 256, (8, 1)),    # the same with K ragged (A packed: half rows)
         (1, 512, 512, 4096, 256, (2, 16)),     # 64 tiles; 16 chunks of 256
         (1, 512, 512, 256, 256, (2, 1)),       # K < 512: no split
     ]

@@ -76,12 +76,11 @@ def lda_for(K):
 def test_ragged_shapes(tile, shape, forced):
     force(tile)
     M, N, K = shape
-    # the configuration for packed operands (lda = K): with K % 4 != 0 the rows of A
-    # are packed first when that pays, else the register-staged twin runs (tile 4,
-    # or 2 for tile 11); with lda padded to a multiple of 4, as here, the
-    # direct-to-LDS tile runs for every shape
+    # the forced direct-to-LDS tile runs for every shape (rows of A with lda = K
+    # not a multiple of 4 are copied 4 bytes at a time); here lda is padded to a
+    # multiple of 4, so A is copied in 16-byte chunks
     t, s = lib.gemm_debug_pick_config(0, M, N, K, 256)
-    assert (t, s) == (tile, 1) or (K % 4 != 0 and t == (2 if tile == 11 else 4))
+    assert (t, s) == (tile, 1)
     check(M, N, K, 1.25, -0.5, seed=900 + tile + M + K, label="tile %d" % tile, lda=lda_for(K))
 
 
@@ -102,7 +101,7 @@ def test_ragged_split(tile, splits, shape, forced):
     force(tile, splits)
     M, N, K = shape
     t, s = lib.gemm_debug_pick_config(0, M, N, K, 256)
-    assert t in (tile, 2 if tile == 11 else 4) and 1 <= s <= splits
+    assert t == tile and 1 <= s <= splits
     check(M, N, K, 0.75, 0.25, seed=940 + tile + splits, label="tile %d x%d" % (tile, s),
           lda=lda_for(K))
 
