@@ -44,7 +44,8 @@ int gemm_debug_force_tile(int op, int tile);
  * Force the number of K chunks (split-K) of later calls: op 0 = sgemm, op 1 =
  * the half products; splits -1 = choose by shape (the default), 1 = never
  * split, 2 .. 32 = that many chunks (still reduced to what K and the workspace
- * allow; the half products split only on their register-staged tiles 0-2).
+ * allow; the half products split only on their register-staged tiles 0-2 and
+ * the 128 x 128 direct-to-LDS tile 8).
  * Returns GEMM_STATUS_INVALID_VALUE for another op or count.  Pure host state,
  * not synchronised with calls in flight on other threads.
  */

@@ -236,7 +236,9 @@ int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   // 640 vs 404 for 64x64; 1024 x 4096 x 4096: 776 vs 528 for 128x128
   // register-staged; 2048 x 2048 x 8192: 823 vs 641; 1000^3: 129 vs 68 for
   // 128x256 direct; 1024^3: 185 vs 155) -- but not once there are more
-  // (3000^3: 494 vs 642 for the eight-wave tile).
+  // (3000^3: 494 vs 642 for the eight-wave tile).  With K split (below) it also
+  // takes outputs down to 16 such tiles once K reaches 4096 (512 x 512 x 8192 in 8 chunks:
+  // 225 vs 188 for 64x64 in 16; 512 x 512 x 4096 in 4: 151 vs 137).
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
   const bool direct = operands_ok;
@@ -244,7 +246,7 @@ int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
     if (!direct) return 0;
     return K >= 2048 ? 7 : 3;
   }
-  if (direct && 4 * t_med >= cus && t_med <= 2L * cus) return 8;
+  if (direct && t_med <= 2L * cus && (4 * t_med >= cus || (K >= 4096 && t_med >= 16))) return 8;
   const int reg = t_med >= 2L * cus ? 1 : 2;
   const int bm = half_tile_bm(reg);
   const bool reg_whole = M % bm == 0 && N % bm == 0 && K % kHalfBK == 0;
@@ -253,10 +255,23 @@ int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   return reg;
 }
 
-// Built-in split rule of the half products, as for FP32: split K (register-
-// staged tiles only) when the tiles do not cover the CUs and K is at least 512,
-// aiming at four workgroups per CU with chunks of at least 128.
+// Built-in split rule of the half products, as for FP32: split K (the
+// register-staged tiles and the 128x128 direct-to-LDS tile) when the tiles do
+// not cover the CUs and K is at least 512, aiming at four workgroups per CU
+// with chunks of at least 128 on the register-staged tiles.
 int half_rule_splits(int M, int N, int K, int tile, int cus) {
+  if (tile == 8) {
+    // The 128x128 direct-to-LDS tile: split outputs of at most half as many
+    // tiles as CUs to about one workgroup per CU, in chunks of at least 512
+    // (1024 x 1024 x 4096, 64 tiles: 209 TFLOP/s unsplit, 301 in 2, 358 in 4,
+    // 293 in 8; 2048 x 1024 x 8192, 128 tiles: 453, 620 in 2, 604 in 4).
+    const long tiles = ceil_div(M, 128) * ceil_div(N, 128);
+    if (2 * tiles > cus) return 1;
+    long s = cus / tiles;
+    if (s > K / 512) s = K / 512;
+    if (s > 16) s = 16;
+    return s < 1 ? 1 : (int)s;
+  }
   if (tile > 2) return 1;
   const long tiles = ceil_div(M, half_tile_bm(tile)) * ceil_div(N, half_tile_bm(tile));
   if (tiles >= cus || K < 512) return 1;
@@ -290,11 +305,11 @@ HalfPlan plan_half(int M, int N, int K, int cus, int force_tile, int force_split
   long s = force_splits > 0 ? force_splits
            : (tuned && force_tile < 0) ? tuned_splits
                                        : half_rule_splits(M, N, K, p.tile, cus);
-  // Legality: register-staged tiles only, whole K steps per chunk, no empty
-  // chunk, partials fit the workspace.
+  // Legality: register-staged tiles and the 128x128 direct-to-LDS tile only,
+  // whole K steps per chunk, no empty chunk, partials fit the workspace.
   const long ktiles = ceil_div(K, kHalfBK);
   const long mn = (long)M * N;
-  if (p.tile > 2) s = 1;
+  if (p.tile > 2 && p.tile != 8) s = 1;
   if (s > kMaxSplits) s = kMaxSplits;
   if (s > ktiles) s = ktiles;
   if (mn > 0 && s > (long)(ws_floats / (size_t)mn)) s = (long)(ws_floats / (size_t)mn);

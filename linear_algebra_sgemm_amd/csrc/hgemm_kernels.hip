@@ -650,12 +650,22 @@ __device__ __forceinline__ void hdma_k_tail(const HgemmArgs& p, f32x16 (&acc)[T:
     }
 }
 
-template <class T, bool EDGE>
+// SPLIT: workgroup row blockIdx.y runs K chunk y (a multiple of 2 BK) and
+// writes its raw FP32 partial sums to the workspace (the split-K scheme of the
+// register-staged kernel, whose reduction kernel applies the epilogue).
+template <class T, bool EDGE, bool SPLIT = false>
 __global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(T::WAVES_PER_SIMD)))
 hgemm_dma_kernel(HgemmArgs p) {
   static_assert(T::KSTEPS % 2 == 0, "fragments ping-pong between two register sets");
   static_assert(T::LOADS_PER_TILE <= T::FM * T::FN, "one direct load per MFMA at most");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[T::STAGES * T::STAGE_BYTES];
+  if constexpr (SPLIT) {
+    const int kbeg = blockIdx.y * p.k_chunk;
+    const int klen = p.K - kbeg < p.k_chunk ? p.K - kbeg : p.k_chunk;
+    p.A += kbeg;
+    p.B += (size_t)kbeg * p.ldb;
+    p.K = klen;
+  }
 
   int tile_m, tile_n;
   tile_of_workgroup(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
@@ -721,6 +731,25 @@ hgemm_dma_kernel(HgemmArgs p) {
   }
   if constexpr (EDGE) {
     if (ktiles * T::BK < p.K) hdma_k_tail<T>(p, acc, lds, ktiles * T::BK, m0, n0, wave, wm, wn, lane);
+  }
+  if constexpr (SPLIT) {
+    // Lane l holds, for n-block j, m-block i and q = 0..3, columns 8 q + 4 (l / 32)
+    // + 0..3 of row l % 32 (as in the epilogue below).
+    float* W = p.ws + (size_t)blockIdx.y * p.M * p.N;
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) {
+          const int row = m0 + wm * T::WTM + 32 * i + lane % 32;
+          const int col = n0 + wn * T::WTN + 32 * j + 8 * q + 4 * (lane / 32);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!EDGE || (row < p.M && col + e < p.N))
+              W[(size_t)row * p.N + col + e] = acc[j][i][4 * q + e];
+        }
+    return;
   }
 
   // Epilogue.  Lane l holds, for n-block j, m-block i and q = 0..3, the four
@@ -854,6 +883,19 @@ __global__ void __launch_bounds__(256) half_splitk_reduce_kernel(int M, int N, i
   }
 }
 
+// The second kernel of a split call: the fixed-order sum of the partials and
+// the epilogue.
+template <class E>
+static hipError_t launch_half_reduce(const HgemmCall& c, int splits, const float* ws,
+                                     hipStream_t s) {
+  const int64_t total = (int64_t)c.M * c.N;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(half_splitk_reduce_kernel<E>, dim3((unsigned)blocks), dim3(256), 0, s, c.M,
+                     c.N, splits, ws, c.alpha, c.bias, c.act, c.C, c.ldc);
+  return hipGetLastError();
+}
+
 template <class T>
 static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s, int splits = 1,
                                int k_chunk = 0, float* ws = nullptr) {
@@ -882,12 +924,7 @@ static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s, i
       hipLaunchKernelGGL((hgemm_mfma_kernel<T, true, true>), grid, block, 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t total = (int64_t)c.M * c.N;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(half_splitk_reduce_kernel<typename T::E>, dim3((unsigned)blocks), dim3(256),
-                       0, s, c.M, c.N, splits, (const float*)ws, c.alpha, c.bias, c.act, c.C, c.ldc);
-    return hipGetLastError();
+    return launch_half_reduce<typename T::E>(c, splits, ws, s);
   }
   const dim3 grid(p.tiles_m * p.tiles_n), block(T::THREADS);
   if (fast)
@@ -922,7 +959,8 @@ static bool dma_whole(const HgemmCall& c) {
 }
 
 template <class T>
-static hipError_t launch_hdma(const HgemmCall& c, int group_m, hipStream_t s) {
+static hipError_t launch_hdma(const HgemmCall& c, int group_m, hipStream_t s, int splits = 1,
+                              int k_chunk = 0, float* ws = nullptr) {
   HgemmArgs p;
   p.M = c.M; p.N = c.N; p.K = c.K;
   p.alpha = c.alpha;
@@ -933,6 +971,19 @@ static hipError_t launch_hdma(const HgemmCall& c, int group_m, hipStream_t s) {
   p.tiles_n = (c.N + T::BN - 1) / T::BN;
   p.group_m = group_m;
   p.nb = readable_cols(c.nb, c.N);
+  p.k_chunk = k_chunk;
+  p.ws = ws;
+  if (splits > 1) {
+    if (ws == nullptr || k_chunk % (2 * T::BK) != 0) return hipErrorInvalidValue;
+    const dim3 grid(p.tiles_m * p.tiles_n, splits);
+    if (dma_whole<T>(c))
+      hipLaunchKernelGGL((hgemm_dma_kernel<T, false, true>), grid, dim3(T::THREADS), 0, s, p);
+    else
+      hipLaunchKernelGGL((hgemm_dma_kernel<T, true, true>), grid, dim3(T::THREADS), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_half_reduce<typename T::E>(c, splits, ws, s);
+  }
   if (dma_whole<T>(c))
     hipLaunchKernelGGL((hgemm_dma_kernel<T, false>), dim3(p.tiles_m * p.tiles_n),
                        dim3(T::THREADS), 0, s, p);
@@ -991,8 +1042,11 @@ template <class E>
 static hipError_t launch_half(const HgemmCall& c, const HalfPlan& plan, int cus, float* ws,
                               hipStream_t s) {
   if (plan.splits > 1) {
-    if (plan.tile > 2 || ws == nullptr) return hipErrorInvalidValue;
+    if ((plan.tile > 2 && plan.tile != 8) || ws == nullptr) return hipErrorInvalidValue;
     switch (plan.tile) {
+      case 8:
+        if (!dma_fits<HDmaSquare<E>>(c)) return hipErrorInvalidValue;
+        return launch_hdma<HDmaSquare<E>>(c, 8, s, plan.splits, plan.k_chunk, ws);
       case 0: return launch_htile<HTileLarge<E>>(c, 4, s, plan.splits, plan.k_chunk, ws);
       case 1: return launch_htile<HTileMedium<E>>(c, 8, s, plan.splits, plan.k_chunk, ws);
       default: return launch_htile<HTileSmall<E>>(c, 8, s, plan.splits, plan.k_chunk, ws);

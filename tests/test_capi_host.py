@@ -187,9 +187,11 @@ def test_config_rule(so):
         (1, 4096, 2048, 4096, 256, (8, 1)),   # 512 tiles of 128x128: one round at two per CU
         (1, 4096, 4096, 256, 256, (1, 1)),    # K < 512: not the 256x256 tiles
         (1, 300, 500, 4096, 256, (2, 22)),     # 40 tiles of 64x64: ~4 workgroups per CU
-        (1, 1024, 1024, 4096, 256, (8, 1)),    # 64 tiles of 128x128: direct 128x128
-        (1, 1024, 1024, 4095, 256, (8, 1)),    # the same with K ragged (A packed: half rows)
-        (1, 512, 512, 4096, 256, (2, 16)),     # 64 tiles; 16 chunks of 256
+        (1, 1024, 1024, 4096, 256, (8, 4)),    # 64 tiles of 128x128: direct 128x128 in 4 chunks
+        (1, 1024, 1024, 4095, 256, (8, 4)),    # the same with K ragged (A packed: half rows)
+        (1, 2048, 1024, 8192, 256, (8, 2)),    # 128 tiles: 2 chunks
+        (1, 512, 512, 4096, 256, (8, 8)),      # 16 tiles of 128x128, K >= 4096: 8 chunks of 512
+        (1, 512, 512, 2048, 256, (2, 16)),     # 64 tiles of 64x64; 16 chunks of 128
         (1, 512, 512, 256, 256, (2, 1)),       # K < 512: no split
     ]
     assert lib.gemm_debug_use_tuned_table(False) == lib.STATUS_SUCCESS

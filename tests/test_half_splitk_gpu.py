@@ -74,6 +74,21 @@ def test_forced_splits(fmt, tile, splits, shape, forced):
 
 
 @pytest.mark.parametrize("fmt", list(FMTS))
+@pytest.mark.parametrize("splits", [2, 7, 32])
+@pytest.mark.parametrize("shape", [(256, 256, 1024), (300, 264, 1000), (128, 640, 2048),
+                                   (1000, 520, 2000), (129, 136, 776)])
+def test_forced_splits_direct_tile(fmt, splits, shape, forced):
+    """The 128x128 direct-to-LDS tile with K split: whole and ragged tiles, K chunks
+    of whole 64-wide steps, the last chunk ragged (its bounds-checked tail step)."""
+    force(8, splits)
+    M, N, K = shape
+    t, s = lib.gemm_debug_pick_config(1, M, N, K, 256)
+    assert t == 8 and 1 <= s <= splits
+    check(fmt, M, N, K, 0.75, lib.ACT_GELU_TANH, seed=760 + splits + M,
+          label="tile 8 x%d" % s)
+
+
+@pytest.mark.parametrize("fmt", list(FMTS))
 def test_epilogue_options_and_padded_ldc(fmt, forced):
     force(2, 6)
     check(fmt, 200, 136, 768, 0.5, lib.ACT_NONE, seed=711, with_bias=False, ldc=141,
