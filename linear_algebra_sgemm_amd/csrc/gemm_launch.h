@@ -50,8 +50,8 @@ inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 // 32x32x2 MFMA blocks); 5 = 256x256 and 6 = 128x256 at two
 // workgroups per CU, both with 16x16x4 MFMA blocks; 7 = 256x256 and 8 = 128x256
 // at two workgroups per CU with direct-to-LDS copies into a multi-stage ring
-// (rows of A and B 16-byte aligned and B readable in whole 4-float chunks, else
-// tile 4); 9 = tile 7 with eight waves, two per SIMD; 10 = 128x128 with
+// (rows of B 16-byte aligned and B readable in whole 4-float chunks, rows of A
+// 4-byte aligned, else tile 4); 9 = tile 7 with eight waves, two per SIMD; 10 = 128x128 with
 // direct-to-LDS copies at two workgroups per CU; 11 = 64x64 with direct-to-LDS
 // copies at up to four workgroups per CU (else tile 2); 12 = 32x32
 // register-staged from 16x16x4 MFMA blocks, K step 32 (small outputs).
@@ -66,8 +66,9 @@ inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 constexpr int kSgemmTileCount = 13;
 constexpr int kHgemmTileCount = 9;
 
-// K granularity of each SGEMM tile configuration: the K step, or for the
-// direct-to-LDS tiles (7-11) their two-tile loop body (checked against the kernels).
+// K granularity of each SGEMM tile configuration: the K step (32 for tiles 3
+// and 12), or for the direct-to-LDS tiles (7-11) their two-tile loop body
+// (checked against the kernels).
 constexpr int sgemm_tile_bk(int tile) { return tile == 3 || tile >= 7 ? 32 : 16; }
 // Output tile of each SGEMM configuration.
 constexpr int sgemm_tile_bm(int tile) {
