@@ -43,6 +43,9 @@ int size_class(int x) {
 
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
+// Share of the tiles' rows (or columns) that fall inside a dimension of size x.
+double fill(long x, long tile) { return (double)x / (double)(ceil_div(x, tile) * tile); }
+
 // K chunks of the one-per-CU direct-to-LDS tiles when their tiles do not
 // cover the CUs: as many as keep every chunk in one round (at most 16), with
 // chunks of at least 384 (shorter ones lose to the fixed cost of a workgroup,
@@ -68,23 +71,34 @@ long round_use(long tiles, int cus, int per_cu) {
 
 // Built-in tile rule, measured on MI355X (the size sweep over powers of two and
 // a sweep of ragged shapes):
-//  * The direct-to-LDS kernels wherever their copies are legal (rows of A and B
-//    16-byte aligned, B readable in whole 4-float chunks: `operands_ok`, which
-//    holds after packing too) and their 256x256 tiles cover the CUs:
+//  * The direct-to-LDS kernels wherever their copies are legal (rows of B
+//    16-byte aligned and readable in whole 4-float chunks, rows of A 4-byte
+//    aligned: `operands_ok`, which holds after packing too) and their 256x256
+//    tiles cover the CUs:
 //    eight waves of 256x256 (4096^3: 146 TFLOP/s, 8192^3: 149; ragged 4000^3:
 //    138 vs 111 for the best register-staged tile), or 128x256 at two per CU
 //    when that wastes less of the last round (6000^3: 116 vs 104; 7000 x 3000 x
 //    2000: 109 vs 89) — weighed by their full-round rates, 89 vs 93 % of peak.
 //    On a ragged shape K must reach 384 (5000 x 5000 x 333: 64 vs 74 for 64x64).
 //  * Fewer 256x256 tiles than CUs: the 128x128 direct-to-LDS tile, unsplit
-//    once its tiles give every CU one and use at least 75 % of the last round
-//    of slots, two per CU (2048^3: 130 vs 114 for the split 256x256 tile;
+//    once its tiles give every CU one and use at least 80 % of the last round
+//    of slots, two per CU (3000^3, 576 tiles, 75 %: 100 vs 120 for 64x64;
+//    2048^3: 130 vs 114 for the split 256x256 tile;
 //    4096 x 2048 x 2048: 139 vs 125 for register-staged 128x128; 2800^3: 128 vs
 //    124; but 1536 x 3072 x 2048, 288 tiles in 512 slots: 80 vs 108 for 64x64),
 //    else with K split so that one round uses at least 70 % of the CUs, in two
 //    or more chunks of at least 384 (1024 x 1024 x 8192: 123 vs 117 for the
 //    256x256 tile in 16 chunks; 1024 x 2048 x 4096: 121 vs 116), as long as
-//    there are 32 tiles (512 x 512 x 8192 keeps 64x64 in 16 chunks: 82 vs 59).
+//    there are 32 tiles (512 x 512 x 8192 keeps 64x64 in 16 chunks: 82 vs 59);
+//    but with K >= 4096 the 256x256 tile in chunks of at least 768 where that
+//    fills a tenth of the CUs more (1280 x 1280 x 8192 in 10 chunks: 124 vs
+//    103 for 128x128 in 2; 1024 x 1024 x 8192 keeps 128x128 in 4, the 256x256
+//    tile's 16 chunks being 512 long).
+//    Not where 128-wide tiles leave a much larger part of the last tile row or
+//    column empty than 64-wide ones (777 x 7777 x 777: 76 vs 86 for 64x64).
+//    Where neither applies and K >= 4096, the eight-wave 256x256 tile with K
+//    split the same way when a round then uses 70 % of the CUs (1536 x 1536 x
+//    6144 in 7 chunks: 126 vs 102 for 64x64).
 //  * Else the register-staged 128x256 tile at two per CU, then 128x128, where
 //    their tiles give every CU two (4096^3: 134 vs 130 for 256x256) — on shapes
 //    the direct-to-LDS kernel takes, only where they are whole (their
@@ -109,10 +123,23 @@ int sgemm_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
     if (t_large >= cus)
       return 89 * round_use(t_tall, cus, 2) > 93 * round_use(t_large, cus, 1) ? 8 : 9;
     if (t_med >= cus) {
-      if (round_use(t_med, cus, 2) >= 75) return 10;
+      // (not where the 128-row or -column tiles leave much more of the last
+      // tile row or column empty than 64-wide ones would)
+      const double fill128 = fill(M, 128) * fill(N, 128), fill64 = fill(M, 64) * fill(N, 64);
+      if (round_use(t_med, cus, 2) >= 80 && fill128 >= 0.95 * fill64) return 10;
     } else {
       const long s = direct_splits(t_med, K, cus);
+      // The 256x256 tile in K chunks instead, where its chunks stay long and it
+      // fills clearly more of the CUs.
+      const long s9 = direct_splits(t_large, K, cus);
+      if (K >= 4096 && s9 >= 2 && K / s9 >= 768 && 10 * t_large * s9 >= 10 * t_med * s + cus &&
+          10 * t_large * s9 >= 7L * cus)
+        return 9;
       if (t_med >= 32 && s >= 2 && 10 * t_med * s >= 7L * cus) return 10;
+    }
+    if (K >= 4096) {
+      const long s = direct_splits(t_large, K, cus);
+      if (s >= 2 && 10 * t_large * s >= 7L * cus) return 9;
     }
   }
   // (on shapes the direct-to-LDS kernel can take, only where these tiles are whole)

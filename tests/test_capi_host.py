@@ -170,6 +170,12 @@ def test_config_rule(so):
         (0, 1024, 3072, 768, 256, (11, 1)),   # 192 tiles of 128x128 would need a split of 1
         (0, 1536, 3072, 2048, 256, (11, 1)),  # 288 tiles of 128x128 fill 56 % of 512 slots
         (0, 1000, 1000, 1000, 256, (11, 1)),  # 256 tiles of 64x64: no split
+        (0, 1536, 1536, 6144, 256, (9, 7)),   # 36 tiles of 256x256, long K: 7 chunks
+        (0, 777, 7777, 777, 256, (11, 1)),    # 128-row tiles leave 13 % of the last row empty
+        (0, 2800, 2800, 2800, 256, (10, 1)),
+        (0, 3000, 3000, 3000, 256, (11, 1)),  # 576 tiles of 128x128 use 75 % of 512 slots
+        (0, 1280, 1280, 8192, 256, (9, 10)),  # 100 tiles of 128x128 in 2 chunks fill 78 %
+        (0, 1792, 1792, 4096, 256, (9, 5)),
         (0, 600, 600, 5000, 256, (11, 5)),    # 100 tiles: about two workgroups per CU
         (0, 4096, 4096, 4096, 64, (9, 1)),
         (0, 128, 128, 16384, 256, (11, 16)),  # 4 tiles; 128 chunks by CUs, capped at 16

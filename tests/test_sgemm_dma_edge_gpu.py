@@ -185,7 +185,7 @@ def test_unaligned_operands_are_packed(forced):
 
 @pytest.mark.parametrize("shape,want", [((4000, 4000, 4008), (9, 1)), ((6000, 6000, 6000), (8, 1)),
                                         ((2800, 2800, 2800), (10, 1)),
-                                        ((4000, 2000, 3000), (10, 1)), ((3000, 3000, 3000), (10, 1))])
+                                        ((4000, 2000, 3000), (10, 1)), ((3000, 3000, 3000), (11, 1))])
 def test_auto_choice_large_ragged(shape, want):
     """Full-size ragged products on the configuration the library picks, checked on
     sampled outputs (the four corners, the last row and column, and uniform picks)."""
