@@ -242,43 +242,42 @@ SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_spl
 namespace {
 
 int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
-  // Built-in rule (from the size sweep): 256x256 tiles once they give every CU
-  // one and K is at least 512 -- with direct-to-LDS copies when the operands
-  // allow them (`operands_ok`: rows of A and B 16-byte aligned, B readable in
-  // whole 8-half chunks, as given or after packing): eight waves
-  // with the head/tail column split (tile 7, which runs as tile 6 where no split
-  // exists) for K >= 2048, four waves (tile 3) for shorter K, where the
-  // eight-wave tile lost up to 14 % -- else 128x128 tiles once they give every
-  // CU two, else 64x64 tiles, which spread small outputs over the most CUs.
-  // Where the copies are legal but the register-staged tile would have to run
-  // bounds-checked (ragged M, N or K), the direct-to-LDS tiles win by far at
-  // every size measured (3000^3: 652 TFLOP/s for the eight-wave tile vs 92 for
-  // the best register-staged one; 2000 x 7000 x 2000: 865 vs 136): the
-  // eight-wave 256x256 tile, or 128x256 where fewer than 64 256x256 tiles exist
-  // and K is below 2048 (1000^3: 68 vs 65; 1000 x 1000 x 4000: 75 vs 97) -- as
-  // long as there are 16 tiles of 128x256; below that the split 64x64 tile is
-  // ahead (504 x 504 x 8000: 33 vs 27).  Between those, where the copies are
-  // legal and the 128x128 tiles number a quarter to twice the CUs (one round
-  // at two per CU), the 128x128 direct-to-LDS tile beats them all (2048^3:
-  // 640 vs 404 for 64x64; 1024 x 4096 x 4096: 776 vs 528 for 128x128
-  // register-staged; 2048 x 2048 x 8192: 823 vs 641; 1000^3: 129 vs 68 for
-  // 128x256 direct; 1024^3: 185 vs 155) -- but not once there are more
-  // (3000^3: 494 vs 642 for the eight-wave tile).  With K split (below) it also
-  // takes outputs down to 16 such tiles once K reaches 4096 (512 x 512 x 8192 in 8 chunks:
-  // 225 vs 188 for 64x64 in 16; 512 x 512 x 4096 in 4: 151 vs 137).
+  // Built-in rule (from the size sweep).  Where the direct-to-LDS copies are
+  // legal (`operands_ok`: rows of A and B 16-byte aligned, B readable in whole
+  // 8-half chunks, as given or after packing):
+  //  * 256x256 tiles with eight waves once they give every CU one, or once the
+  //    128x128 tiles would need more than one round at two per CU (K >= 128),
+  //    with the head/tail column split (tile 7, which runs as tile 6 where no
+  //    split exists) for K >= 2048.  The eight-wave tile leads the four-wave one
+  //    at every K measured (4096^2 x 1024: 902 vs 758; x 512: 670 vs 530; 3072^3:
+  //    906 vs 758) and the register-staged tiles by far (3072^3: 906 vs 450 for
+  //    128x128; 4096^2 x 256: 443 vs 358; 3000^3: 652 vs 92).
+  //  * Between a quarter of the CUs and two per CU in 128x128 tiles (one round
+  //    at two per CU), the 128x128 direct-to-LDS tile (2048^3: 640 vs 404 for
+  //    64x64; 1024 x 4096 x 4096: 776 vs 528 for 128x128 register-staged;
+  //    2048 x 2048 x 8192: 823 vs 641; 1000^3: 129 vs 68 for 128x256 direct;
+  //    1024^3: 185 vs 155); with K split (below) it also takes outputs down to
+  //    16 such tiles once K reaches 4096 (512 x 512 x 8192 in 8 chunks: 225 vs
+  //    188 for 64x64 in 16; 512 x 512 x 4096 in 4: 151 vs 137).
+  //  * Smaller outputs: the register-staged 64x64 tile, which spreads them over
+  //    the most CUs with split-K -- unless it would run bounds-checked (ragged
+  //    M, N or K) and there are 16 tiles of 128x256: then 128x256 direct-to-LDS
+  //    (or the eight-wave 256x256 tile for K >= 2048; 504 x 504 x 8000 stays on
+  //    the split 64x64 tile: 33 vs 27).
+  // Otherwise (operands the copies cannot take) the register-staged 256x256
+  // tile where 256x256 tiles give every CU one and K >= 512, else 128x128 tiles
+  // once they give every CU two, else 64x64.
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
   const bool direct = operands_ok;
-  if (t_large >= cus && K >= 512) {
-    if (!direct) return 0;
-    return K >= 2048 ? 7 : 3;
-  }
+  if (direct && K >= 128 && (t_large >= cus || t_med > 2L * cus)) return K >= 2048 ? 7 : 6;
   if (direct && t_med <= 2L * cus && (4 * t_med >= cus || (K >= 4096 && t_med >= 16))) return 8;
+  if (!direct && t_large >= cus && K >= 512) return 0;
   const int reg = t_med >= 2L * cus ? 1 : 2;
   const int bm = half_tile_bm(reg);
   const bool reg_whole = M % bm == 0 && N % bm == 0 && K % kHalfBK == 0;
   const long t_tall = ceil_div(M, 128) * ceil_div(N, 256);
-  if (direct && !reg_whole && t_tall >= 16) return (t_large >= 64 || K >= 2048) ? 6 : 4;
+  if (direct && !reg_whole && t_tall >= 16) return K >= 2048 ? 6 : 4;
   return reg;
 }
 

@@ -183,7 +183,8 @@ def test_config_rule(so):
         (0, 300, 521, 100, 256, (2, 1)),      # N odd and too small to pack: register-staged
         (1, 4096, 14336, 4096, 256, (7, 1)),  # whole 256-tiles, long K: eight waves + tail split
         (1, 4096, 4096, 4096, 256, (6, 1)),   # no partial round: eight waves, no split
-        (1, 4096, 4096, 1024, 256, (3, 1)),   # shorter K: four waves
+        (1, 4096, 4096, 1024, 256, (6, 1)),   # shorter K: eight waves, no split
+        (1, 3072, 3072, 3072, 256, (6, 1)),   # 144 tiles of 256x256, 576 of 128x128
         (1, 4096, 4000, 4096, 256, (6, 1)),   # ragged N: eight waves, no column split
         (1, 4096, 4004, 4096, 256, (6, 1)),   # N not a multiple of 8: B packed first
         (1, 2048, 2000, 4096, 256, (8, 1)),   # ragged N, 256 tiles of 128x128: direct 128x128
@@ -191,7 +192,8 @@ def test_config_rule(so):
         (1, 1000, 1004, 1000, 256, (8, 1)),   # N not a multiple of 8: B packed, as above
         (1, 3000, 3000, 3000, 256, (6, 1)),   # 576 tiles of 128x128: more than one round
         (1, 4096, 2048, 4096, 256, (8, 1)),   # 512 tiles of 128x128: one round at two per CU
-        (1, 4096, 4096, 256, 256, (1, 1)),    # K < 512: not the 256x256 tiles
+        (1, 4096, 4096, 256, 256, (6, 1)),    # K = 256: still the eight-wave tile
+        (1, 4096, 4096, 64, 256, (1, 1)),     # K < 128: register-staged 128x128
         (1, 300, 500, 4096, 256, (2, 22)),     # 40 tiles of 64x64: ~4 workgroups per CU
         (1, 1024, 1024, 4096, 256, (8, 4)),    # 64 tiles of 128x128: direct 128x128 in 4 chunks
         (1, 1024, 1024, 4095, 256, (8, 4)),    # the same with K ragged (A packed: half rows)
