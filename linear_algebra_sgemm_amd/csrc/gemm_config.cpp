@@ -15,8 +15,9 @@
 // the DeepGEMM page's offline tuning of block shapes and split-K with a table
 // lookup at run time (section 5.3).
 #include <atomic>
-#include <cmath>
 #include <cstddef>
+#include <cstdint>
+#include <cstring>
 
 #include "gemm_launch.h"
 
@@ -35,10 +36,39 @@ const TunedEntry kTuned[] = {
 
 std::atomic<bool> g_use_tuned{true};
 
+// log2(x) rounded to the nearest integer, clamped to [7, 14]: floor(log2 x),
+// plus one where x exceeds 2^c sqrt(2) (x^2 > 2^(2c+1); never equal for integers).
 int size_class(int x) {
   if (x <= 1) return 7;
-  const long c = std::lround(std::log2((double)x));
-  return c < 7 ? 7 : c > 14 ? 14 : (int)c;
+  int c = 31 - __builtin_clz((unsigned)x);
+  if ((uint64_t)x * (uint64_t)x > (uint64_t(1) << (2 * c + 1))) ++c;
+  return c < 7 ? 7 : c > 14 ? 14 : c;
+}
+
+// The table as a direct index (op, class of M, N, K), the first entry of a
+// class winning as in a scan of kTuned; built once.
+struct TunedIndex {
+  signed char tile[2][8][8][8];
+  signed char splits[2][8][8][8];
+};
+
+const TunedIndex& tuned_index() {
+  static const TunedIndex index = [] {
+    TunedIndex t;
+    std::memset(t.tile, -1, sizeof(t.tile));
+    std::memset(t.splits, -1, sizeof(t.splits));
+    for (const TunedEntry* e = kTuned; e->op >= 0; ++e) {
+      if (e->op > 1 || e->lm < 7 || e->lm > 14 || e->ln < 7 || e->ln > 14 || e->lk < 7 ||
+          e->lk > 14)
+        continue;
+      signed char& tile = t.tile[e->op][e->lm - 7][e->ln - 7][e->lk - 7];
+      if (tile >= 0) continue;
+      tile = e->tile;
+      t.splits[e->op][e->lm - 7][e->ln - 7][e->lk - 7] = e->splits;
+    }
+    return t;
+  }();
+  return index;
 }
 
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
@@ -186,15 +216,13 @@ void set_use_tuned(bool on) { g_use_tuned.store(on); }
 
 bool tuned_config(int op, int M, int N, int K, int* tile, int* splits) {
   if (!g_use_tuned.load()) return false;
-  const int lm = size_class(M), ln = size_class(N), lk = size_class(K);
-  for (const TunedEntry* e = kTuned; e->op >= 0; ++e) {
-    if (e->op == op && e->lm == lm && e->ln == ln && e->lk == lk) {
-      *tile = e->tile;
-      *splits = e->splits;
-      return true;
-    }
-  }
-  return false;
+  if (op < 0 || op > 1) return false;
+  const int lm = size_class(M) - 7, ln = size_class(N) - 7, lk = size_class(K) - 7;
+  const TunedIndex& index = tuned_index();
+  if (index.tile[op][lm][ln][lk] < 0) return false;
+  *tile = index.tile[op][lm][ln][lk];
+  *splits = index.splits[op][lm][ln][lk];
+  return true;
 }
 
 SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_splits,
