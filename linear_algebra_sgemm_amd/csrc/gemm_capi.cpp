@@ -233,23 +233,75 @@ bool half_b_ok(const void* B, int ldb, int N) {
   return ldb % 8 == 0 && N % 8 == 0 && aligned16(B) && (int64_t)ldb * 32 * 2 < (int64_t(1) << 31);
 }
 
+// The inputs a decision depends on; each thread keeps its last decision per
+// product, so a loop of equal calls plans once (about half a microsecond of
+// host time per call otherwise).
+struct DecisionKey {
+  int M, N, K, cus, ft, fs;
+  bool a16, a_ok, b_ok, tuned;
+  size_t ws_floats, pack_bytes;
+  bool operator==(const DecisionKey& o) const {
+    return M == o.M && N == o.N && K == o.K && cus == o.cus && ft == o.ft && fs == o.fs &&
+           a16 == o.a16 && a_ok == o.a_ok && b_ok == o.b_ok && tuned == o.tuned &&
+           ws_floats == o.ws_floats && pack_bytes == o.pack_bytes;
+  }
+};
+template <class Plan>
+struct Decision {
+  bool valid = false;
+  DecisionKey key{};
+  Plan plan{};
+  Packing pk;
+  bool pack = false;
+};
+thread_local Decision<lasg::SgemmPlan> t_last_sgemm;
+thread_local Decision<lasg::HalfPlan> t_last_half;
+
 // The FP32 plan, and whether (and how) operands are packed for it: `a16`,
 // `a_ok`, `b_ok` as above.
 lasg::SgemmPlan decide_sgemm(int M, int N, int K, bool a16, bool a_ok, bool b_ok, int cus,
                              size_t ws_floats, size_t pack_bytes, Packing& pk, bool& pack) {
   const int ft = g_force_sgemm_tile.load(), fs = g_force_sgemm_splits.load();
+  const DecisionKey key{M, N, K, cus, ft, fs, a16, a_ok, b_ok, lasg::use_tuned(), ws_floats,
+                        pack_bytes};
+  Decision<lasg::SgemmPlan>& last = t_last_sgemm;
+  if (last.valid && last.key == key) {
+    pk = last.pk;
+    pack = last.pack;
+    return last.plan;
+  }
   pack = !(a_ok && b_ok) && plan_packing(M, N, K, a_ok, b_ok, 4, pack_bytes, pk);
   const lasg::SgemmPlan plan =
       lasg::plan_sgemm(M, N, K, cus, ft, fs, ws_floats, pack || (a_ok && b_ok));
   if (plan_padding(M, N, K, plan.tile, a16 && b_ok, pack_bytes, pk)) pack = true;
+  last.valid = true;
+  last.key = key;
+  last.plan = plan;
+  last.pk = pk;
+  last.pack = pack;
   return plan;
 }
 
 lasg::HalfPlan decide_half(int M, int N, int K, bool a_ok, bool b_ok, int cus, size_t ws_floats,
                            size_t pack_bytes, Packing& pk, bool& pack) {
   const int ft = g_force_hgemm_tile.load(), fs = g_force_half_splits.load();
+  const DecisionKey key{M, N, K, cus, ft, fs, false, a_ok, b_ok, lasg::use_tuned(), ws_floats,
+                        pack_bytes};
+  Decision<lasg::HalfPlan>& last = t_last_half;
+  if (last.valid && last.key == key) {
+    pk = last.pk;
+    pack = last.pack;
+    return last.plan;
+  }
   pack = K > 0 && !(a_ok && b_ok) && plan_packing(M, N, K, a_ok, b_ok, 2, pack_bytes, pk);
-  return lasg::plan_half(M, N, K, cus, ft, fs, ws_floats, pack || (a_ok && b_ok));
+  const lasg::HalfPlan plan =
+      lasg::plan_half(M, N, K, cus, ft, fs, ws_floats, pack || (a_ok && b_ok));
+  last.valid = true;
+  last.key = key;
+  last.plan = plan;
+  last.pk = pk;
+  last.pack = pack;
+  return plan;
 }
 
 }  // namespace

@@ -213,6 +213,7 @@ int sgemm_rule_splits(int M, int N, int K, int tile, int cus) {
 }  // namespace
 
 void set_use_tuned(bool on) { g_use_tuned.store(on); }
+bool use_tuned() { return g_use_tuned.load(); }
 
 bool tuned_config(int op, int M, int N, int K, int* tile, int* splits) {
   if (!g_use_tuned.load()) return false;

@@ -156,6 +156,7 @@ int hgemm_tail_split(int M, int N, int cus);
 // Whether the offline-tuned table is consulted (default on; a test hook turns
 // it off to see the built-in rule).
 void set_use_tuned(bool on);
+bool use_tuned();
 
 // `ws` holds at least plan.splits * M * N floats when plan.splits > 1.
 hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hipStream_t s);
