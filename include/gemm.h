@@ -26,7 +26,11 @@
  *    returns GEMM_STATUS_HIP_ERROR; gemm_status_string then names the HIP error.
  *  - Threads: after gemm_create the compute calls may be made concurrently from
  *    several host threads and on several streams.  gemm_create/gemm_destroy must
- *    not race with compute calls.
+ *    not race with compute calls.  Calls that use the library's workspace or pack
+ *    buffer (split-K, operand copies) are ordered by the library: on one stream by
+ *    stream order; the first such call on a second stream waits on the host for
+ *    the device to finish its queued work (once; not under graph capture), and
+ *    from then on such calls order themselves with an event.
  */
 #ifndef LINEAR_ALGEBRA_SGEMM_AMD_GEMM_H
 #define LINEAR_ALGEBRA_SGEMM_AMD_GEMM_H
