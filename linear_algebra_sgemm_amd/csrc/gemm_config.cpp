@@ -138,11 +138,12 @@ long round_use(long tiles, int cus, int per_cu) {
 //    register-staged 64x64 tile and 94 for 128x128 direct at 192 tiles;
 //    1000 x 3000 x 777: 83 vs 69; 1500^3: 89 vs 73 for the best register-staged
 //    tile; 256^3: 4.8 vs 3.8), else register-staged.  But where there are at
-//    most a quarter as many 64x64 tiles as CUs, K is at most 2048 and the shape
-//    is whole in 32s, the 32x32 tile of 16x16x4 blocks: its shorter per-wave
-//    MFMA chain sets the time there (per call, 256^3: 7.1 us vs 9.2; 512^3:
-//    10.1 vs 13.9; 256 x 256 x 1024: 14.7 vs 22.1; but 1024 x 1024 x 256,
-//    256 tiles of 64x64: 11.8 vs 10.5).
+//    most a quarter as many 64x64 tiles as CUs and K is at most 2048, the
+//    32x32 tile of 16x16x4 blocks: its shorter per-wave MFMA chain sets the
+//    time there (per call, 256^3: 7.1 us vs 9.2; 512^3: 10.1 vs 13.9; 256 x 256
+//    x 1024: 14.7 vs 22.1; ragged too, bounds-checked: 300 x 520 x 100: 9.5 vs
+//    12.6, 500 x 500 x 777: 20.8 vs 26.1; but 1024 x 1024 x 256, 256 tiles of
+//    64x64: 11.8 vs 10.5).
 int sgemm_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_tall = ceil_div(M, 128) * ceil_div(N, 256);
@@ -176,8 +177,7 @@ int sgemm_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   if (t_tall >= 2L * cus && (!direct || (M % 128 == 0 && N % 256 == 0 && K % 16 == 0))) return 4;
   if (t_med >= 2L * cus && (!direct || (M % 128 == 0 && N % 128 == 0 && K % 16 == 0))) return 1;
   const long t_small = ceil_div(M, 64) * ceil_div(N, 64);
-  if (direct && 4 * t_small <= cus && K <= 2048 && M % 32 == 0 && N % 32 == 0 && K % 32 == 0)
-    return 12;
+  if (direct && 4 * t_small <= cus && K <= 2048) return 12;
   return direct ? 11 : 2;
 }
 

@@ -157,7 +157,7 @@ def test_config_rule(so):
         (0, 256, 256, 1024, 256, (12, 1)),
         (0, 512, 512, 512, 256, (12, 1)),     # 64 tiles of 64x64
         (0, 512, 512, 480, 256, (12, 1)),
-        (0, 512, 512, 500, 256, (11, 1)),     # K not a multiple of 32: 64x64 direct-to-LDS
+        (0, 512, 512, 500, 256, (12, 1)),     # K not a multiple of 32: still 32x32
         (0, 512, 576, 512, 256, (11, 1)),     # 72 tiles of 64x64
         (0, 1000, 3000, 777, 256, (11, 1)),   # 752 tiles
         (0, 2048, 2048, 2048, 256, (10, 1)),  # 64 tiles of 256x256, 256 of 128x128: direct 128x128
@@ -179,7 +179,7 @@ def test_config_rule(so):
         (0, 600, 600, 5000, 256, (11, 5)),    # 100 tiles: about two workgroups per CU
         (0, 4096, 4096, 4096, 64, (9, 1)),
         (0, 128, 128, 16384, 256, (11, 16)),  # 4 tiles; 128 chunks by CUs, capped at 16
-        (0, 300, 520, 100, 256, (11, 1)),     # ragged and small: the bounds-checked 64x64 copies
+        (0, 300, 520, 100, 256, (12, 1)),     # ragged and small: 32x32, bounds-checked
         (0, 300, 521, 100, 256, (2, 1)),      # N odd and too small to pack: register-staged
         (1, 4096, 14336, 4096, 256, (7, 1)),  # whole 256-tiles, long K: eight waves + tail split
         (1, 4096, 4096, 4096, 256, (6, 1)),   # no partial round: eight waves, no split
