@@ -198,11 +198,19 @@ static void half_gemm(decode16_fn dec, int M, int N, int K, double alpha, const 
                       double *ref, double *den, int threads) {
   int nt = oracle_threads(threads);
   int skip_product = (alpha == 0.0) || (K == 0);
+  /* B decoded to double once (the conversion is exact, so this changes no value;
+   * it only avoids decoding every element of B once per output row). */
+  double *bdec = NULL;
+  if (!skip_product && N > 0) {
+    bdec = (double *)malloc(sizeof(double) * (size_t)K * (size_t)N);
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int k = 0; k < K; ++k)
+      for (int j = 0; j < N; ++j) bdec[(size_t)k * N + j] = dec(B[(size_t)k * ldb + j]);
+  }
 #pragma omp parallel num_threads(nt)
   {
     double *acc = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
     double *mag = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
-    double *brow = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
 #pragma omp for schedule(dynamic, 1)
     for (int i = 0; i < M; ++i) {
       for (int j = 0; j < N; ++j) {
@@ -212,8 +220,7 @@ static void half_gemm(decode16_fn dec, int M, int N, int K, double alpha, const 
       if (!skip_product) {
         for (int k = 0; k < K; ++k) {
           double a = dec(A[(size_t)i * lda + k]);
-          const uint16_t *bsrc = B + (size_t)k * ldb;
-          for (int j = 0; j < N; ++j) brow[j] = dec(bsrc[j]);
+          const double *brow = bdec + (size_t)k * N;
           for (int j = 0; j < N; ++j) acc[j] += a * brow[j];
           if (den) {
             double aa = fabs(a);
@@ -230,8 +237,8 @@ static void half_gemm(decode16_fn dec, int M, int N, int K, double alpha, const 
     }
     free(acc);
     free(mag);
-    free(brow);
   }
+  free(bdec);
 }
 
 /* Sampled entries of the 16-bit product, one ascending-k dot product each. */

@@ -11,7 +11,7 @@ What pins what:
 * all-ones products (exact): the number of k terms summed;
 * alpha = 0 and beta = 0 with NaN-filled operands: the BLAS reading that unread
   operands never reach the result;
-* exact rational brute force on every shape up to 6 x 6 x 6 with padded leading
+* exact rational brute force on every shape up to 8 x 8 x 8 with padded leading
   dimensions: the whole sum, within the double-precision rounding bound, and the
   error scale ``den`` it returns;
 * small-integer operands (exact): the product against Python integer arithmetic;
@@ -19,12 +19,14 @@ What pins what:
   65536 bit patterns;
 * GELU(tanh) against its odd-part identity gelu(x) - gelu(-x) = x, its limits and
   torch's float64 ``gelu(approximate='tanh')``;
-* the binary16 and bfloat16 products against torch.matmul in float64 and torch's GELU.
+* the binary16 and bfloat16 products against torch.matmul in float64 and torch's GELU;
+* the 16-bit products on small-integer operands with padded, NaN-filled leading
+  dimensions against Python integer arithmetic (exact), and A = I giving B exactly:
+  their indexing, leading dimensions and the number of k terms.
 """
 from __future__ import annotations
 
 import itertools
-import math
 from fractions import Fraction
 
 import numpy as np
@@ -149,7 +151,7 @@ def _exact_sgemm(A, B, C0, alpha, beta, M, N, K, lda, ldb, ldc):
 
 def pin_brute_force_rational(o: _oracle.Oracle):
     rng = _rng(5)
-    dims = range(1, 7)
+    dims = range(1, 9)
     for (M, N, K) in itertools.product(dims, dims, dims):
         lda, ldb, ldc = K + (M % 3), N + (K % 2), N + 1
         alpha = float(np.float32(rng.uniform(-2, 2)))
@@ -301,10 +303,43 @@ def pin_half_unread(o: _oracle.Oracle):
     assert np.allclose(ref, np.broadcast_to(want, (M, N)), rtol=1e-14, atol=1e-15)
 
 
+def pin_half_integers_padded_exact(o: _oracle.Oracle):
+    """Small integers are exact in binary16 and bfloat16 and so are their K-term sums here,
+    so the 16-bit products must equal Python's integer arithmetic bit for bit, with the
+    padding of A and B (NaN) never read."""
+    rng = _rng(10)
+    for fmt, dt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        for (M, N, K) in [(5, 7, 3), (13, 11, 29), (8, 33, 64)]:
+            lda, ldb = K + 3, N + 2
+            Ai = rng.integers(-6, 7, size=(M, K))
+            Bi = rng.integers(-6, 7, size=(K, N))
+            A = torch.full((M, lda), float("nan"), dtype=dt)
+            A[:, :K] = torch.from_numpy(Ai.astype(np.float32)).to(dt)
+            B = torch.full((K, ldb), float("nan"), dtype=dt)
+            B[:, :N] = torch.from_numpy(Bi.astype(np.float32)).to(dt)
+            bits = lambda t: t.contiguous().view(torch.int16).numpy()  # noqa: E731
+            ref, den = o.hgemm_bias_act(M, N, K, 2.0, bits(A), lda, bits(B), ldb, None,
+                                        _oracle.ACT_NONE, fmt=fmt)
+            want = [[2 * sum(int(Ai[i, k]) * int(Bi[k, j]) for k in range(K)) for j in range(N)]
+                    for i in range(M)]
+            mag = [[2 * sum(abs(int(Ai[i, k]) * int(Bi[k, j])) for k in range(K))
+                    for j in range(N)] for i in range(M)]
+            assert np.array_equal(ref, np.array(want, np.float64)), "%s integer product" % fmt
+            assert np.array_equal(den, np.array(mag, np.float64)), "%s integer magnitudes" % fmt
+            # A = I (M = K): the product returns B's rows exactly, bias added per column
+            eye = torch.full((K, K + 1), float("nan"), dtype=dt)
+            eye[:, :K] = torch.eye(K).to(dt)
+            bias = np.arange(N, dtype=np.float32) - N / 2
+            refi, _ = o.hgemm_bias_act(K, N, K, 1.0, bits(eye), K + 1, bits(B), ldb, bias,
+                                       _oracle.ACT_NONE, fmt=fmt)
+            assert np.array_equal(refi, Bi.astype(np.float64) + bias.astype(np.float64)), \
+                "%s identity product" % fmt
+
+
 PINS = [pin_identity, pin_permutation, pin_all_ones, pin_alpha_zero_and_unread,
         pin_brute_force_rational, pin_small_integers_exact, pin_entries_match_full,
         pin_half_decoder, pin_bf16_decoder, pin_gelu, pin_half_product_vs_torch,
-        pin_bf16_product_vs_torch, pin_half_unread]
+        pin_bf16_product_vs_torch, pin_half_unread, pin_half_integers_padded_exact]
 
 
 def failing_pins(o: _oracle.Oracle):

@@ -36,6 +36,13 @@ MUTATIONS = {
     "bf16_shift": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
     "hgemm_bias_row_index": ("double b = bias ? (double)bias[j] : 0.0;",
                              "double b = bias ? (double)bias[i % N] : 0.0;"),
+    "half_ldb_ignored": ("dec(B[(size_t)k * ldb + j]);", "dec(B[(size_t)k * N + j]);"),
+    "half_lda_ignored": ("double a = dec(A[(size_t)i * lda + k]);",
+                         "double a = dec(A[(size_t)i * K + k]);"),
+    "half_drop_last_k": ("for (int k = 0; k < K; ++k) {\n          double a = dec(",
+                         "for (int k = 0; k < K - 1; ++k) {\n          double a = dec("),
+    "half_B_row_stride": ("const double *brow = bdec + (size_t)k * N;",
+                          "const double *brow = bdec + (size_t)k;"),
     "den_missing_beta": ("cmag = fabs(beta) * fabs(c);\n        }\n        ref[",
                          "cmag = 0.0;\n        }\n        ref["),
 }
