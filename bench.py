@@ -9,15 +9,17 @@ U[-1, 1] from seed 1).  C is restored from a pristine copy before every call,
 outside the timed events.  Each call is bracketed by HIP events on the stream
 it is launched on (created without the system-scope fence, which would write
 back and invalidate the caches at every record inside the timed interval);
-TFLOP/s = 2*M*N*K / mean call time.  The run prints ONE JSON
-line with the throughput, the roofline position of the GEMM kernel and the CPU
-oracle's own throughput on a bounded sample of the same workload (parity of
-this exact launch configuration is checked by the GPU test suite).
+TFLOP/s = 2*M*N*K / mean call time.  The default run also times the
+inference-FFN product (M = 4096, N = 14336, K = 4096, bias + GELU) in binary16
+and in bfloat16, for the percentage of the matrix peak of each dtype.  After
+the GPU phase, every element of each workload's first timed output is compared
+with the CPU oracle.  The run prints ONE JSON line with the throughput, the
+roofline position of the GEMM kernel, the per-dtype figures, the parity result
+and the CPU oracle's own throughput on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import re
@@ -30,16 +32,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOPS at 4096³ FP32 (α,β) + % of MI355X matrix peak per dtype"
 PROFILES = os.path.join(ROOT, "profiles")
-_CSRC = os.path.join(ROOT, "linear_algebra_sgemm_amd", "csrc")
-# The sources that decide what one call of each op runs: its kernels, the shared
-# copy helpers and the shape -> configuration choice with its tuned table.
-_CHOICE = [os.path.join(_CSRC, f) for f in ("dma_common.h", "gemm_config.cpp", "gemm_tuned.inc")]
-KERNEL_SOURCES = {
-    "sgemm": [os.path.join(_CSRC, "sgemm_kernels.hip")] + _CHOICE,
-    "hgemm_bias_gelu": [os.path.join(_CSRC, "hgemm_kernels.hip")] + _CHOICE,
-    "bgemm_bias_gelu": [os.path.join(_CSRC, "hgemm_kernels.hip")] + _CHOICE,
-}
-
 
 class HipTimer:
     """Timing events of the HIP runtime the process already uses (torch's), created
@@ -96,16 +88,12 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-parity", action="store_true",
+                   help="skip the oracle comparison of the first timed call's output")
+    p.add_argument("--no-extras", action="store_true",
+                   help="time only --workload (by default the 4096^3 FP32 run also times the "
+                        "binary16 and bfloat16 FFN products)")
     return p.parse_args()
-
-
-def source_digest(paths) -> str:
-    """First 16 hex digits of the SHA-256 of the files' contents, in order."""
-    h = hashlib.sha256()
-    for path in paths:
-        with open(path, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def profiled_traffic(workload: str, op: str):
@@ -120,7 +108,8 @@ def profiled_traffic(workload: str, op: str):
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not (m_src and m_bytes):
         return None
-    if m_src.group(1) != source_digest(KERNEL_SOURCES[op]):
+    from linear_algebra_sgemm_amd.profile_summary import source_digest
+    if m_src.group(1) != source_digest(op):
         return None
     return float(m_bytes.group(1))
 
@@ -155,7 +144,142 @@ def cpu_baseline(w, A, B, C, target_seconds: float):
     tf = cost.gemm_flops(rows, N, K) / t / 1e12
     return {"value": tf, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "%d of %d output rows (%d x %d x %d), fp64 accumulation, %.1f s"
-                      % (rows, M, rows, N, K, t)}
+                      % (rows, M, rows, N, K, t),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def parity(w, A, B, C, got):
+    """Every element of the first timed call's output against the CPU oracle: the largest
+    normalised error |C - ref| / (|alpha| sum_k |a||b| + |beta||c| or |bias|) and where."""
+    import numpy as np
+    import torch
+
+    import oracle
+    M, N, K = w.M, w.N, w.K
+    t0 = time.perf_counter()
+    if w.op == "sgemm":
+        ref, den = oracle.sgemm(M, N, K, w.alpha, A.numpy(), K, B.numpy(), N, w.beta, C.numpy(), N)
+        tol = 1e-5
+    else:
+        bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+        ref, den = oracle.hgemm_bias_act(M, N, K, w.alpha, bits(A), K, bits(B), N, C.numpy(),
+                                         oracle.ACT_GELU_TANH,
+                                         fmt="bf16" if w.op == "bgemm_bias_gelu" else "f16")
+        tol = 1e-2
+    e = oracle.normalized_error(got.float().numpy(), ref, den)
+    k = int(np.argmax(e))
+    return {"max_err": float(e[k // N, k % N]), "where": [k // N, k % N], "tol": tol,
+            "entries": M * N, "pass": bool(e.max() <= tol),
+            "oracle_s": round(time.perf_counter() - t0, 2)}
+
+
+def time_workload(w, steps: int, warmup: int):
+    """Warm-up calls, then `steps` timed calls of one workload on the current stream.
+    Returns the per-call times (ms), the host inputs and a copy of the first timed
+    call's output (taken after its end event, outside the timed interval)."""
+    import torch
+
+    import linear_algebra_sgemm_amd as lib
+    from linear_algebra_sgemm_amd import inputs
+
+    A, B, C = inputs.workload_inputs(w)   # C is the bias vector for the half-precision product
+    M, N, K = w.M, w.N, w.K
+    dev = torch.device("cuda:0")
+    dA, dB = A.to(dev), B.to(dev)
+    stream = torch.cuda.current_stream()
+    if w.op == "sgemm":
+        dC0 = C.to(dev)
+        dC = dC0.clone()
+
+        def call():
+            lib.sgemm(M, N, K, w.alpha, dA, K, dB, N, w.beta, dC, N, stream=stream)
+
+        def reset():
+            dC.copy_(dC0)
+    else:
+        bf16 = w.op == "bgemm_bias_gelu"
+        dbias = C.to(dev)
+        dC = torch.empty((M, N), dtype=torch.bfloat16 if bf16 else torch.float16, device=dev)
+        fn = lib.bgemm_bias_act if bf16 else lib.hgemm_bias_act
+
+        def call():
+            fn(M, N, K, w.alpha, dA, K, dB, N, dbias, lib.ACT_GELU_TANH, dC, N, stream=stream)
+
+        def reset():
+            pass
+
+    for _ in range(warmup):
+        reset()
+        call()
+    torch.cuda.synchronize()
+
+    timer = HipTimer(2 * steps)
+    handle = stream.cuda_stream
+    first = torch.empty_like(dC)
+    if w.op != "sgemm":
+        dC.fill_(float("nan"))   # the first timed call must write every element itself
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        reset()
+        timer.record(2 * i, handle)
+        call()
+        timer.record(2 * i + 1, handle)
+        if i == 0:
+            first.copy_(dC)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [timer.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)]
+    timer.close()
+    out = first.cpu()
+    del dA, dB, dC, first
+    return {"ms": ms, "wall_s": wall, "inputs": (A, B, C), "first": out}
+
+
+def call_stats(ms):
+    srt = sorted(ms)
+    p90 = srt[min(len(srt) - 1, int(round(0.9 * (len(srt) - 1))))]
+    return {"mean": round(statistics.fmean(ms), 5), "median": round(statistics.median(ms), 5),
+            "min": round(min(ms), 5), "p90": round(p90, 5), "max": round(max(ms), 5),
+            "stdev": round(statistics.stdev(ms), 5) if len(ms) > 1 else 0.0}
+
+
+def kernel_label(w, dtype: str) -> str:
+    import torch
+
+    import linear_algebra_sgemm_amd as lib
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if w.op == "sgemm":
+        tile, splits = lib.gemm_debug_pick_config(0, w.M, w.N, w.K, cus)
+        name = "%s, tile config %d" % ("sgemm_dma_kernel" if tile >= 7 else "sgemm_mfma_kernel",
+                                       tile)
+        if splits > 1:
+            name += ", split-K x%d + sgemm_splitk_reduce_kernel (timed together)" % splits
+        return name
+    tile, splits = lib.gemm_debug_pick_config(1, w.M, w.N, w.K, cus)
+    name = "%s, %s, tile config %d" % ("hgemm_dma_kernel" if tile >= 3 else "hgemm_mfma_kernel",
+                                       dtype, tile)
+    if splits > 1:
+        name += ", split-K x%d + half_splitk_reduce_kernel (timed together)" % splits
+    return name
+
+
+# The half-precision workloads measured beside the FP32 headline ("% of MI355X matrix
+# peak per dtype"): the FFN product in binary16 and in bfloat16.
+PER_DTYPE_EXTRAS = ("hgemm_ffn", "bgemm_ffn")
+EXTRA_MIN_STEPS = 50
+EXTRA_MIN_WARMUP = 10
 
 
 def main():
@@ -176,81 +300,55 @@ def main():
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
     steps = max(1, args.steps)
-
-    A, B, C = inputs.workload_inputs(w)   # C is the bias vector for the half-precision product
-    M, N, K = w.M, w.N, w.K
+    extras = [] if (args.no_extras or args.workload != "sgemm_4096") else list(PER_DTYPE_EXTRAS)
 
     cpu = None
     if not args.no_cpu_baseline:
+        A, B, C = inputs.workload_inputs(w)
         cpu = cpu_baseline(w, A, B, C, args.cpu_seconds)
+        del A, B, C
 
     lib.gemm_create()
-    dev = torch.device("cuda:0")
-    dA, dB = A.to(dev), B.to(dev)
-    stream = torch.cuda.current_stream()
-    if w.op == "sgemm":
-        dC0 = C.to(dev)
-        dC = dC0.clone()
+    # GPU phase: every timed workload, the headline one last; the CPU checks follow.
+    # The per-dtype workloads take at least 50 timed calls after at least 10 warm-up
+    # calls (the reporting rule of these workloads); the headline takes exactly
+    # --steps after --warmup.
+    runs = {}
+    for name in extras:
+        runs[name] = time_workload(inputs.WORKLOADS[name], max(steps, EXTRA_MIN_STEPS),
+                                   max(args.warmup, EXTRA_MIN_WARMUP))
+    runs[w.name] = time_workload(w, steps, args.warmup)
+    lib.gemm_destroy()
 
-        def call():
-            lib.sgemm(M, N, K, w.alpha, dA, K, dB, N, w.beta, dC, N, stream=stream)
+    def dtype_of(wl):
+        return {"sgemm": "f32", "hgemm_bias_gelu": "f16", "bgemm_bias_gelu": "bf16"}[wl.op]
 
-        def reset():
-            dC.copy_(dC0)
-        dtype, flops_dtype = "f32", "f32"
-        nbytes = cost.sgemm_bytes(M, N, K, w.beta)
-    else:
-        bf16 = w.op == "bgemm_bias_gelu"
-        dbias = C.to(dev)
-        dC = torch.empty((M, N), dtype=torch.bfloat16 if bf16 else torch.float16, device=dev)
-        fn = lib.bgemm_bias_act if bf16 else lib.hgemm_bias_act
+    per_dtype = {}
+    for name, r in runs.items():
+        wl = inputs.WORKLOADS[name]
+        dt = dtype_of(wl)
+        st = call_stats(r["ms"])
+        tf = cost.gemm_flops(wl.M, wl.N, wl.K) / (st["mean"] * 1e-3) / 1e12
+        entry = {"workload": name, "steps": len(r["ms"]), "tflops": round(tf, 3),
+                 "pct_of_peak": round(100.0 * tf / cost.PEAK_TFLOPS[dt], 2),
+                 "peak_tflops": cost.PEAK_TFLOPS[dt], "call_ms": st,
+                 "kernel": kernel_label(wl, dt)}
+        if not args.no_parity:
+            A, B, C = r["inputs"]
+            entry["parity"] = parity(wl, A, B, C, r["first"])
+        per_dtype[dt] = entry
 
-        def call():
-            fn(M, N, K, w.alpha, dA, K, dB, N, dbias, lib.ACT_GELU_TANH, dC, N, stream=stream)
-
-        def reset():
-            pass
-        dtype = flops_dtype = "bf16" if bf16 else "f16"
-        nbytes = cost.hgemm_bias_act_bytes(M, N, K)
-    flops = cost.gemm_flops(M, N, K)
-
-    for _ in range(args.warmup):
-        reset()
-        call()
-    torch.cuda.synchronize()
-
-    timer = HipTimer(2 * steps)
-    handle = stream.cuda_stream
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        reset()
-        timer.record(2 * i, handle)
-        call()
-        timer.record(2 * i + 1, handle)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = [timer.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)]
-    timer.close()
-    mean_ms = statistics.fmean(ms)
+    main_run = runs[w.name]
+    dtype = dtype_of(w)
+    st = call_stats(main_run["ms"])
+    mean_ms = st["mean"]
+    flops = cost.gemm_flops(w.M, w.N, w.K)
     tflops = flops / (mean_ms * 1e-3) / 1e12
-    peak = cost.PEAK_TFLOPS[flops_dtype]
-
-    traffic = profiled_traffic(w.name, w.op)
-    if w.op == "sgemm":
-        tile, splits = lib.gemm_debug_pick_config(
-            0, M, N, K, torch.cuda.get_device_properties(0).multi_processor_count)
-        kernel_name = "%s, tile config %d" % (
-            "sgemm_dma_kernel" if tile >= 7 else "sgemm_mfma_kernel", tile)
-        if splits > 1:
-            kernel_name += ", split-K x%d + sgemm_splitk_reduce_kernel (timed together)" % splits
-    else:
-        tile, _ = lib.gemm_debug_pick_config(
-            1, M, N, K, torch.cuda.get_device_properties(0).multi_processor_count)
-        kernel_name = "%s, %s, tile config %d" % (
-            "hgemm_dma_kernel" if tile >= 3 else "hgemm_mfma_kernel", dtype, tile)
-        if tile == 7:
-            kernel_name += " (256x256 head + 128x256 tail launches, timed together)"
+    peak = cost.PEAK_TFLOPS[dtype]
+    nbytes = (cost.sgemm_bytes(w.M, w.N, w.K, w.beta) if w.op == "sgemm"
+              else cost.hgemm_bias_act_bytes(w.M, w.N, w.K))
+    A, B, C = main_run["inputs"]
+    par = per_dtype[dtype].get("parity")
     line = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -258,31 +356,35 @@ def main():
         "n_gpus": 1,
         "steps": steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / steps * 1e3, 4),
+        "ms_per_step": round(main_run["wall_s"] / steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "op": w.op, "M": M, "N": N, "K": K, "alpha": w.alpha,
-                   "beta": w.beta, "layout": "row-major, packed",
+        "config": {"workload": w.name, "op": w.op, "M": w.M, "N": w.N, "K": w.K,
+                   "alpha": w.alpha, "beta": w.beta, "layout": "row-major, packed",
                    "inputs": "%s, seed %d" % (w.dist_ab, w.seed),
+                   "inputs_sha256": inputs.sha256(A, B, C),
                    "timing": "per-call HIP events (no system-scope fence) on the launch "
                              "stream, C reset before each call outside the events; "
                              "ms_per_step is wall time per step including that reset"},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
-        "call_ms": {"mean": round(mean_ms, 5), "median": round(statistics.median(ms), 5),
-                    "min": round(min(ms), 5), "max": round(max(ms), 5)},
+        "call_ms": st,
+        "parity_max_err": None if par is None else par["max_err"],
+        "parity": par,
+        "per_dtype": per_dtype,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                     "traffic": traffic,
+                     "traffic": profiled_traffic(w.name, w.op),
                      "algorithmic_bytes": nbytes,
-                     "kernel": kernel_name},
+                     "kernel": kernel_label(w, dtype)},
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),
     }
-    lib.gemm_destroy()
     print(json.dumps(line), flush=True)
+    if par is not None and not par["pass"]:
+        sys.exit("parity failed: max normalised error %.3g > %g" % (par["max_err"], par["tol"]))
 
 
 if __name__ == "__main__":
