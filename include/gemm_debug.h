@@ -75,6 +75,27 @@ int gemm_debug_use_tuned_table(int on);
  */
 int gemm_debug_pick_config(int op, int M, int N, int K, int cus, int* tile, int* splits);
 
+/*
+ * Tile order of later launches (both products): group_m 0 = each launch's own
+ * group size (the default), 1..64 = walk that many tile rows per group;
+ * xcd_remap 1 = renumber workgroups so that each of the eight XCDs takes one
+ * contiguous run of the order (the default), 0 = keep the dispatcher's order.
+ * Only the order of the output tiles changes, never a result.  Returns
+ * GEMM_STATUS_INVALID_VALUE for other values.  Pure host state.
+ */
+int gemm_debug_force_swizzle(int group_m, int xcd_remap);
+
+/*
+ * The output tile (tile_m[wg], tile_n[wg]) that workgroup wg of a launch over
+ * tiles_m x tiles_n tiles computes, for every wg < tiles_m * tiles_n, with
+ * group size group_m and the XCD renumbering on (xcd_remap 1) or off (0): the
+ * same function the kernels run.  tile_m and tile_n are host arrays of
+ * tiles_m * tiles_n ints.  Returns GEMM_STATUS_INVALID_VALUE for non-positive
+ * sizes, more than 2^24 tiles or null arrays.  Pure host computation.
+ */
+int gemm_debug_tile_map(int tiles_m, int tiles_n, int group_m, int xcd_remap, int* tile_m,
+                        int* tile_n);
+
 #ifdef __cplusplus
 }
 #endif

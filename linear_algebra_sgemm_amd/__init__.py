@@ -16,7 +16,8 @@ import os
 
 __all__ = ["GemmError", "gemm_create", "gemm_destroy", "sgemm", "hgemm_bias_act", "bgemm_bias_act",
            "gemm_status_string", "gemm_debug_force_tile", "gemm_debug_force_splits",
-           "gemm_debug_pick_config", "gemm_debug_use_tuned_table", "library_path",
+           "gemm_debug_pick_config", "gemm_debug_use_tuned_table", "gemm_debug_force_swizzle",
+           "gemm_debug_tile_map", "library_path",
            "load_library", "EXPORTED_SYMBOLS", "ACT_NONE", "ACT_GELU_TANH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +36,8 @@ ACT_GELU_TANH = 1
 # Every symbol declared in include/gemm.h and include/gemm_debug.h.
 EXPORTED_SYMBOLS = ("gemm_create", "gemm_destroy", "sgemm", "hgemm_bias_act", "bgemm_bias_act",
                     "gemm_status_string", "gemm_debug_force_tile", "gemm_debug_force_splits",
-                    "gemm_debug_pick_config", "gemm_debug_use_tuned_table")
+                    "gemm_debug_pick_config", "gemm_debug_use_tuned_table",
+                    "gemm_debug_force_swizzle", "gemm_debug_tile_map")
 
 _lib = None
 
@@ -81,6 +83,10 @@ def load_library():
     lib.gemm_debug_pick_config.restype = I
     lib.gemm_debug_use_tuned_table.argtypes = [I]
     lib.gemm_debug_use_tuned_table.restype = I
+    lib.gemm_debug_force_swizzle.argtypes = [I, I]
+    lib.gemm_debug_force_swizzle.restype = I
+    lib.gemm_debug_tile_map.argtypes = [I, I, I, I, P, P]
+    lib.gemm_debug_tile_map.restype = I
     _lib = lib
     return lib
 
@@ -171,3 +177,20 @@ def gemm_debug_pick_config(op: int, M: int, N: int, K: int, cus: int):
                                                 ctypes.byref(tile), ctypes.byref(splits))
     _check(st, "gemm_debug_pick_config", True)
     return tile.value, splits.value
+
+
+def gemm_debug_force_swizzle(group_m: int, xcd_remap: bool = True) -> int:
+    """Tile order of later launches: group_m 0 = each launch's own; see include/gemm_debug.h."""
+    return load_library().gemm_debug_force_swizzle(int(group_m), 1 if xcd_remap else 0)
+
+
+def gemm_debug_tile_map(tiles_m: int, tiles_n: int, group_m: int, xcd_remap: bool = True):
+    """(tile_m, tile_n) int arrays: the output tile of every workgroup of such a launch."""
+    import numpy as np
+    n = int(tiles_m) * int(tiles_n)
+    tm = np.empty(max(n, 1), np.int32)
+    tn = np.empty(max(n, 1), np.int32)
+    st = load_library().gemm_debug_tile_map(int(tiles_m), int(tiles_n), int(group_m),
+                                            1 if xcd_remap else 0, tm.ctypes.data, tn.ctypes.data)
+    _check(st, "gemm_debug_tile_map", True)
+    return tm[:n], tn[:n]

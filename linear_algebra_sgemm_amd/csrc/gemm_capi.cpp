@@ -17,6 +17,7 @@
 
 #include "../../include/gemm.h"
 #include "../../include/gemm_debug.h"
+#include "gemm_common.h"
 #include "gemm_launch.h"
 
 namespace {
@@ -519,6 +520,24 @@ int gemm_debug_force_splits(int op, int splits) {
 int gemm_debug_use_tuned_table(int on) {
   if (on != 0 && on != 1) return GEMM_STATUS_INVALID_VALUE;
   lasg::set_use_tuned(on == 1);
+  return GEMM_STATUS_SUCCESS;
+}
+
+int gemm_debug_force_swizzle(int group_m, int xcd_remap) {
+  if (group_m < 0 || group_m > 64 || (xcd_remap != 0 && xcd_remap != 1))
+    return GEMM_STATUS_INVALID_VALUE;
+  lasg::set_swizzle(group_m, xcd_remap == 1);
+  return GEMM_STATUS_SUCCESS;
+}
+
+int gemm_debug_tile_map(int tiles_m, int tiles_n, int group_m, int xcd_remap, int* tile_m,
+                        int* tile_n) {
+  if (tiles_m <= 0 || tiles_n <= 0 || group_m <= 0 || (xcd_remap != 0 && xcd_remap != 1) ||
+      tile_m == nullptr || tile_n == nullptr || (int64_t)tiles_m * tiles_n > (1 << 24))
+    return GEMM_STATUS_INVALID_VALUE;
+  const int g = xcd_remap ? group_m : -group_m;
+  for (int wg = 0; wg < tiles_m * tiles_n; ++wg)
+    lasg::tile_of_workgroup(wg, tiles_m, tiles_n, g, tile_m[wg], tile_n[wg]);
   return GEMM_STATUS_SUCCESS;
 }
 

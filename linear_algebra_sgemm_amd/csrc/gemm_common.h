@@ -30,14 +30,23 @@ __device__ __forceinline__ int mfma32_row(int r, int lane) {
 // Step 2, grouped order: walk `group_m` tile rows column by column, so the
 // tiles that run together on one XCD share a few A row panels and B column
 // panels (the L2-reuse block swizzle of the DeepGEMM page, section 3.4).
-__device__ __forceinline__ void tile_of_workgroup(int wg, int tiles_m, int tiles_n, int group_m,
-                                                  int& tile_m, int& tile_n) {
+// A negative `group_m` skips step 1 (a test hook compares both orders) and
+// groups -group_m rows.  Both steps are bijections of [0, tiles_m * tiles_n),
+// which a host test checks over all grids up to 64 x 64.
+__host__ __device__ __forceinline__ void tile_of_workgroup(int wg, int tiles_m, int tiles_n,
+                                                           int group_m, int& tile_m,
+                                                           int& tile_n) {
   const int total = tiles_m * tiles_n;
-  const int xcd = wg % kXcds;
-  const int slot = wg / kXcds;
-  const int per = total / kXcds;
-  const int rem = total % kXcds;
-  const int t = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  int t = wg;
+  if (group_m > 0) {
+    const int xcd = wg % kXcds;
+    const int slot = wg / kXcds;
+    const int per = total / kXcds;
+    const int rem = total % kXcds;
+    t = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  } else {
+    group_m = -group_m;
+  }
   const int group = group_m * tiles_n;
   const int gid = t / group;
   const int first = gid * group_m;

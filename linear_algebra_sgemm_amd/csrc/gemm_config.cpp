@@ -215,6 +215,22 @@ int sgemm_rule_splits(int M, int N, int K, int tile, int cus) {
 void set_use_tuned(bool on) { g_use_tuned.store(on); }
 bool use_tuned() { return g_use_tuned.load(); }
 
+namespace {
+std::atomic<int> g_force_group{0};      // 0: each launch's own group size
+std::atomic<bool> g_xcd_remap{true};
+}  // namespace
+
+void set_swizzle(int group_m, bool xcd_remap) {
+  g_force_group.store(group_m);
+  g_xcd_remap.store(xcd_remap);
+}
+
+int swizzle_group(int launch_group_m) {
+  const int forced = g_force_group.load();
+  const int g = forced > 0 ? forced : launch_group_m;
+  return g_xcd_remap.load() ? g : -g;
+}
+
 bool tuned_config(int op, int M, int N, int K, int* tile, int* splits) {
   if (!g_use_tuned.load()) return false;
   if (op < 0 || op > 1) return false;

@@ -158,6 +158,14 @@ int hgemm_tail_split(int M, int N, int cus);
 void set_use_tuned(bool on);
 bool use_tuned();
 
+// Tile order of the launches (tile_of_workgroup): by default each launch's own
+// group size with the XCD renumbering.  A test hook forces another group size
+// (group_m > 0) or none (0) and turns the renumbering off or on.
+void set_swizzle(int group_m, bool xcd_remap);
+// The group_m value a launch passes to its kernel: the forced or the launch's
+// own group size, negated when the XCD renumbering is off.
+int swizzle_group(int launch_group_m);
+
 // `ws` holds at least plan.splits * M * N floats when plan.splits > 1.
 hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hipStream_t s);
 hipError_t launch_sgemm_scale(int M, int N, float beta, float* C, int ldc, hipStream_t s);

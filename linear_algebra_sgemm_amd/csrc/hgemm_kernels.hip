@@ -907,7 +907,7 @@ static hipError_t launch_htile(const HgemmCall& c, int group_m, hipStream_t s, i
   p.C = c.C; p.ldc = c.ldc;
   p.tiles_m = (c.M + T::BM - 1) / T::BM;
   p.tiles_n = (c.N + T::BN - 1) / T::BN;
-  p.group_m = group_m;
+  p.group_m = swizzle_group(group_m);
   p.k_chunk = k_chunk;
   p.nb = c.N;
   p.ws = ws;
@@ -969,7 +969,7 @@ static hipError_t launch_hdma(const HgemmCall& c, int group_m, hipStream_t s, in
   p.C = c.C; p.ldc = c.ldc;
   p.tiles_m = (c.M + T::BM - 1) / T::BM;
   p.tiles_n = (c.N + T::BN - 1) / T::BN;
-  p.group_m = group_m;
+  p.group_m = swizzle_group(group_m);
   p.nb = readable_cols(c.nb, c.N);
   p.k_chunk = k_chunk;
   p.ws = ws;

@@ -807,7 +807,7 @@ static hipError_t launch_tile(const SgemmCall& c, const SgemmPlan& plan, int gro
   p.A = c.A; p.lda = c.lda; p.B = c.B; p.ldb = c.ldb; p.C = c.C; p.ldc = c.ldc;
   p.tiles_m = (c.M + T::BM - 1) / T::BM;
   p.tiles_n = (c.N + T::BN - 1) / T::BN;
-  p.group_m = group_m;
+  p.group_m = swizzle_group(group_m);
   p.k_chunk = plan.k_chunk;
   p.ws = ws;
   p.a_vec = c.lda % 4 == 0 && aligned16(c.A);
@@ -900,7 +900,7 @@ static hipError_t launch_sdma_as(const SgemmCall& c, const SgemmPlan& plan, int 
   p.A = c.A; p.lda = c.lda; p.B = c.B; p.ldb = c.ldb; p.C = c.C; p.ldc = c.ldc;
   p.tiles_m = (c.M + T::BM - 1) / T::BM;
   p.tiles_n = (c.N + T::BN - 1) / T::BN;
-  p.group_m = group_m;
+  p.group_m = swizzle_group(group_m);
   p.k_chunk = plan.splits > 1 ? plan.k_chunk : c.K;
   p.ws = ws;
   p.a_vec = p.b_vec = 1;
