@@ -187,12 +187,26 @@ struct HStage {
 // rounding) instead of a full-precision division, which costs about ten
 // instructions per element in the epilogue.  It tends to x for large positive x
 // and to -0 for large negative x.
-__device__ __forceinline__ float gelu_tanh(float x) {
+__device__ __forceinline__ float gelu_factor(float x) {
   const float k1 = 0.044715f;
   const float c = -2.302208198f;   // -2 sqrt(2 / pi) log2(e)
   const float t = c * __builtin_fmaf(k1 * x, x * x, x);
-  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
+__device__ __forceinline__ float gelu_tanh(float x) { return x * gelu_factor(x); }
+
+// The activation of a call, chosen without a branch per element: x times
+// gs * factor + (1 - gs), with gs = 1 (GELU: exactly x * factor) or gs = 0
+// (identity: exactly x * 1; the factor is finite).  A branch on the activation
+// inside the element loops would be taken once per element.
+struct Activation {
+  float gs, g0;
+  __device__ __forceinline__ explicit Activation(int act)
+      : gs(act == 1 ? 1.0f : 0.0f), g0(act == 1 ? 0.0f : 1.0f) {}
+  __device__ __forceinline__ float operator()(float x) const {
+    return x * __builtin_fmaf(gs, gelu_factor(x), g0);
+  }
+};
 
 template <class T, bool EDGE, bool SPLIT>
 __global__ void __launch_bounds__(T::THREADS) hgemm_mfma_kernel(HgemmArgs p) {
@@ -650,6 +664,136 @@ __device__ __forceinline__ void hdma_k_tail(const HgemmArgs& p, f32x16 (&acc)[T:
     }
 }
 
+// Bias of the wave's output columns, n-blocks j0 .. j0 + JB - 1: lane l needs,
+// for n-block j and q = 0..3, columns 32 j + 8 q + 4 (l / 32) + 0..3 of the
+// wave's tile (zero without a bias, and past N on a ragged tile).  All loads of
+// a batch are issued before any value is used.
+template <class T, bool EDGE, int JB>
+__device__ __forceinline__ void hdma_load_bias(const HgemmArgs& p, float (&bias)[JB][4][4], int j0,
+                                               int n0, int wn, int lane) {
+#pragma unroll
+  for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int col = n0 + wn * T::WTN + 32 * (j0 + jj) + 8 * q + 4 * (lane / 32);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        bias[jj][q][e] = (p.bias != nullptr && (!EDGE || col + e < p.N)) ? p.bias[col + e] : 0.0f;
+    }
+}
+
+// n-blocks whose bias values a wave holds at once: two (32 values per lane) for
+// the tiles of at most two n-blocks per wave, one for the wider wave tiles,
+// whose accumulators and epilogue leave less room.
+template <class T>
+constexpr int bias_batch() { return T::FN == 2 ? 2 : 1; }
+
+// Epilogue of the direct-to-LDS kernel: x = alpha acc + bias, the activation,
+// rounded to the 16-bit format and stored.  Lane l holds, for n-block j, m-block
+// i and q = 0..3, the four columns n = 8 q + 4 (l / 32) + 0..3 of row m = l % 32.
+template <class T, bool EDGE>
+__device__ __forceinline__ void hdma_epilogue(const HgemmArgs& p, const f32x16 (&acc)[T::FN][T::FM],
+                                              uint8_t* lds, int m0, int n0, int wave, int wm,
+                                              int wn, int lane) {
+  constexpr int JB = bias_batch<T>();
+  static_assert(T::FN % JB == 0, "n-blocks split into whole batches");
+  // The eight-wave tiles load the first batch of bias values before the
+  // barrier, so their latency overlaps the wait for the other waves; the
+  // four-wave tiles, whose accumulators fill their registers up to the last
+  // K tile, load it after.
+  constexpr bool EARLY = T::WAVES_PER_SIMD == 2;
+  float bias0[JB][4][4];
+  if constexpr (EARLY) hdma_load_bias<T, EDGE, JB>(p, bias0, 0, n0, wn, lane);
+  const float alpha = p.alpha;
+  const Activation act(p.act);
+  if (p.ldc % 8 == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15u) == 0 && (!EDGE || p.N % 8 == 0)) {
+    // Through LDS, so that every store instruction writes whole rows: the wave
+    // puts its finished WTM x WTN tile into its own region of the (now idle)
+    // stages, then reads it back 16 bytes per lane along rows.  16-byte chunks
+    // of row r are permuted by (r / rows-per-256-bytes) % chunks-per-row, so
+    // the writes of one column over 32 rows spread over the banks.
+    static_assert(T::BM * T::BN * 2 <= T::STAGES * T::STAGE_BYTES, "output tile must fit the stages");
+    constexpr int RB = T::WTN * 2;          // bytes per row of a wave's tile
+    constexpr int CPR = RB / 16;            // 16-byte chunks per row
+    constexpr int RPL = RB >= 256 ? 1 : 256 / RB;
+    static_assert(RB % 128 == 0 && 1024 % RB == 0, "rows of 128 or 256 bytes");
+    lds_barrier();   // every wave is done with the stages
+    if constexpr (!EARLY) hdma_load_bias<T, EDGE, JB>(p, bias0, 0, n0, wn, lane);
+    uint8_t* region = lds + wave * (T::WTM * RB);
+#pragma unroll
+    for (int j0 = 0; j0 < T::FN; j0 += JB) {
+      float bias_next[JB][4][4];
+      if (j0 > 0) hdma_load_bias<T, EDGE, JB>(p, bias_next, j0, n0, wn, lane);
+      float (&bias)[JB][4][4] = j0 > 0 ? bias_next : bias0;
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj) {
+        const int j = j0 + jj;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+          for (int i = 0; i < T::FM; ++i) {
+            const int r = 32 * i + lane % 32;
+            uint16_t h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              h[e] = T::E::bits(act(__builtin_fmaf(alpha, acc[j][i][4 * q + e], bias[jj][q][e])));
+            }
+            const int chunk = 4 * j + q;
+            *reinterpret_cast<uint2*>(region + r * RB + 16 * (chunk ^ ((r / RPL) % CPR)) +
+                                      8 * (lane / 32)) = __builtin_bit_cast(uint2, h);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < T::WTM * RB / 1024; ++it) {
+      const int r = it * (1024 / RB) + lane / CPR;
+      const int chunk = lane % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(region + r * RB +
+                                                      16 * (chunk ^ ((r / RPL) % CPR)));
+      // (N is a multiple of 8 here: a chunk is wholly in or out)
+      if (EDGE && (m0 + wm * T::WTM + r >= p.M || n0 + wn * T::WTN + 8 * chunk >= p.N)) continue;
+      *reinterpret_cast<u32x4*>(p.C + (size_t)(m0 + wm * T::WTM + r) * p.ldc + n0 +
+                                wn * T::WTN + 8 * chunk) = v;
+    }
+    return;
+  }
+  if constexpr (!EARLY) hdma_load_bias<T, EDGE, JB>(p, bias0, 0, n0, wn, lane);
+  const bool vec_store = (p.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.C) & 7u) == 0);
+#pragma unroll
+  for (int j0 = 0; j0 < T::FN; j0 += JB) {
+    float bias_next[JB][4][4];
+    if (j0 > 0) hdma_load_bias<T, EDGE, JB>(p, bias_next, j0, n0, wn, lane);
+    float (&bias)[JB][4][4] = j0 > 0 ? bias_next : bias0;
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+      const int j = j0 + jj;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn * T::WTN + 32 * j + 8 * q + 4 * (lane / 32);
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) {
+          const int row = m0 + wm * T::WTM + 32 * i + lane % 32;
+          uint16_t h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            h[e] = T::E::bits(act(__builtin_fmaf(alpha, acc[j][i][4 * q + e], bias[jj][q][e])));
+          }
+          uint16_t* dst = p.C + (size_t)row * p.ldc + col;
+          if (EDGE && (row >= p.M || col >= p.N)) continue;
+          if (vec_store && (!EDGE || col + 3 < p.N)) {
+            *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, h);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (!EDGE || col + e < p.N) dst[e] = h[e];
+          }
+        }
+      }
+    }
+  }
+}
+
 // SPLIT: workgroup row blockIdx.y runs K chunk y (a multiple of 2 BK) and
 // writes its raw FP32 partial sums to the workspace (the split-K scheme of the
 // register-staged kernel, whose reduction kernel applies the epilogue).
@@ -752,97 +896,7 @@ hgemm_dma_kernel(HgemmArgs p) {
     return;
   }
 
-  // Epilogue.  Lane l holds, for n-block j, m-block i and q = 0..3, the four
-  // columns n = 8 q + 4 (l / 32) + 0..3 of row m = l % 32.
-  const float alpha = p.alpha;
-  const bool gelu = p.act == 1;
-  if (p.ldc % 8 == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15u) == 0 && (!EDGE || p.N % 8 == 0)) {
-    // Through LDS, so that every store instruction writes whole rows: the wave
-    // puts its finished WTM x WTN tile into its own region of the (now idle)
-    // stages, then reads it back 16 bytes per lane along rows.  16-byte chunks
-    // of row r are permuted by (r / rows-per-256-bytes) % chunks-per-row, so
-    // the writes of one column over 32 rows spread over the banks.
-    static_assert(T::BM * T::BN * 2 <= T::STAGES * T::STAGE_BYTES, "output tile must fit the stages");
-    constexpr int RB = T::WTN * 2;          // bytes per row of a wave's tile
-    constexpr int CPR = RB / 16;            // 16-byte chunks per row
-    constexpr int RPL = RB >= 256 ? 1 : 256 / RB;
-    static_assert(RB % 128 == 0 && 1024 % RB == 0, "rows of 128 or 256 bytes");
-    lds_barrier();   // every wave is done with the stages
-    uint8_t* region = lds + wave * (T::WTM * RB);
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int cl = wn * T::WTN + 32 * j + 8 * q + 4 * (lane / 32);
-        float bias4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (p.bias != nullptr) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (!EDGE || n0 + cl + e < p.N) bias4[e] = p.bias[n0 + cl + e];
-        }
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i) {
-          const int r = 32 * i + lane % 32;
-          uint16_t h[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float x = __builtin_fmaf(alpha, acc[j][i][4 * q + e], bias4[e]);
-            if (gelu) x = gelu_tanh(x);
-            h[e] = T::E::bits(x);
-          }
-          const int chunk = 4 * j + q;
-          *reinterpret_cast<uint2*>(region + r * RB + 16 * (chunk ^ ((r / RPL) % CPR)) +
-                                    8 * (lane / 32)) = __builtin_bit_cast(uint2, h);
-        }
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < T::WTM * RB / 1024; ++it) {
-      const int r = it * (1024 / RB) + lane / CPR;
-      const int chunk = lane % CPR;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(region + r * RB +
-                                                      16 * (chunk ^ ((r / RPL) % CPR)));
-      // (N is a multiple of 8 here: a chunk is wholly in or out)
-      if (EDGE && (m0 + wm * T::WTM + r >= p.M || n0 + wn * T::WTN + 8 * chunk >= p.N)) continue;
-      *reinterpret_cast<u32x4*>(p.C + (size_t)(m0 + wm * T::WTM + r) * p.ldc + n0 +
-                                wn * T::WTN + 8 * chunk) = v;
-    }
-    return;
-  }
-  const bool vec_store = (p.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.C) & 7u) == 0);
-#pragma unroll
-  for (int j = 0; j < T::FN; ++j) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int col = n0 + wn * T::WTN + 32 * j + 8 * q + 4 * (lane / 32);
-      float bias4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (p.bias != nullptr) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (!EDGE || col + e < p.N) bias4[e] = p.bias[col + e];
-      }
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i) {
-        const int row = m0 + wm * T::WTM + 32 * i + lane % 32;
-        uint16_t h[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = __builtin_fmaf(alpha, acc[j][i][4 * q + e], bias4[e]);
-          if (gelu) x = gelu_tanh(x);
-          h[e] = T::E::bits(x);
-        }
-        uint16_t* dst = p.C + (size_t)row * p.ldc + col;
-        if (EDGE && (row >= p.M || col >= p.N)) continue;
-        if (vec_store && (!EDGE || col + 3 < p.N)) {
-          *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, h);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (!EDGE || col + e < p.N) dst[e] = h[e];
-        }
-      }
-    }
-  }
+  hdma_epilogue<T, EDGE>(p, acc, lds, m0, n0, wave, wm, wn, lane);
 }
 
 template <class E> using HTileLarge = HgemmTile<E, 256, 256, 64, 2, 2>;

@@ -186,40 +186,46 @@ struct Stage {
 };
 
 // Epilogue of one wave: C = alpha * acc + beta * C over the wave's WTM x WTN
-// sub-tile at (r0, c0), C read only when beta != 0.  For each row of blocks, all
-// C loads are issued before the first one is consumed, so their latencies
-// overlap instead of adding up.
+// sub-tile at (r0, c0), C read only when beta != 0.  The C loads of a batch of
+// JB blocks of one block row are all issued before the first one is consumed,
+// so their latencies overlap instead of adding up: a whole block row on whole
+// tiles, one block at a time in the bounds-checked form (EDGE), whose row and
+// column checks hold registers of their own.
 template <class T, bool EDGE, class ACC>
 __device__ __forceinline__ void sgemm_store(const SgemmArgs& p, const ACC& acc, int r0, int c0,
                                             int lane) {
   using MF = typename T::MF;
+  constexpr int JB = EDGE ? 1 : T::FN;
   const int lb = lane % T::BLK;
   const float alpha = p.alpha, beta = p.beta;
   const bool read_c = beta != 0.0f;
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
-    float cv[T::FN][MF::ACC];
-    if (read_c) {
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
-        const int col = c0 + j * T::BLK + lb;
+    for (int j0 = 0; j0 < T::FN; j0 += JB) {
+      float cv[JB][MF::ACC];
+      if (read_c) {
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+          const int col = c0 + (j0 + jj) * T::BLK + lb;
+#pragma unroll
+          for (int r = 0; r < MF::ACC; ++r) {
+            const int row = r0 + i * T::BLK + MF::row(r, lane);
+            const bool ok = !EDGE || (row < p.M && col < p.N);
+            cv[jj][r] = ok ? p.C[(size_t)row * p.ldc + col] : 0.0f;
+          }
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj) {
+        const int col = c0 + (j0 + jj) * T::BLK + lb;
 #pragma unroll
         for (int r = 0; r < MF::ACC; ++r) {
           const int row = r0 + i * T::BLK + MF::row(r, lane);
-          const bool ok = !EDGE || (row < p.M && col < p.N);
-          cv[j][r] = ok ? p.C[(size_t)row * p.ldc + col] : 0.0f;
+          if (EDGE && (row >= p.M || col >= p.N)) continue;
+          const float v = alpha * acc[i][j0 + jj][r];
+          p.C[(size_t)row * p.ldc + col] = read_c ? __builtin_fmaf(beta, cv[jj][r], v) : v;
         }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) {
-      const int col = c0 + j * T::BLK + lb;
-#pragma unroll
-      for (int r = 0; r < MF::ACC; ++r) {
-        const int row = r0 + i * T::BLK + MF::row(r, lane);
-        if (EDGE && (row >= p.M || col >= p.N)) continue;
-        const float v = alpha * acc[i][j][r];
-        p.C[(size_t)row * p.ldc + col] = read_c ? __builtin_fmaf(beta, cv[j][r], v) : v;
       }
     }
   }
@@ -366,13 +372,18 @@ __global__ void __launch_bounds__(256) sgemm_scale_kernel(int M, int N, float be
 //    different halves of the 64 banks.
 // ---------------------------------------------------------------------------
 template <int BM_, int BN_, int STAGES_, int WAVES_PER_SIMD_ = 1, int WAVES_M_ = 2,
-          int WAVES_N_ = 2, bool A_DW_ = false>
+          int WAVES_N_ = 2, bool A_DW_ = false, bool LEAN_ = false>
 struct SDmaTile {
   using MF = MfmaF32x32;
   static constexpr int BM = BM_, BN = BN_, BK = 16, STAGES = STAGES_;
   static constexpr bool A_DW = A_DW_;
+  // LEAN: two fragment sets instead of four (sdma_tile2): the second group of
+  // a K tile is read under the MFMAs of its first group, and the next tile's
+  // first group under those of the second; for the tile whose accumulators
+  // leave no room for four sets.
+  static constexpr bool LEAN = LEAN_;
   // The same tile copying A with 4-byte copies.
-  using WithADw = SDmaTile<BM_, BN_, STAGES_, WAVES_PER_SIMD_, WAVES_M_, WAVES_N_, true>;
+  using WithADw = SDmaTile<BM_, BN_, STAGES_, WAVES_PER_SIMD_, WAVES_M_, WAVES_N_, true, LEAN_>;
   static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M * WAVES_N;
   static constexpr int WG_PER_CU = WAVES_PER_SIMD * 4 / WAVES;
@@ -582,6 +593,68 @@ __device__ __forceinline__ void sdma_tile(const SgemmArgs& p, f32x16 (&acc)[T::F
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// One K tile with two fragment sets (LEAN tiles).  On entry x0 holds group 0
+// of tile kt.  The MFMAs of group 0 run while group 1 of the same tile is read
+// into x1; then the MFMAs of group 1 run while group 0 of tile kt + 1 is read
+// back into x0, and the copies of tile kt + STAGES - 1 go out among the last of
+// them.  The wait and barrier for tile kt + 1 come first, as in sdma_tile; past
+// the barrier every wave has also read all of stage (kt - 1) % STAGES (its
+// second group during tile kt - 1), which those copies refill.
+template <class T, bool STEADY>
+__device__ __forceinline__ void sdma_tile2(const SgemmArgs& p, f32x16 (&acc)[T::FM][T::FN],
+                                           int kt, int ktiles, SFrags<T>& x0, SFrags<T>& x1,
+                                           const uint8_t* lds, uint32_t lds_base,
+                                           const SDmaPlan<T>& plan, const float* a_tile,
+                                           const float* b_tile, int wave, int wm, int wn,
+                                           int lane) {
+  constexpr int NM = 4 * T::FM * T::FN;            // MFMAs per group
+  constexpr int NR = T::FM + 4 * T::FN;            // LDS reads per group
+  constexpr int PRE = 2;
+  constexpr int R0 = (NR + NM - PRE - 1) / (NM - PRE);
+  constexpr int TAIL = NM - T::LOADS_PER_TILE;
+  constexpr int R1 = (NR + TAIL - 1) / TAIL;
+  static_assert(TAIL >= NR / 2 && TAIL >= 1, "enough MFMAs to spread the reads over");
+  smfma<T>(acc, x0, 0);
+  smfma<T>(acc, x0, 1);
+  if constexpr (STEADY) {
+    wait_vmcnt<(T::STAGES - 3) * T::LOADS_PER_TILE>();
+  } else {
+    const int left = ktiles - 2 - kt;
+    swait_tiles<T>(left < 0 ? 0 : (left < T::STAGES - 3 ? left : T::STAGES - 3));
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  const uint8_t* cur = lds + (kt % T::STAGES) * T::STAGE_BYTES;
+  const uint8_t* next = lds + ((kt + 1) % T::STAGES) * T::STAGE_BYTES;
+  sload_frags<T>(x1, cur, 1, wm, wn, lane);
+#pragma unroll
+  for (int x = PRE; x < NM; ++x) smfma<T>(acc, x0, x);
+#pragma unroll
+  for (int x = 0; x < NM - PRE; ++x) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int kt_issue = kt + T::STAGES - 1;
+  const bool issue = STEADY || kt_issue < ktiles;
+  const uint32_t st_issue = lds_base + (kt_issue % T::STAGES) * T::STAGE_BYTES;
+  sload_frags<T>(x0, next, 0, wm, wn, lane);
+#pragma unroll
+  for (int x = 0; x < TAIL; ++x) smfma<T>(acc, x1, x);
+#pragma unroll
+  for (int x = 0; x < TAIL; ++x) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, R1, 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int x = 0; x < T::LOADS_PER_TILE; ++x) {
+    smfma<T>(acc, x1, TAIL + x);
+    if (issue) sdma_issue<T>(p, plan, a_tile, b_tile, kt_issue, st_issue, wave, x);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // The last K - K % 32 < 32 values of k on a ragged K: both stages 0 and 1 are
 // filled with bounds-checked loads and plain LDS stores, in the layout the
 // copies produce (zeros for k >= K, clamped rows and columns as in SDmaPlan),
@@ -685,20 +758,30 @@ sgemm_dma_kernel(SgemmArgs p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     sload_frags<T>(f0, lds, 0, wm, wn, lane);
-    sload_frags<T>(f1, lds, 1, wm, wn, lane);
+    if constexpr (!T::LEAN) sload_frags<T>(f1, lds, 1, wm, wn, lane);
   }
   int kt = 0;
-  for (; kt + T::STAGES < ktiles; kt += 2) {
-    sdma_tile<T, true>(p, acc, kt, ktiles, f0, f1, f2, f3, lds, lds_base, plan, a_tile, b_tile,
-                       wave, wm, wn, lane);
-    sdma_tile<T, true>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, plan, a_tile, b_tile,
-                       wave, wm, wn, lane);
-  }
-  for (; kt < ktiles; kt += 2) {
-    sdma_tile<T, false>(p, acc, kt, ktiles, f0, f1, f2, f3, lds, lds_base, plan, a_tile, b_tile,
-                        wave, wm, wn, lane);
-    sdma_tile<T, false>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, plan, a_tile,
-                        b_tile, wave, wm, wn, lane);
+  if constexpr (T::LEAN) {
+    // One tile per trip: each tile leaves the next tile's first group in f0.
+    for (; kt + T::STAGES - 1 < ktiles; ++kt)
+      sdma_tile2<T, true>(p, acc, kt, ktiles, f0, f1, lds, lds_base, plan, a_tile, b_tile, wave,
+                          wm, wn, lane);
+    for (; kt < ktiles; ++kt)
+      sdma_tile2<T, false>(p, acc, kt, ktiles, f0, f1, lds, lds_base, plan, a_tile, b_tile, wave,
+                           wm, wn, lane);
+  } else {
+    for (; kt + T::STAGES < ktiles; kt += 2) {
+      sdma_tile<T, true>(p, acc, kt, ktiles, f0, f1, f2, f3, lds, lds_base, plan, a_tile, b_tile,
+                         wave, wm, wn, lane);
+      sdma_tile<T, true>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, plan, a_tile,
+                         b_tile, wave, wm, wn, lane);
+    }
+    for (; kt < ktiles; kt += 2) {
+      sdma_tile<T, false>(p, acc, kt, ktiles, f0, f1, f2, f3, lds, lds_base, plan, a_tile, b_tile,
+                          wave, wm, wn, lane);
+      sdma_tile<T, false>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, plan, a_tile,
+                          b_tile, wave, wm, wn, lane);
+    }
   }
   if constexpr (EDGE) {
     if (ktiles * T::BK < p.K) sdma_k_tail<T>(p, acc, lds, ktiles * T::BK, m0, n0, wm, wn, lane);
@@ -759,7 +842,7 @@ using TileTall16 = SgemmTile<128, 256, 16, 2, 2, 2, MfmaF16x16>;
 // Direct-to-LDS: 256 x 256, 4 stages of 32.5 KiB, one workgroup per CU / 128 x 256,
 // 3 stages of 24.5 KiB, two workgroups per CU.
 using SDmaLarge = SDmaTile<256, 256, 4, 1>;
-using SDmaTall = SDmaTile<128, 256, 3, 2>;
+using SDmaTall = SDmaTile<128, 256, 3, 2, 2, 2, false, true>;
 // 256 x 256 with eight waves (2 x 4, each 128 x 64), two per SIMD.
 using SDmaEight = SDmaTile<256, 256, 4, 2, 2, 4>;
 // 128 x 128 with four waves of 64 x 64, 4 stages of 16.5 KiB, two workgroups per CU:
