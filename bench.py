@@ -90,6 +90,9 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true",
                    help="skip the oracle comparison of the first timed call's output")
+    p.add_argument("--swizzle", default=None, metavar="GROUP,REMAP",
+                   help="tile order for a counter comparison: rows per group (0 = each "
+                        "launch's own) and the XCD renumbering (1 on, 0 off)")
     p.add_argument("--no-extras", action="store_true",
                    help="time only --workload (by default the 4096^3 FP32 run also times the "
                         "binary16 and bfloat16 FFN products)")
@@ -309,6 +312,10 @@ def main():
         del A, B, C
 
     lib.gemm_create()
+    if args.swizzle:
+        g, r = (int(x) for x in args.swizzle.split(","))
+        if lib.gemm_debug_force_swizzle(g, bool(r)) != lib.STATUS_SUCCESS:
+            sys.exit("invalid --swizzle %s" % args.swizzle)
     # GPU phase: every timed workload, the headline one last; the CPU checks follow.
     # The per-dtype workloads take at least 50 timed calls after at least 10 warm-up
     # calls (the reporting rule of these workloads); the headline takes exactly
@@ -366,6 +373,7 @@ def main():
                    "alpha": w.alpha, "beta": w.beta, "layout": "row-major, packed",
                    "inputs": "%s, seed %d" % (w.dist_ab, w.seed),
                    "inputs_sha256": inputs.sha256(A, B, C),
+                   "tile_order": args.swizzle or "default",
                    "timing": "per-call HIP events (no system-scope fence) on the launch "
                              "stream, C reset before each call outside the events; "
                              "ms_per_step is wall time per step including that reset"},

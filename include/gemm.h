@@ -29,8 +29,11 @@
  *    not race with compute calls.  Calls that use the library's workspace or pack
  *    buffer (split-K, operand copies) are ordered by the library: on one stream by
  *    stream order; the first such call on a second stream waits on the host for
- *    the device to finish its queued work (once; not under graph capture), and
- *    from then on such calls order themselves with an event.
+ *    the device to finish its queued work (once), and from then on such calls
+ *    order themselves with an event.  A call made while its stream is being
+ *    captured into a HIP graph uses neither: it runs without split-K, and
+ *    operands whose rows are off 16-byte boundaries are read in place by the
+ *    bounds-checked kernels, so its replays need no ordering with other calls.
  */
 #ifndef LINEAR_ALGEBRA_SGEMM_AMD_GEMM_H
 #define LINEAR_ALGEBRA_SGEMM_AMD_GEMM_H

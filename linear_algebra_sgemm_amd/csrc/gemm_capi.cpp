@@ -70,10 +70,10 @@ bool ld_ok(int ld, int cols) { return ld >= (cols > 1 ? cols : 1); }
 // the workspace, stream order alone keeps its users apart and no event is
 // recorded (an event record between two kernels costs about 4 us of GPU time
 // per call).  The first user on a second stream waits, once, for all work
-// queued on the device (nothing recorded the earlier users' completion; under
-// graph capture nothing runs, and there is nothing to wait for); from then on
-// every user records `done` and a user on another stream than the last waits
-// for it.
+// queued on the device (nothing recorded the earlier users' completion); from
+// then on every user records `done` and a user on another stream than the last
+// waits for it.  Calls made under stream capture never get here (they are
+// planned without the workspace: see capturing()).
 template <class F>
 int with_workspace(hipStream_t stream, F launch) {
   std::lock_guard<std::mutex> wl(g_ws.mu);
@@ -81,13 +81,8 @@ int with_workspace(hipStream_t stream, F launch) {
   hipError_t e;
   if (g_ws.used && g_ws.last != stream) {
     if (!g_ws.multi) {
-      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-      e = hipStreamIsCapturing(stream, &cs);
+      e = hipDeviceSynchronize();
       if (e != hipSuccess) return hip_failure(e);
-      if (cs == hipStreamCaptureStatusNone) {
-        e = hipDeviceSynchronize();
-        if (e != hipSuccess) return hip_failure(e);
-      }
       g_ws.multi = true;
     } else {
       e = hipStreamWaitEvent(stream, g_ws.done, 0);
@@ -103,6 +98,21 @@ int with_workspace(hipStream_t stream, F launch) {
   g_ws.last = stream;
   g_ws.used = true;
   return GEMM_STATUS_SUCCESS;
+}
+
+// Whether `stream` is being captured into a graph.  A captured call may be
+// replayed at any later time, unordered with the eager calls that share the
+// workspace, so such calls are planned without it: no split-K and no operand
+// copies (operands off 16-byte rows then take the bounds-checked kernels).
+// Sets *status on a HIP failure.
+bool capturing(hipStream_t stream, int* status) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) {
+    *status = hip_failure(e);
+    return false;
+  }
+  return cs != hipStreamCaptureStatusNone;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -408,9 +418,18 @@ int sgemm(int M, int N, int K, float alpha, const float* A, int lda, const float
     lasg::SgemmCall c{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
     Packing pk;
     bool pack = false;
-    const lasg::SgemmPlan plan =
-        decide_sgemm(M, N, K, sgemm_a_rows16(A, lda), sgemm_a_ok(A, lda), sgemm_b_ok(B, ldb, N),
-                     g_cus.load(), g_ws.floats, g_ws.pack_bytes, pk, pack);
+    const bool a16 = sgemm_a_rows16(A, lda), a_ok = sgemm_a_ok(A, lda);
+    const bool b_ok = sgemm_b_ok(B, ldb, N);
+    lasg::SgemmPlan plan = decide_sgemm(M, N, K, a16, a_ok, b_ok, g_cus.load(), g_ws.floats,
+                                        g_ws.pack_bytes, pk, pack);
+    if (plan.splits > 1 || pack) {
+      int st = GEMM_STATUS_SUCCESS;
+      if (capturing(stream, &st)) {
+        pk = Packing();
+        plan = decide_sgemm(M, N, K, a16, a_ok, b_ok, g_cus.load(), 0, 0, pk, pack);
+      }
+      if (st != GEMM_STATUS_SUCCESS) return st;
+    }
     if (plan.splits > 1 || pack) {
       return with_workspace(stream, [&](float* ws, void* pbuf) {
         lasg::SgemmCall cc = c;
@@ -455,8 +474,17 @@ int half_product(bool bf16, int M, int N, int K, float alpha, const uint16_t* A,
   const int cus = g_cus.load();
   Packing pk;
   bool pack = false;
-  const lasg::HalfPlan plan = decide_half(M, N, c.K, half_a_ok(A, lda), half_b_ok(B, ldb, N), cus,
-                                          g_ws.floats, g_ws.pack_bytes, pk, pack);
+  const bool a_ok = half_a_ok(A, lda), b_ok = half_b_ok(B, ldb, N);
+  lasg::HalfPlan plan = decide_half(M, N, c.K, a_ok, b_ok, cus, g_ws.floats, g_ws.pack_bytes, pk,
+                                    pack);
+  if (plan.splits > 1 || pack) {
+    int st = GEMM_STATUS_SUCCESS;
+    if (capturing(stream, &st)) {
+      pk = Packing();
+      plan = decide_half(M, N, c.K, a_ok, b_ok, cus, 0, 0, pk, pack);
+    }
+    if (st != GEMM_STATUS_SUCCESS) return st;
+  }
   auto launch = [&](float* ws, void* pbuf) {
     lasg::HgemmCall cc = c;
     if (pack) {

@@ -271,6 +271,37 @@ def counters_markdown(workload: str, op: str, flops: int, algo_bytes: int, copy_
     return "\n".join(lines) + "\n"
 
 
+def tile_order_markdown(cases, commands, note: str = "") -> str:
+    """A/B of tile orders: per case (workload, label, FETCH csv, WRITE csv, kernel-stats
+    csv), the HBM bytes per call (copy-calibrated as in counters_markdown) and the
+    library kernels' summed average duration per call."""
+    from . import cost, inputs
+    lines = ["# Tile order A/B: HBM traffic and kernel time per call", "",
+             "Commands ($REPO = repository root on the GPU box; W = workload, G,R = rows per "
+             "group and XCD renumbering, as passed to bench.py --swizzle):", ""]
+    lines += ["    " + c for c in commands]
+    lines += [""]
+    if note:
+        lines += [note, ""]
+    lines += ["| Workload | group rows | XCD renumbering | HBM bytes per call | vs algorithmic | "
+              "kernel time per call (us) |", "|---|---|---|---|---|---|"]
+    for workload, label, fetch_csv, write_csv, stats_csv in cases:
+        w = inputs.WORKLOADS[workload]
+        half = w.op != "sgemm"
+        algo = (cost.hgemm_bias_act_bytes(w.M, w.N, w.K) if half
+                else cost.sgemm_bytes(w.M, w.N, w.K, w.beta))
+        f, wr = dispatches(fetch_csv), dispatches(write_csv)
+        fs, ws, _ = copy_scale(wr, f, w.M * w.N * (2 if half else 4))
+        merged, _ = per_call([f, wr])
+        hbm = (merged.get("FETCH_SIZE", 0.0) * fs + merged.get("WRITE_SIZE", 0.0) * ws) * 1024
+        us = sum(r[2] for r in trace_table(stats_csv) if LIB_PREFIX in (r[0] or "")) / 1e3
+        g, r = label.split(",")
+        lines.append("| `%s` | %s | %s | %.4g | %.2fx | %.1f |"
+                     % (workload, g if g != "0" else "launch's own", "on" if r == "1" else "off",
+                        hbm, hbm / algo, us))
+    return "\n".join(lines) + "\n"
+
+
 def _norm(name: str) -> str:
     return re.sub(r"\s+", "", name)
 
@@ -303,6 +334,12 @@ def parse_args(argv=None):
                    help="a file holding those remarks (instead of compiling)")
     c.add_argument("--note", default="")
     c.add_argument("--out", required=True)
+    o = sub.add_parser("tile-order")
+    o.add_argument("--case", dest="cases", action="append", required=True,
+                   metavar="WORKLOAD:G,R:FETCH_CSV:WRITE_CSV:STATS_CSV")
+    o.add_argument("--command", dest="commands", action="append", required=True)
+    o.add_argument("--note", default="")
+    o.add_argument("--out", required=True)
     return ap.parse_args(argv)
 
 
@@ -317,6 +354,9 @@ def main(argv=None):
     args = parse_args(argv)
     if args.what == "trace":
         text = trace_markdown(args.workload, args.stats, args.command, args.note)
+    elif args.what == "tile-order":
+        text = tile_order_markdown([tuple(c.split(":")) for c in args.cases], args.commands,
+                                   args.note)
     else:
         sys.path.insert(0, ROOT)
         from . import cost, inputs
