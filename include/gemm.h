@@ -88,6 +88,27 @@ int sgemm(int M, int N, int K, float alpha,
           float beta, float* C, int ldc, hipStream_t stream);
 
 /*
+ * sgemm for callers that cannot allocate device memory on the call path: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, layout, conventions and errors as sgemm, and the
+ * same kernels; it calls no hipMalloc, hipFree or allocating library routine.
+ * Its split-K partial sums live in a static device array of 16 MiB (4 Mi
+ * floats; one copy per GPU, held until the process ends) instead of the
+ * workspace gemm_create allocates: split counts are limited to
+ * splits * M * N <= 4 Mi, and operands whose rows are off 16-byte boundaries
+ * are read by the bounds-checked kernels instead of being copied.  A plan that
+ * would need more scratch returns GEMM_STATUS_INVALID_VALUE.  Needs
+ * gemm_create, which looks the array up on its device (another device's is
+ * looked up by the first call there).  Every sgemm_noalloc call on one GPU
+ * shares that GPU's array, which keeps the last call's contents; calls that
+ * overlap on one GPU (different streams, or a graph replayed while another
+ * call runs) race.
+ */
+int sgemm_noalloc(int M, int N, int K, float alpha,
+                  const float* A, int lda, const float* B, int ldb,
+                  float beta, float* C, int ldc, hipStream_t stream);
+
+/*
  * C = act(alpha * A x B + bias) with A (M x K) and B (K x N) in IEEE binary16
  * (passed as uint16_t bit patterns), FP32 accumulation, an FP32 bias of length
  * N added to every row (NULL = no bias), the activation `act` (gemm_act_t) and

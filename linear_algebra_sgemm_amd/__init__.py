@@ -14,7 +14,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["GemmError", "gemm_create", "gemm_destroy", "sgemm", "hgemm_bias_act", "bgemm_bias_act",
+__all__ = ["GemmError", "gemm_create", "gemm_destroy", "sgemm", "sgemm_noalloc", "hgemm_bias_act",
+           "bgemm_bias_act",
            "gemm_status_string", "gemm_debug_force_tile", "gemm_debug_force_splits",
            "gemm_debug_pick_config", "gemm_debug_use_tuned_table", "gemm_debug_force_swizzle",
            "gemm_debug_tile_map", "library_path",
@@ -34,7 +35,8 @@ ACT_NONE = 0
 ACT_GELU_TANH = 1
 
 # Every symbol declared in include/gemm.h and include/gemm_debug.h.
-EXPORTED_SYMBOLS = ("gemm_create", "gemm_destroy", "sgemm", "hgemm_bias_act", "bgemm_bias_act",
+EXPORTED_SYMBOLS = ("gemm_create", "gemm_destroy", "sgemm", "sgemm_noalloc", "hgemm_bias_act",
+                    "bgemm_bias_act",
                     "gemm_status_string", "gemm_debug_force_tile", "gemm_debug_force_splits",
                     "gemm_debug_pick_config", "gemm_debug_use_tuned_table",
                     "gemm_debug_force_swizzle", "gemm_debug_tile_map")
@@ -68,6 +70,8 @@ def load_library():
     lib.gemm_destroy.restype = I
     lib.sgemm.argtypes = [I, I, I, F, P, I, P, I, F, P, I, P]
     lib.sgemm.restype = I
+    lib.sgemm_noalloc.argtypes = [I, I, I, F, P, I, P, I, F, P, I, P]
+    lib.sgemm_noalloc.restype = I
     lib.hgemm_bias_act.argtypes = [I, I, I, F, P, I, P, I, P, I, P, I, P]
     lib.hgemm_bias_act.restype = I
     lib.bgemm_bias_act.argtypes = [I, I, I, F, P, I, P, I, P, I, P, I, P]
@@ -131,6 +135,15 @@ def sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None, *, raise_on
     st = load_library().sgemm(int(M), int(N), int(K), float(alpha), _ptr(A), int(lda), _ptr(B),
                               int(ldb), float(beta), _ptr(C), int(ldc), _stream(stream))
     return _check(st, "sgemm", raise_on_error)
+
+
+def sgemm_noalloc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None, *,
+                  raise_on_error=True):
+    """sgemm without device allocation on the call path; see include/gemm.h."""
+    st = load_library().sgemm_noalloc(int(M), int(N), int(K), float(alpha), _ptr(A), int(lda),
+                                      _ptr(B), int(ldb), float(beta), _ptr(C), int(ldc),
+                                      _stream(stream))
+    return _check(st, "sgemm_noalloc", raise_on_error)
 
 
 def hgemm_bias_act(M, N, K, alpha, A, lda, B, ldb, bias, act, C, ldc, stream=None, *,

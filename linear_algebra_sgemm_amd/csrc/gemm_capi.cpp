@@ -57,6 +57,22 @@ std::atomic<int> g_force_half_splits{-1};
 
 thread_local char t_last_error[256] = "";
 
+// Scratch of the entry point that allocates nothing (sgemm_noalloc): the FP32
+// split-K partial sums of one call, at most kScratchFloats floats.
+constexpr size_t kScratchFloats = size_t(4) << 20;   // 16 MiB
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+// One copy per GPU, held until the process ends.  In host code `scratch` only
+// names the symbol: its device address, per device, comes from
+// hipGetSymbolAddress (scratch_on_current_device) and is what kernels receive.
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+namespace {
+
+std::atomic<float*> g_scratch_ptr[kMaxDevices];
+
 int hip_failure(hipError_t e) {
   std::snprintf(t_last_error, sizeof(t_last_error), "HIP error %d: %s", (int)e,
                 hipGetErrorString(e));
@@ -64,6 +80,25 @@ int hip_failure(hipError_t e) {
 }
 
 bool ld_ok(int ld, int cols) { return ld >= (cols > 1 ? cols : 1); }
+
+// Device address of `scratch` on the current device, looked up once per device
+// (by gemm_create, or by the first sgemm_noalloc call on another device).
+int scratch_on_current_device(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_failure(e);
+  if (dev < 0 || dev >= kMaxDevices) return GEMM_STATUS_INTERNAL;
+  float* ptr = g_scratch_ptr[dev].load();
+  if (ptr == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_failure(e);
+    ptr = static_cast<float*>(addr);
+    g_scratch_ptr[dev].store(ptr);
+  }
+  *out = ptr;
+  return GEMM_STATUS_SUCCESS;
+}
 
 // Runs `launch(ws, pack)` with the workspace, ordered after the previous
 // workspace user when that ran on another stream.  While one stream has used
@@ -366,6 +401,20 @@ int gemm_create(void) {
     g_ws.used = false;
     g_ws.multi = false;
   }
+  {
+    float* sp = nullptr;
+    const int st = scratch_on_current_device(&sp);
+    if (st != GEMM_STATUS_SUCCESS) {
+      std::lock_guard<std::mutex> wl(g_ws.mu);
+      (void)hipEventDestroy(g_ws.done);
+      (void)hipFree(g_ws.ptr);
+      (void)hipFree(g_ws.pack);
+      g_ws.ptr = nullptr;
+      g_ws.pack = nullptr;
+      g_ws.done = nullptr;
+      return st;
+    }
+  }
   g_state.device = dev;
   g_state.cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   g_cus.store(g_state.cus);
@@ -450,6 +499,39 @@ int sgemm(int M, int N, int K, float alpha, const float* A, int lda, const float
     } else {
       e = lasg::launch_sgemm(c, plan, nullptr, stream);
     }
+  }
+  return e == hipSuccess ? GEMM_STATUS_SUCCESS : hip_failure(e);
+}
+
+int sgemm_noalloc(int M, int N, int K, float alpha, const float* A, int lda, const float* B,
+                  int ldb, float beta, float* C, int ldc, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0) return GEMM_STATUS_INVALID_VALUE;
+  if (!ld_ok(lda, K) || !ld_ok(ldb, N) || !ld_ok(ldc, N)) return GEMM_STATUS_INVALID_VALUE;
+  const bool empty = (M == 0 || N == 0);
+  const bool reads_ab = !empty && K > 0 && alpha != 0.0f;
+  if (!empty && C == nullptr) return GEMM_STATUS_INVALID_VALUE;
+  if (reads_ab && (A == nullptr || B == nullptr)) return GEMM_STATUS_INVALID_VALUE;
+  if (!g_ready.load()) return GEMM_STATUS_NOT_INITIALIZED;
+  if (empty) return GEMM_STATUS_SUCCESS;
+  hipError_t e;
+  if (!reads_ab) {
+    e = lasg::launch_sgemm_scale(M, N, beta, C, ldc, stream);
+  } else {
+    float* ws = nullptr;
+    const int st = scratch_on_current_device(&ws);
+    if (st != GEMM_STATUS_SUCCESS) return st;
+    // Planned with the static scratch as the split-K workspace and no pack
+    // buffer: split counts are clamped so that splits * M * N fits, and
+    // operands off 16-byte rows take the bounds-checked kernels.
+    Packing pk;
+    bool pack = false;
+    const lasg::SgemmPlan plan =
+        decide_sgemm(M, N, K, sgemm_a_rows16(A, lda), sgemm_a_ok(A, lda), sgemm_b_ok(B, ldb, N),
+                     g_cus.load(), kScratchFloats, 0, pk, pack);
+    if (pack || (plan.splits > 1 && (size_t)plan.splits * M * N > kScratchFloats))
+      return GEMM_STATUS_INVALID_VALUE;   // beyond the scratch (the plan never asks for it)
+    lasg::SgemmCall c{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+    e = lasg::launch_sgemm(c, plan, ws, stream);
   }
   return e == hipSuccess ? GEMM_STATUS_SUCCESS : hip_failure(e);
 }
