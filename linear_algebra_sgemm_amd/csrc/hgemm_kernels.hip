@@ -797,14 +797,15 @@ __device__ __forceinline__ void hdma_epilogue(const HgemmArgs& p, const f32x16 (
 // SPLIT: workgroup row blockIdx.y runs K chunk y (a multiple of 2 BK) and
 // writes its raw FP32 partial sums to the workspace (the split-K scheme of the
 // register-staged kernel, whose reduction kernel applies the epilogue).
-template <class T, bool EDGE, bool SPLIT = false>
-__global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(T::WAVES_PER_SIMD)))
-hgemm_dma_kernel(HgemmArgs p) {
+// The work of one workgroup: output tile number `wg` of the launch (in the
+// tile order of tile_of_workgroup) and K chunk `chunk` (SPLIT), in the LDS
+// array `lds` of at least STAGES * STAGE_BYTES bytes.
+template <class T, bool EDGE, bool SPLIT>
+__device__ __forceinline__ void hdma_workgroup(HgemmArgs p, int wg, int chunk, uint8_t* lds) {
   static_assert(T::KSTEPS % 2 == 0, "fragments ping-pong between two register sets");
   static_assert(T::LOADS_PER_TILE <= T::FM * T::FN, "one direct load per MFMA at most");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[T::STAGES * T::STAGE_BYTES];
   if constexpr (SPLIT) {
-    const int kbeg = blockIdx.y * p.k_chunk;
+    const int kbeg = chunk * p.k_chunk;
     const int klen = p.K - kbeg < p.k_chunk ? p.K - kbeg : p.k_chunk;
     p.A += kbeg;
     p.B += (size_t)kbeg * p.ldb;
@@ -812,7 +813,7 @@ hgemm_dma_kernel(HgemmArgs p) {
   }
 
   int tile_m, tile_n;
-  tile_of_workgroup(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
+  tile_of_workgroup(wg, p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
   const int m0 = tile_m * T::BM;
   const int n0 = tile_n * T::BN;
   const int lane = threadIdx.x % kWave;
@@ -879,7 +880,7 @@ hgemm_dma_kernel(HgemmArgs p) {
   if constexpr (SPLIT) {
     // Lane l holds, for n-block j, m-block i and q = 0..3, columns 8 q + 4 (l / 32)
     // + 0..3 of row l % 32 (as in the epilogue below).
-    float* W = p.ws + (size_t)blockIdx.y * p.M * p.N;
+    float* W = p.ws + (size_t)chunk * p.M * p.N;
 #pragma unroll
     for (int j = 0; j < T::FN; ++j)
 #pragma unroll
@@ -897,6 +898,31 @@ hgemm_dma_kernel(HgemmArgs p) {
   }
 
   hdma_epilogue<T, EDGE>(p, acc, lds, m0, n0, wave, wm, wn, lane);
+}
+
+template <class T, bool EDGE, bool SPLIT = false>
+__global__ void __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(T::WAVES_PER_SIMD)))
+hgemm_dma_kernel(HgemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[T::STAGES * T::STAGE_BYTES];
+  hdma_workgroup<T, EDGE, SPLIT>(p, blockIdx.x, blockIdx.y, lds);
+}
+
+// Two tile shapes in one launch: workgroups 0 .. head_wgs - 1 take the tiles of
+// `head` (tile shape H), the rest those of `tail` (shape T2), so the tail's
+// tiles start on each compute unit as soon as it has finished its last head
+// tile instead of after the whole head has drained.  Both shapes have the same
+// number of waves; the LDS array is the larger of the two.
+template <class H, class T2>
+__global__ void __launch_bounds__(H::THREADS) __attribute__((amdgpu_waves_per_eu(H::WAVES_PER_SIMD)))
+hgemm_dma_head_tail_kernel(HgemmArgs head, HgemmArgs tail, int head_wgs) {
+  static_assert(H::THREADS == T2::THREADS && H::WAVES_PER_SIMD == T2::WAVES_PER_SIMD,
+                "both shapes run the same workgroup");
+  constexpr int HB = H::STAGES * H::STAGE_BYTES, TB = T2::STAGES * T2::STAGE_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[HB > TB ? HB : TB];
+  if ((int)blockIdx.x < head_wgs)
+    hdma_workgroup<H, false, false>(head, blockIdx.x, 0, lds);
+  else
+    hdma_workgroup<T2, false, false>(tail, blockIdx.x - head_wgs, 0, lds);
 }
 
 template <class E> using HTileLarge = HgemmTile<E, 256, 256, 64, 2, 2>;
@@ -1013,8 +1039,7 @@ static bool dma_whole(const HgemmCall& c) {
 }
 
 template <class T>
-static hipError_t launch_hdma(const HgemmCall& c, int group_m, hipStream_t s, int splits = 1,
-                              int k_chunk = 0, float* ws = nullptr) {
+static HgemmArgs hdma_args(const HgemmCall& c, int group_m, int k_chunk, float* ws) {
   HgemmArgs p;
   p.M = c.M; p.N = c.N; p.K = c.K;
   p.alpha = c.alpha;
@@ -1027,6 +1052,13 @@ static hipError_t launch_hdma(const HgemmCall& c, int group_m, hipStream_t s, in
   p.nb = readable_cols(c.nb, c.N);
   p.k_chunk = k_chunk;
   p.ws = ws;
+  return p;
+}
+
+template <class T>
+static hipError_t launch_hdma(const HgemmCall& c, int group_m, hipStream_t s, int splits = 1,
+                              int k_chunk = 0, float* ws = nullptr) {
+  const HgemmArgs p = hdma_args<T>(c, group_m, k_chunk, ws);
   if (splits > 1) {
     if (ws == nullptr || k_chunk % (2 * T::BK) != 0) return hipErrorInvalidValue;
     const dim3 grid(p.tiles_m * p.tiles_n, splits);
@@ -1139,9 +1171,15 @@ static hipError_t launch_half(const HgemmCall& c, const HalfPlan& plan, int cus,
       if (n1 == 0 || !dma_fits<HDmaEight<E>>(head) || !dma_fits<HDmaHalfEight<E>>(tail) ||
           !dma_whole<HDmaEight<E>>(head) || !dma_whole<HDmaHalfEight<E>>(tail))
         return hipErrorInvalidValue;
-      const hipError_t e = launch_hdma<HDmaEight<E>>(head, 4, s);
-      if (e != hipSuccess) return e;
-      return launch_hdma<HDmaHalfEight<E>>(tail, 8, s);
+      using H = HDmaEight<E>;
+      using T2 = HDmaHalfEight<E>;
+      const HgemmArgs ph = hdma_args<H>(head, 4, 0, nullptr);
+      const HgemmArgs pt = hdma_args<T2>(tail, 8, 0, nullptr);
+      const int head_wgs = ph.tiles_m * ph.tiles_n;
+      hipLaunchKernelGGL((hgemm_dma_head_tail_kernel<H, T2>),
+                         dim3(head_wgs + pt.tiles_m * pt.tiles_n), dim3(H::THREADS), 0, s, ph, pt,
+                         head_wgs);
+      return hipGetLastError();
     }
     default: return hipErrorInvalidValue;
   }
