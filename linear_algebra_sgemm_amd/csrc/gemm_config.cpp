@@ -190,6 +190,7 @@ int sgemm_rule_splits(int M, int N, int K, int tile, int cus) {
   const long tiles = ceil_div(M, sgemm_tile_bm(tile)) * ceil_div(N, sgemm_tile_bn(tile));
   if (tile == 7 || tile == 9 || tile == 10) return (int)direct_splits(tiles, K, cus);
   if (tile == 12) return 1;   // measured unsplit only
+  if (tile == 13) return 1;   // splits K inside the workgroup instead
   if (tile == 11) {
     // Up to four workgroups share a CU: split only outputs of at most half as
     // many tiles as CUs, to about two workgroups per CU, in chunks of at least
@@ -260,10 +261,22 @@ SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_spl
   long s = force_splits > 0 ? force_splits
            : (tuned && force_tile < 0) ? tuned_splits
                                        : sgemm_rule_splits(M, N, K, p.tile, cus);
+  // Small outputs that would split K across workgroups (a second launch adds the
+  // partials): the 16x16 tile, whose four waves split K inside the workgroup,
+  // where its tiles fit one round (at most one per CU) and K is at most 2048.
+  // Kernel time, split choice + reduction -> tile 13: 192 x 192 x 768: 4.7 + 4.5 ->
+  // 5.1 us; 256 x 256 x 1024: 5.1 + 4.6 -> 6.5; 256 x 256 x 2048: 6.0 + 4.6 -> 10.1
+  // (but 512 x 256 x 1536, two tiles per CU: 7.3 + 4.6 -> 12.6).
+  if (force_tile < 0 && force_splits < 0 && s > 1 && K <= 2048 &&
+      ceil_div(M, 16) * ceil_div(N, 16) <= cus) {
+    p.tile = 13;
+    s = 1;
+  }
   // Legality: whole K tiles per chunk, no empty chunk, partials fit the workspace.
   const long bk = sgemm_tile_bk(p.tile);
   const long ktiles = ceil_div(K, bk);
   const long mn = (long)M * N;
+  if (p.tile == 13) s = 1;   // its waves split K; it never splits across workgroups
   if (s > kMaxSplits) s = kMaxSplits;
   if (s > ktiles) s = ktiles;
   if (mn > 0 && s > (long)(ws_floats / (size_t)mn)) s = (long)(ws_floats / (size_t)mn);

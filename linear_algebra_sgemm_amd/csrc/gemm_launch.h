@@ -54,7 +54,9 @@ inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 // 4-byte aligned, else tile 4); 9 = tile 7 with eight waves, two per SIMD; 10 = 128x128 with
 // direct-to-LDS copies at two workgroups per CU; 11 = 64x64 with direct-to-LDS
 // copies at up to four workgroups per CU (else tile 2); 12 = 32x32
-// register-staged from 16x16x4 MFMA blocks, K step 32 (small outputs).
+// register-staged from 16x16x4 MFMA blocks, K step 32 (small outputs); 13 =
+// 16x16 output tiles with K split over the workgroup's four waves, operands
+// loaded straight into registers (small outputs; any shape, never split-K).
 // HGEMM: 0 = 256x256, 1 = 128x128, 2 = 64x64 (register-staged, K step 64),
 // 3 = 256x256 direct-to-LDS, 4 stages of K step 32, 4 = 128x256 direct-to-LDS,
 // 3 stages, two workgroups per CU, 5 = 256x256 direct-to-LDS, 5 stages, 6 = 256x256
@@ -63,22 +65,27 @@ inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 // rows of A and B 16-byte aligned and B readable in whole 8-half chunks, 7 also
 // whole tiles; other operands fall back to 0); 8 = 128x128 direct-to-LDS, 4
 // stages, two workgroups per CU (other operands fall back to 1).
-constexpr int kSgemmTileCount = 13;
+constexpr int kSgemmTileCount = 14;
 constexpr int kHgemmTileCount = 9;
 
 // K granularity of each SGEMM tile configuration: the K step (32 for tiles 3
 // and 12), or for the direct-to-LDS tiles (7-11) their two-tile loop body
 // (checked against the kernels).
-constexpr int sgemm_tile_bk(int tile) { return tile == 3 || tile >= 7 ? 32 : 16; }
+constexpr int sgemm_tile_bk(int tile) { return tile == 13 ? 64 : tile == 3 || tile >= 7 ? 32 : 16; }
 // Output tile of each SGEMM configuration.
 constexpr int sgemm_tile_bm(int tile) {
   return tile == 0 || tile == 3 || tile == 5 || tile == 7 || tile == 9 ? 256
          : tile == 2 || tile == 11                                      ? 64
          : tile == 12                                                   ? 32
+         : tile == 13                                                   ? 16
                                                                         : 128;
 }
 constexpr int sgemm_tile_bn(int tile) {
-  return tile == 1 || tile == 10 ? 128 : tile == 2 || tile == 11 ? 64 : tile == 12 ? 32 : 256;
+  return tile == 1 || tile == 10 ? 128
+         : tile == 2 || tile == 11 ? 64
+         : tile == 12              ? 32
+         : tile == 13              ? 16
+                                   : 256;
 }
 
 // Split-K: at most this many K chunks per output tile.

@@ -336,6 +336,74 @@ sgemm_mfma_kernel(SgemmArgs p) {
   sgemm_store<T, STORE_EDGE>(p, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Small outputs: one 16 x 16 output tile per workgroup, its K range split over
+// the four waves (the split-K of lecture 24, section 8.3, inside one workgroup).
+// A 256^3 product gives 256 such workgroups, one per CU, and each wave runs 16
+// v_mfma_f32_16x16x4_f32 per 256 values of k; operands go straight from global
+// memory into registers (no LDS staging), and the four partial tiles meet in
+// LDS, where they are added in wave order (0 + 1 + 2 + 3, so results do not
+// change from run to run) before alpha and beta are applied.
+//
+// k mapping: for a K chunk of 64 starting at kb, MFMA step s (0..15) gives
+// k-slot h (lane / 16) the index kb + 16 h + s, so a lane's 16 A values of a
+// chunk are contiguous in its row (four 16-byte loads) and A and B agree on
+// which k each product uses.  Any M, N, K and leading dimension: loads outside
+// the matrices read zero, stores are predicated.
+// ---------------------------------------------------------------------------
+constexpr int kWksTile = 16;      // output tile edge
+constexpr int kWksChunk = 64;     // k per wave per step
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+sgemm_wave_ksplit_kernel(SgemmArgs p) {
+  __shared__ float part[4][kWksTile * kWksTile];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int m0 = (blockIdx.x / p.tiles_n) * kWksTile;
+  const int n0 = (blockIdx.x % p.tiles_n) * kWksTile;
+  const int l16 = lane % 16, h = lane / 16;
+  const int row = m0 + l16, col = n0 + l16;
+  const bool row_ok = row < p.M, col_ok = col < p.N;
+  const float* arow = p.A + (size_t)(row_ok ? row : 0) * p.lda;
+  f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int kb = wave * kWksChunk; kb < p.K; kb += 4 * kWksChunk) {
+    const int ka = kb + 16 * h;
+    float a[16], b[16];
+    if (p.a_vec && row_ok && ka + 15 < p.K) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(arow + ka + 4 * v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[4 * v + e] = x[e];
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) a[t] = (row_ok && ka + t < p.K) ? arow[ka + t] : 0.0f;
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      b[t] = (col_ok && ka + t < p.K) ? p.B[(size_t)(ka + t) * p.ldb + col] : 0.0f;
+    // two accumulators, so consecutive MFMAs do not wait for each other
+#pragma unroll
+    for (int t = 0; t < 16; t += 2) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t + 1], b[t + 1], acc1, 0, 0, 0);
+    }
+  }
+  // lane l holds column l % 16, rows 4 (l / 16) + r of this wave's partial tile
+#pragma unroll
+  for (int r = 0; r < 4; ++r) part[wave][(4 * h + r) * kWksTile + l16] = acc0[r] + acc1[r];
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int i = m0 + t / kWksTile, j = n0 + t % kWksTile;
+  if (i < p.M && j < p.N) {
+    const float sum = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
+    float* dst = p.C + (size_t)i * p.ldc + j;
+    const float v = p.alpha * sum;
+    *dst = p.beta != 0.0f ? __builtin_fmaf(p.beta, *dst, v) : v;
+  }
+}
+
 // C = beta * C (C = 0 when beta == 0, without reading C): the alpha == 0 / K == 0 case.
 __global__ void __launch_bounds__(256) sgemm_scale_kernel(int M, int N, float beta, float* C,
                                                            int ldc) {
@@ -1011,6 +1079,23 @@ int sgemm_resolve_tile(int tile, int M, int N, int K, int splits, bool operands_
   return tile;
 }
 
+static hipError_t launch_wave_ksplit(const SgemmCall& c, hipStream_t s) {
+  SgemmArgs p;
+  p.M = c.M; p.N = c.N; p.K = c.K;
+  p.alpha = c.alpha; p.beta = c.beta;
+  p.A = c.A; p.lda = c.lda; p.B = c.B; p.ldb = c.ldb; p.C = c.C; p.ldc = c.ldc;
+  p.tiles_m = (c.M + kWksTile - 1) / kWksTile;
+  p.tiles_n = (c.N + kWksTile - 1) / kWksTile;
+  p.group_m = 1;
+  p.k_chunk = c.K;
+  p.ws = nullptr;
+  p.a_vec = c.lda % 4 == 0 && aligned16(c.A);
+  p.b_vec = 0;
+  p.nb = c.N;
+  hipLaunchKernelGGL(sgemm_wave_ksplit_kernel, dim3(p.tiles_m * p.tiles_n), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hipStream_t s) {
   if (plan.splits > 1 && ws == nullptr) return hipErrorInvalidValue;
   switch (sgemm_resolve_tile(plan.tile, c.M, c.N, c.K, plan.splits, direct_operands_ok(c))) {
@@ -1027,6 +1112,7 @@ hipError_t launch_sgemm(const SgemmCall& c, const SgemmPlan& plan, float* ws, hi
     case 10: return launch_sdma<SDmaSmall>(c, plan, 8, ws, s);
     case 11: return launch_sdma<SDmaMini>(c, plan, 8, ws, s);
     case 12: return launch_tile<TileTiny>(c, plan, 8, ws, s);
+    case 13: return launch_wave_ksplit(c, s);
     default: return hipErrorInvalidValue;
   }
 }

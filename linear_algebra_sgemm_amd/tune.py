@@ -49,7 +49,7 @@ DEFAULT_TABLE = os.path.join(HERE, "csrc", "gemm_tuned.inc")
 DEFAULT_REPORT = os.path.join(ROOT, "profiles", "size_sweep.md")
 
 OPS = {"sgemm": 0, "half": 1}
-SGEMM_TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12)
+SGEMM_TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13)
 HALF_TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8)
 SPLITS = (1, 2, 4, 8, 16, 32)
 TILE_NAMES = {
@@ -57,7 +57,7 @@ TILE_NAMES = {
         5: "256x256 (16x16 MFMA)", 6: "128x256 (2 WG/CU, 16x16 MFMA)", 7: "256x256 direct",
         8: "128x256 direct (2 WG/CU)", 9: "256x256 direct, 8 waves",
         10: "128x128 direct (2 WG/CU)", 11: "64x64 direct (4 WG/CU)",
-        12: "32x32 (16x16 MFMA, BK 32)"},
+        12: "32x32 (16x16 MFMA, BK 32)", 13: "16x16, K split over 4 waves"},
     1: {0: "256x256 reg", 1: "128x128 reg", 2: "64x64 reg", 3: "256x256 direct",
         4: "128x256 direct", 5: "256x256 direct, 5 stages", 6: "256x256 direct, 8 waves",
         7: "256x256 direct, 8 waves + 128x256 tail", 8: "128x128 direct (2 WG/CU)"},

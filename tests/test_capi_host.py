@@ -300,6 +300,11 @@ def test_config_tuned_entries_are_used(so):
         op, lm, ln, lk, tile, splits = (int(g) for g in m.groups())
         M, N, K = 1 << lm, 1 << ln, 1 << lk
         got = pick(op, M, N, K)
+        if op == 0 and splits > 1 and K <= 2048 and -(-M // 16) * -(-N // 16) <= 256:
+            # small outputs that would split K across workgroups take the 16x16 tile,
+            # whose waves split K inside the workgroup
+            assert got == (13, 1), (op, M, N, K, got)
+            continue
         # tile 7 of the half products runs as 6 where the shape has no head/tail split
         assert got[0] == tile or (op, tile, got[0]) == (1, 7, 6), (op, M, N, K, got, tile)
         if op == 0 and splits * M * N <= (64 << 20) // 4 and splits <= -(-K // 32):
@@ -307,7 +312,7 @@ def test_config_tuned_entries_are_used(so):
 
 
 def bk_of(tile):
-    return 32 if tile == 3 or tile >= 7 else 16
+    return 64 if tile == 13 else 32 if tile == 3 or tile >= 7 else 16
 
 
 def test_split_legality(so):
@@ -377,7 +382,8 @@ def test_forced_splits(so):
 
 
 def test_force_tile_values(so):
-    assert lib.gemm_debug_force_tile(0, 13) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(0, 14) == lib.STATUS_INVALID_VALUE
+    assert lib.gemm_debug_force_tile(0, 13) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(0, 12) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(0, 11) == lib.STATUS_SUCCESS
     assert lib.gemm_debug_force_tile(0, 9) == lib.STATUS_SUCCESS
