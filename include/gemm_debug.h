@@ -30,7 +30,8 @@ extern "C" {
  * half products also have 3 = 256 x 256 and 4 = 128 x 256 direct-to-LDS kernels
  * 5 = the 256 x 256 one with a five-stage pipeline, 6 = the 256 x 256 one
  * with eight waves and 7 = tile 6 on the columns that fill whole rounds of
- * workgroups plus 128 x 256 tiles on the rest (whole tiles only, else the
+ * workgroups plus 128 x 256 tiles on the rest, one persistent workgroup per
+ * compute unit walking both lists (whole tiles only, else the
  * 256 x 256 register-staged kernel; 7 becomes 6 where no such split exists),
  * 8 = 128 x 128 direct-to-LDS tiles at two workgroups per compute unit (tile 1
  * where the operands do not allow direct copies).

@@ -49,6 +49,12 @@ __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t offset, u
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :: "s"(lds_base), "v"(offset), "s"(base) : "memory", "m0");
 }
+// The same with the LDS address passed through readfirstlane: for callers in
+// which the compiler cannot see that the address is wave-uniform (it is), so
+// that it stays in a scalar register.
+__device__ __forceinline__ void dma16_sbase_u(const void* base, uint32_t offset, uint32_t lds_base) {
+  dma16_sbase(base, offset, __builtin_amdgcn_readfirstlane(lds_base));
+}
 // The same with 4 bytes per lane (lane l writes LDS bytes [lds_base + 4 l, +4)):
 // for sources whose rows are only 4-byte aligned.
 __device__ __forceinline__ void dma4_sbase(const void* base, uint32_t offset, uint32_t lds_base) {

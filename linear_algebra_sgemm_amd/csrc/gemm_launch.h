@@ -61,7 +61,8 @@ inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 // 3 = 256x256 direct-to-LDS, 4 stages of K step 32, 4 = 128x256 direct-to-LDS,
 // 3 stages, two workgroups per CU, 5 = 256x256 direct-to-LDS, 5 stages, 6 = 256x256
 // direct-to-LDS with eight waves, 7 = tile 6 on the columns that fill whole
-// rounds of workgroups and 128 x 256 direct-to-LDS tiles on the rest (3 to 7 need
+// rounds of workgroups and 128 x 256 direct-to-LDS tiles on the rest, in one
+// persistent launch of one workgroup per CU where K is at least 5 steps (3 to 7 need
 // rows of A and B 16-byte aligned and B readable in whole 8-half chunks, 7 also
 // whole tiles; other operands fall back to 0); 8 = 128x128 direct-to-LDS, 4
 // stages, two workgroups per CU (other operands fall back to 1).

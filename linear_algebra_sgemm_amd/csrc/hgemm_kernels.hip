@@ -468,7 +468,7 @@ __device__ __forceinline__ void hdma_issue_tile(const HgemmArgs& p, const HDmaOf
   const uint16_t* b = b_tile + (size_t)kt * T::BK * p.ldb;
 #pragma unroll
   for (int v = 0; v < T::LOADS_PER_TILE; ++v)
-    dma16_sbase(v < T::A_PER_WAVE ? a : b, o.off[v], stage + hdma_lds_slot<T>(v, wave));
+    dma16_sbase_u(v < T::A_PER_WAVE ? a : b, o.off[v], stage + hdma_lds_slot<T>(v, wave));
 }
 
 // MFMA operand fragments of one k step of one wave.
@@ -530,13 +530,31 @@ __device__ __forceinline__ void wait_tiles_in_flight(int ahead) {
 // the reads hit a stage that is no longer used; their values are dropped.
 // STEADY: the caller guarantees kt + STAGES - 1 < ktiles (the look-ahead tile
 // exists), so the wait depth is fixed and the loads are issued unconditionally.
+// Wait until at most N + extra vector-memory operations of this wave are
+// outstanding: extra counts stores issued after the awaited copies (a previous
+// tile's epilogue in the persistent kernel) and is one of 0, 8 or 16 there;
+// any other value waits for everything, which is always safe.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_plus(int extra) {
+  if (extra == 16)
+    wait_vmcnt<N + 16>();
+  else if (extra == 8)
+    wait_vmcnt<N + 8>();
+  else if (extra == 0)
+    wait_vmcnt<N>();
+  else
+    wait_vmcnt<0>();
+}
+
+// `extra`: stores issued after this tile's awaited copies (see wait_vmcnt_plus;
+// a literal 0 everywhere but the first two tiles of a persistent kernel's tile).
 template <class T, bool STEADY>
 __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::FN][T::FM], int kt,
                                           int ktiles, HFrags<T>& x0, HFrags<T>& x1,
                                           HFrags<T>& y0, HFrags<T>& y1, const uint8_t* lds,
                                           uint32_t lds_base, const HDmaOffsets<T>& dma,
                                           const uint16_t* a_tile, const uint16_t* b_tile,
-                                          int wave, int wm, int wn, int lane) {
+                                          int wave, int wm, int wn, int lane, int extra = 0) {
   static_assert(T::KSTEPS == 2, "two k steps per tile");
   constexpr int NM = T::FM * T::FN;                  // MFMAs per k step
   constexpr int NR = T::FM + 2 * T::FN;              // LDS reads per k step
@@ -554,10 +572,16 @@ __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::F
   hmfma<T>(acc, x0, 0);
   hmfma<T>(acc, x0, 1);
   if constexpr (STEADY) {
-    wait_vmcnt<(T::STAGES - 3) * T::LOADS_PER_TILE>();
+    if (extra != 0)
+      wait_vmcnt_plus<(T::STAGES - 3) * T::LOADS_PER_TILE>(extra);
+    else
+      wait_vmcnt<(T::STAGES - 3) * T::LOADS_PER_TILE>();
   } else {
     const int left = ktiles - 2 - kt;    // tiles after kt + 1 that may stay in flight
-    wait_tiles_in_flight<T>(left < 0 ? 0 : (left < T::STAGES - 3 ? left : T::STAGES - 3));
+    if (extra != 0)
+      wait_vmcnt<0>();
+    else
+      wait_tiles_in_flight<T>(left < 0 ? 0 : (left < T::STAGES - 3 ? left : T::STAGES - 3));
   }
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -581,7 +605,7 @@ __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::F
 #pragma unroll
     for (int x = 0; x < L0; ++x)
       if (issue)
-        dma16_sbase(x < T::A_PER_WAVE ? a_issue : b_issue, dma.off[x],
+        dma16_sbase_u(x < T::A_PER_WAVE ? a_issue : b_issue, dma.off[x],
                     st_issue + hdma_lds_slot<T>(x, wave));
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -604,7 +628,7 @@ __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::F
     for (int x = L0; x < T::LOADS_PER_TILE; ++x) {
       hmfma<T>(acc, x1, TAIL + x - L0);
       if (issue)
-        dma16_sbase(x < T::A_PER_WAVE ? a_issue : b_issue, dma.off[x],
+        dma16_sbase_u(x < T::A_PER_WAVE ? a_issue : b_issue, dma.off[x],
                     st_issue + hdma_lds_slot<T>(x, wave));
     }
   } else {
@@ -614,7 +638,7 @@ __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::F
     for (int x = L0; x < T::LOADS_PER_TILE; ++x) {
       hmfma<T>(acc, x1, x - L0);
       if (issue)
-        dma16_sbase(x < T::A_PER_WAVE ? a_issue : b_issue, dma.off[x],
+        dma16_sbase_u(x < T::A_PER_WAVE ? a_issue : b_issue, dma.off[x],
                     st_issue + hdma_lds_slot<T>(x, wave));
     }
     hload_frags<T>(y1, next, 1, wm, wn, lane);
@@ -791,6 +815,250 @@ __device__ __forceinline__ void hdma_epilogue(const HgemmArgs& p, const f32x16 (
         }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent form of the column split (the FFN shape): one workgroup per CU
+// walks a list of output tiles, head tiles (shape H) then tail tiles (shape
+// T2), items g, g + G, g + 2G, ... for workgroup g of G.  After the K loop of a
+// tile, once every wave is done reading the stages, the workgroup issues the
+// direct loads of the next tile's first STAGES - 1 K tiles (and a copy of that
+// tile's bias into LDS) before it runs this tile's epilogue, so those loads are
+// in flight while the bias, GELU and stores of this tile run, and the next K
+// loop starts on landed data (the pipelined main loop of the DeepGEMM page,
+// 3.3, carried across tiles).  LDS: the K-tile ring at [0, STAGES x stage),
+// the epilogue's staging area right after the largest ring's first three
+// stages, two 1 KiB bias slots after the largest ring.
+//
+// The epilogue's stores are issued after the next tile's first loads, so the
+// first two waits of the next K loop also allow them (vmcnt counts loads and
+// stores in issue order): 16 stores per lane after a 256 x 256 tile, 8 after a
+// 128 x 256 one.
+// ---------------------------------------------------------------------------
+template <class H, class T2>
+struct HPersist {
+  static constexpr int RING = H::STAGES * H::STAGE_BYTES > T2::STAGES * T2::STAGE_BYTES
+                                  ? H::STAGES * H::STAGE_BYTES
+                                  : T2::STAGES * T2::STAGE_BYTES;
+  // staging: after the first three stages of either ring, 4 KiB per wave
+  static constexpr int STAGING = 3 * H::STAGE_BYTES > 3 * T2::STAGE_BYTES ? 3 * H::STAGE_BYTES
+                                                                          : 3 * T2::STAGE_BYTES;
+  static constexpr int STAGING_BYTES = 4096 * (H::THREADS / kWave);
+  static constexpr int BIAS = RING > STAGING + STAGING_BYTES ? RING : STAGING + STAGING_BYTES;
+  static constexpr int LDS_BYTES = BIAS + 2 * 1024;
+  static constexpr int STORES_H = H::WTM * H::WTN * 2 / 1024;    // 16-byte stores per lane
+  static constexpr int STORES_T2 = T2::WTM * T2::WTN * 2 / 1024;
+  static_assert(H::THREADS == T2::THREADS && H::WAVES_PER_SIMD == T2::WAVES_PER_SIMD,
+                "both shapes run the same workgroup");
+  static_assert(H::BN == 256 && T2::BN == 256, "a 1 KiB bias slot holds a tile's columns");
+  static_assert(H::WTN == 64 && T2::WTN == 64, "staging rows of 128 bytes");
+  static_assert(H::STAGES >= 4 && T2::STAGES >= 4, "three K tiles prefetched, one more in the ring");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(STORES_H == 16 && STORES_T2 == 8, "wait_vmcnt_plus knows 8 and 16");
+};
+
+// Issue the bias copy (every wave the same 1 KiB, at `bias_slot`) and the direct
+// loads of K tiles 0 .. STAGES - 2 of tile `t` of the launch `p`.
+template <class T>
+__device__ __forceinline__ void hpersist_issue_first(const HgemmArgs& p, int t, uint32_t lds_base,
+                                                     uint32_t bias_slot, int wave, int lane) {
+  int tile_m, tile_n;
+  tile_of_workgroup(t, p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
+  const int m0 = tile_m * T::BM, n0 = tile_n * T::BN;
+  if (p.bias != nullptr)
+    dma16_sbase_u(p.bias + n0, 16u * (uint32_t)lane, bias_slot);
+  const HDmaOffsets<T> dma(p, wave, lane, m0, n0);
+  const uint16_t* a_tile = p.A + (size_t)m0 * p.lda;
+  const uint16_t* b_tile = p.B + n0;
+#pragma unroll
+  for (int st = 0; st < T::STAGES - 1; ++st)
+    hdma_issue_tile<T>(p, dma, a_tile, b_tile, st, lds_base + st * T::STAGE_BYTES, wave);
+}
+
+// K loop of tile `t` of `p`, whose first STAGES - 1 K tiles are in flight;
+// `extra` stores were issued after them.  Whole tiles only, K a multiple of 2 BK
+// with at least STAGES K tiles.
+template <class T>
+__device__ __forceinline__ void hpersist_k_loop(const HgemmArgs& p, int t,
+                                                f32x16 (&acc)[T::FN][T::FM], uint8_t* lds,
+                                                uint32_t lds_base, int wave, int lane,
+                                                int extra) {
+  int tile_m, tile_n;
+  tile_of_workgroup(t, p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
+  const int m0 = tile_m * T::BM, n0 = tile_n * T::BN;
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+  const int ktiles = p.K / T::BK;
+  const uint16_t* a_tile = p.A + (size_t)m0 * p.lda;
+  const uint16_t* b_tile = p.B + n0;
+  const HDmaOffsets<T> dma(p, wave, lane, m0, n0);
+  HFrags<T> f0, f1, f2, f3;
+  wait_vmcnt_plus<(T::STAGES - 2) * T::LOADS_PER_TILE>(extra);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  hload_frags<T>(f0, lds, 0, wm, wn, lane);
+  hload_frags<T>(f1, lds, 1, wm, wn, lane);
+  // The first two tiles allow the extra stores in their waits.
+  hdma_tile<T, true>(p, acc, 0, ktiles, f0, f1, f2, f3, lds, lds_base, dma, a_tile, b_tile, wave,
+                     wm, wn, lane, extra);
+  hdma_tile<T, true>(p, acc, 1, ktiles, f2, f3, f0, f1, lds, lds_base, dma, a_tile, b_tile, wave,
+                     wm, wn, lane, extra);
+  int kt = 2;
+  for (; kt + T::STAGES < ktiles; kt += 2) {
+    hdma_tile<T, true>(p, acc, kt, ktiles, f0, f1, f2, f3, lds, lds_base, dma, a_tile, b_tile,
+                       wave, wm, wn, lane);
+    hdma_tile<T, true>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, dma, a_tile, b_tile,
+                       wave, wm, wn, lane);
+  }
+  for (; kt < ktiles; kt += 2) {
+    hdma_tile<T, false>(p, acc, kt, ktiles, f0, f1, f2, f3, lds, lds_base, dma, a_tile, b_tile,
+                        wave, wm, wn, lane);
+    hdma_tile<T, false>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, dma, a_tile,
+                        b_tile, wave, wm, wn, lane);
+  }
+}
+
+// Epilogue of tile `t` of `p` with its bias in LDS at `bias`: x = alpha acc +
+// bias, the activation, 16-bit rounding; each wave stages 32 rows (4 KiB) at a
+// time in its part of the staging area and stores them as whole rows.  Issues
+// exactly WTM * WTN * 2 / 1024 stores per lane.
+template <class T>
+__device__ __forceinline__ void hpersist_epilogue(const HgemmArgs& p, int t,
+                                                  const f32x16 (&acc)[T::FN][T::FM],
+                                                  const float* bias, uint8_t* staging, int wave,
+                                                  int lane) {
+  int tile_m, tile_n;
+  tile_of_workgroup(t, p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
+  const int m0 = tile_m * T::BM, n0 = tile_n * T::BN;
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+  const float alpha = p.alpha;
+  const Activation act(p.act);
+  const bool has_bias = p.bias != nullptr;
+  constexpr int RB = T::WTN * 2;    // 128 bytes per row of a wave's tile
+  constexpr int CPR = RB / 16;      // 8 chunks per row
+  constexpr int RPL = 256 / RB;     // 2 rows per 256 bytes
+  uint8_t* region = staging + wave * 4096;
+  float bv[T::FN][4][4];
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int cl = wn * T::WTN + 32 * j + 8 * q + 4 * (lane / 32);
+      const f32x4 b4 = has_bias ? *reinterpret_cast<const f32x4*>(bias + cl)
+                                : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[j][q][e] = b4[e];
+    }
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {   // block row i = rows 32 i .. 32 i + 31 of the wave's tile
+    const int r = lane % 32;
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          h[e] = T::E::bits(act(__builtin_fmaf(alpha, acc[j][i][4 * q + e], bv[j][q][e])));
+        const int chunk = 4 * j + q;
+        *reinterpret_cast<uint2*>(region + r * RB + 16 * (chunk ^ ((r / RPL) % CPR)) +
+                                  8 * (lane / 32)) = __builtin_bit_cast(uint2, h);
+      }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int rr = it * (1024 / RB) + lane / CPR;
+      const int chunk = lane % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(region + rr * RB +
+                                                      16 * (chunk ^ ((rr / RPL) % CPR)));
+      *reinterpret_cast<u32x4*>(p.C + (size_t)(m0 + wm * T::WTM + 32 * i + rr) * p.ldc + n0 +
+                                wn * T::WTN + 8 * chunk) = v;
+    }
+  }
+}
+
+// The launch arguments of the tail tiles: the columns from n1 on.
+template <class T2>
+__device__ __forceinline__ HgemmArgs hpersist_tail_args(const HgemmArgs& p, int n1) {
+  HgemmArgs t = p;
+  t.N = p.N - n1;
+  t.B = p.B + n1;
+  t.C = p.C + n1;
+  t.bias = p.bias != nullptr ? p.bias + n1 : nullptr;
+  t.nb = p.nb - n1;
+  t.tiles_m = p.M / T2::BM;
+  t.tiles_n = t.N / T2::BN;
+  t.group_m = p.k_chunk;   // the tail's tile order (k_chunk is unused by these tiles)
+  return t;
+}
+
+// `p`: the head launch (columns [0, n1), tiles_m x tiles_n tiles of H); the
+// tail tiles (shape T2) cover columns [n1, N).
+template <class H, class T2>
+__global__ void __launch_bounds__(H::THREADS) __attribute__((amdgpu_waves_per_eu(H::WAVES_PER_SIMD)))
+hgemm_dma_persistent_kernel(HgemmArgs p, int n1) {
+  using L = HPersist<H, T2>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L::LDS_BYTES];
+  const int lane0 = threadIdx.x % kWave;
+  const int lane = lane0;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const uint32_t lds_base = lds_offset(lds);
+  const int G = gridDim.x;
+  const int head_items = p.tiles_m * p.tiles_n;
+  const int total_items = head_items + (p.M / T2::BM) * ((p.N - n1) / T2::BN);
+  int item = blockIdx.x;
+  if (item >= total_items) return;
+  uint8_t* staging = lds + L::STAGING;
+  int n = 0, extra = 0;
+  if (item < head_items) {
+    hpersist_issue_first<H>(p, item, lds_base, lds_base + L::BIAS, wave, lane);
+    for (; item < head_items; item += G, ++n) {
+      // Per-lane addresses are recomputed in every iteration rather than held
+      // across the loop: opaque copies of the lane and the LDS base keep the
+      // compiler from hoisting them (they would not fit beside the accumulators).
+      int lane = lane0;
+      asm volatile("" : "+v"(lane));
+      const int next = item + G;
+      const uint32_t next_bias =
+          __builtin_amdgcn_readfirstlane(lds_base + L::BIAS + ((n + 1) & 1) * 1024);
+      f32x16 acc[H::FN][H::FM];
+      hpersist_k_loop<H>(p, item, acc, lds, lds_base, wave, lane, extra);
+      lds_barrier();   // every wave is done reading the ring
+      if (next < head_items)
+        hpersist_issue_first<H>(p, next, lds_base, next_bias, wave, lane);
+      else if (next < total_items)
+        hpersist_issue_first<T2>(hpersist_tail_args<T2>(p, n1), next - head_items, lds_base,
+                                 next_bias, wave, lane);
+      hpersist_epilogue<H>(p, item, acc,
+                           reinterpret_cast<const float*>(lds + L::BIAS + (n & 1) * 1024), staging,
+                           wave, lane);
+      extra = L::STORES_H;
+    }
+  } else {
+    hpersist_issue_first<T2>(hpersist_tail_args<T2>(p, n1), item - head_items, lds_base,
+                             lds_base + L::BIAS, wave, lane);
+  }
+  const HgemmArgs t = hpersist_tail_args<T2>(p, n1);
+  for (; item < total_items; item += G, ++n) {
+    int lane = lane0;
+    asm volatile("" : "+v"(lane));
+    const int next = item + G;
+    const uint32_t next_bias =
+        __builtin_amdgcn_readfirstlane(lds_base + L::BIAS + ((n + 1) & 1) * 1024);
+    f32x16 acc[T2::FN][T2::FM];
+    hpersist_k_loop<T2>(t, item - head_items, acc, lds, lds_base, wave, lane, extra);
+    lds_barrier();
+    if (next < total_items)
+      hpersist_issue_first<T2>(t, next - head_items, lds_base, next_bias, wave, lane);
+    hpersist_epilogue<T2>(t, item - head_items, acc,
+                          reinterpret_cast<const float*>(lds + L::BIAS + (n & 1) * 1024), staging,
+                          wave, lane);
+    extra = L::STORES_T2;
   }
 }
 
@@ -1176,9 +1444,22 @@ static hipError_t launch_half(const HgemmCall& c, const HalfPlan& plan, int cus,
       const HgemmArgs ph = hdma_args<H>(head, 4, 0, nullptr);
       const HgemmArgs pt = hdma_args<T2>(tail, 8, 0, nullptr);
       const int head_wgs = ph.tiles_m * ph.tiles_n;
-      hipLaunchKernelGGL((hgemm_dma_head_tail_kernel<H, T2>),
-                         dim3(head_wgs + pt.tiles_m * pt.tiles_n), dim3(H::THREADS), 0, s, ph, pt,
-                         head_wgs);
+      const int total = head_wgs + pt.tiles_m * pt.tiles_n;
+      if (c.K / H::BK >= H::STAGES + 2) {
+        // One workgroup per CU walks its tiles, loading the next tile's first K
+        // tiles under the current tile's epilogue.  The tail's arguments are
+        // derived in the kernel from the head's (k_chunk carries its tile order).
+        HgemmArgs pp = ph;
+        pp.k_chunk = pt.group_m;
+        pp.N = c.N;
+        pp.nb = readable_cols(c.nb, c.N);
+        const int grid = total < cus ? total : cus;
+        hipLaunchKernelGGL((hgemm_dma_persistent_kernel<H, T2>), dim3(grid), dim3(H::THREADS), 0,
+                           s, pp, n1);
+        return hipGetLastError();
+      }
+      hipLaunchKernelGGL((hgemm_dma_head_tail_kernel<H, T2>), dim3(total), dim3(H::THREADS), 0, s,
+                         ph, pt, head_wgs);
       return hipGetLastError();
     }
     default: return hipErrorInvalidValue;
