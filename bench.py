@@ -93,28 +93,42 @@ def parse_args():
     p.add_argument("--swizzle", default=None, metavar="GROUP,REMAP",
                    help="tile order for a counter comparison: rows per group (0 = each "
                         "launch's own) and the XCD renumbering (1 on, 0 off)")
+    p.add_argument("--headline-first", action="store_true",
+                   help="time --workload before the per-dtype workloads instead of after them")
     p.add_argument("--no-extras", action="store_true",
                    help="time only --workload (by default the 4096^3 FP32 run also times the "
                         "binary16 and bfloat16 FFN products)")
     return p.parse_args()
 
 
-def profiled_traffic(workload: str, op: str):
-    """HBM bytes per call (all kernels of one call) from the committed rocprofv3 counter
-    summary of this workload, or None when there is none or the sources that decide
-    what the call runs changed since it was taken."""
+def profiled_figures(workload: str, op: str):
+    """Figures per call from the committed rocprofv3 counter summary of this workload:
+    HBM bytes ("traffic"), the effective clock and MfmaUtil under the counter passes;
+    None when there is no summary or the sources that decide what the call runs
+    changed since it was taken."""
     path = os.path.join(PROFILES, "%s_counters.md" % workload)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m_src and m_bytes):
+    if not m_src:
         return None
     from linear_algebra_sgemm_amd.profile_summary import source_digest
     if m_src.group(1) != source_digest(op):
         return None
-    return float(m_bytes.group(1))
+    out = {}
+    for key, name in (("traffic", "hbm_bytes_per_launch"), ("effective_clock_ghz",
+                                                           "effective_clock_ghz"),
+                      ("mfma_util_pct", "mfma_util_pct")):
+        m = re.search(r"%s:\s*([0-9.eE+]+)" % name, text)
+        out[key] = float(m.group(1)) if m else None
+    return out
+
+
+def profiled_traffic(workload: str, op: str):
+    """HBM bytes per call from the committed counter summary, or None (see profiled_figures)."""
+    f = profiled_figures(workload, op)
+    return None if f is None else f["traffic"]
 
 
 def cpu_baseline(w, A, B, C, target_seconds: float):
@@ -255,7 +269,8 @@ def call_stats(ms):
     p90 = srt[min(len(srt) - 1, int(round(0.9 * (len(srt) - 1))))]
     return {"mean": round(statistics.fmean(ms), 5), "median": round(statistics.median(ms), 5),
             "min": round(min(ms), 5), "p90": round(p90, 5), "max": round(max(ms), 5),
-            "stdev": round(statistics.stdev(ms), 5) if len(ms) > 1 else 0.0}
+            "stdev": round(statistics.stdev(ms), 5) if len(ms) > 1 else 0.0,
+            "first": [round(x, 4) for x in ms[:8]], "last": [round(x, 4) for x in ms[-8:]]}
 
 
 def kernel_label(w, dtype: str) -> str:
@@ -321,10 +336,13 @@ def main():
     # calls (the reporting rule of these workloads); the headline takes exactly
     # --steps after --warmup.
     runs = {}
+    if args.headline_first:
+        runs[w.name] = time_workload(w, steps, args.warmup)
     for name in extras:
         runs[name] = time_workload(inputs.WORKLOADS[name], max(steps, EXTRA_MIN_STEPS),
                                    max(args.warmup, EXTRA_MIN_WARMUP))
-    runs[w.name] = time_workload(w, steps, args.warmup)
+    if not args.headline_first:
+        runs[w.name] = time_workload(w, steps, args.warmup)
     lib.gemm_destroy()
 
     def dtype_of(wl):
@@ -385,6 +403,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": profiled_traffic(w.name, w.op),
+                     "profiled": profiled_figures(w.name, w.op),
                      "algorithmic_bytes": nbytes,
                      "kernel": kernel_label(w, dtype)},
         "cpu_baseline": cpu,

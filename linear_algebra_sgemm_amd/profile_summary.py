@@ -265,9 +265,26 @@ def counters_markdown(workload: str, op: str, flops: int, algo_bytes: int, copy_
                 lines.append("| `%s` | %s | %s | %s | %s | %s | %s |"
                              % (name, r.get("vgprs"), r.get("agprs"), r.get("sgprs"),
                                 r.get("scratch"), r.get("lds"), r.get("occupancy")))
+    # Call-level figures (duration-weighted over the call's kernels): the effective
+    # clock where the dispatches are long enough, and MfmaUtil.
+    clk_cycles = clk_ns = util_ns = util_sum = 0.0
+    for cs in kernels.values():
+        durs = cs.get("_durations", {})
+        d = durs.get("GRBM_GUI_ACTIVE")
+        if "GRBM_GUI_ACTIVE" in cs and d and d >= MIN_CLOCK_NS:
+            clk_cycles += cs["GRBM_GUI_ACTIVE"] / XCDS
+            clk_ns += d
+        d = durs.get("MfmaUtil")
+        if "MfmaUtil" in cs and d:
+            util_sum += cs["MfmaUtil"] * d
+            util_ns += d
     lines += ["", "kernel_source_sha256: %s" % source_digest(op)]
     if hbm is not None:
         lines.append("hbm_bytes_per_launch: %.0f" % hbm)
+    if clk_ns > 0:
+        lines.append("effective_clock_ghz: %.3f" % (clk_cycles / clk_ns))
+    if util_ns > 0:
+        lines.append("mfma_util_pct: %.2f" % (util_sum / util_ns))
     return "\n".join(lines) + "\n"
 
 

@@ -39,6 +39,7 @@ def test_counter_summary_figures():
     assert "0 of 3.369e+07 active LDS cycles (0.00 %)" in text
     assert "| `%s` | 2 | MfmaUtil | 88.4137 |" % KERNEL in text
     assert "kernel_source_sha256: %s" % ps.source_digest("sgemm") in text
+    assert "effective_clock_ghz: 2.104" in text and "mfma_util_pct: 88.41" in text
 
 
 def test_trace_summary_table():
