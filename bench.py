@@ -9,7 +9,9 @@ U[-1, 1] from seed 1).  C is restored from a pristine copy before every call,
 outside the timed events.  Each call is bracketed by HIP events on the stream
 it is launched on (created without the system-scope fence, which would write
 back and invalidate the caches at every record inside the timed interval);
-TFLOP/s = 2*M*N*K / mean call time.  The default run also times the
+TFLOP/s = 2*M*N*K / mean call time.  Before its --warmup calls each workload
+runs untimed until its call time stops falling (the card's clock settles over
+the first tens of calls; at most --settle-seconds).  The default run also times the
 inference-FFN product (M = 4096, N = 14336, K = 4096, bias + GELU) in binary16
 and in bfloat16, for the percentage of the matrix peak of each dtype.  After
 the GPU phase, every element of each workload's first timed output is compared
@@ -93,6 +95,9 @@ def parse_args():
     p.add_argument("--swizzle", default=None, metavar="GROUP,REMAP",
                    help="tile order for a counter comparison: rows per group (0 = each "
                         "launch's own) and the XCD renumbering (1 on, 0 off)")
+    p.add_argument("--settle-seconds", type=float, default=SETTLE_MAX_S,
+                   help="longest untimed settling phase per workload before its warm-up "
+                        "calls (0 = none); it ends once the call time stops falling")
     p.add_argument("--headline-first", action="store_true",
                    help="time --workload before the per-dtype workloads instead of after them")
     p.add_argument("--no-extras", action="store_true",
@@ -201,10 +206,55 @@ def parity(w, A, B, C, got):
             "oracle_s": round(time.perf_counter() - t0, 2)}
 
 
-def time_workload(w, steps: int, warmup: int):
-    """Warm-up calls, then `steps` timed calls of one workload on the current stream.
-    Returns the per-call times (ms), the host inputs and a copy of the first timed
-    call's output (taken after its end event, outside the timed interval)."""
+# Settling: untimed calls before the warm-up calls, in groups of SETTLE_GROUP, until
+# the median call time of a group is no longer SETTLE_DROP below the previous
+# group's (at least SETTLE_MIN_GROUPS groups, at most SETTLE_MAX_S seconds).  A card
+# that has been idle raises its clock over the first tens of calls, and one that
+# has just run power-limited 16-bit work starts the next workload at a lower clock;
+# five warm-up calls do not cover that (4096^3 FP32: 1.08 ms for the first calls,
+# 0.94 ms once settled).
+SETTLE_GROUP = 10
+SETTLE_MIN_GROUPS = 3
+SETTLE_DROP = 0.005
+SETTLE_MAX_S = 3.0
+
+
+def settle(call, reset, handle, max_s: float):
+    """Untimed calls until the per-call time has stopped falling; returns their count
+    and the median call time (ms) of each group."""
+    import torch
+
+    if max_s <= 0:
+        return 0, []
+    timer = HipTimer(2 * SETTLE_GROUP)
+    medians = []
+    t0 = time.perf_counter()
+    calls = 0
+    try:
+        while True:
+            for i in range(SETTLE_GROUP):
+                reset()
+                timer.record(2 * i, handle)
+                call()
+                timer.record(2 * i + 1, handle)
+            torch.cuda.synchronize()
+            calls += SETTLE_GROUP
+            medians.append(statistics.median(timer.elapsed_ms(2 * i, 2 * i + 1)
+                                             for i in range(SETTLE_GROUP)))
+            settled = (len(medians) >= SETTLE_MIN_GROUPS and
+                       medians[-1] >= (1.0 - SETTLE_DROP) * medians[-2])
+            if settled or time.perf_counter() - t0 > max_s:
+                break
+    finally:
+        timer.close()
+    return calls, [round(m, 4) for m in medians]
+
+
+def time_workload(w, steps: int, warmup: int, settle_s: float = SETTLE_MAX_S):
+    """Settling calls, warm-up calls, then `steps` timed calls of one workload on the
+    current stream.  Returns the per-call times (ms), the settling record, the host
+    inputs and a copy of the first timed call's output (taken after its end event,
+    outside the timed interval)."""
     import torch
 
     import linear_algebra_sgemm_amd as lib
@@ -236,13 +286,14 @@ def time_workload(w, steps: int, warmup: int):
         def reset():
             pass
 
+    handle = stream.cuda_stream
+    settle_calls, settle_ms = settle(call, reset, handle, settle_s)
     for _ in range(warmup):
         reset()
         call()
     torch.cuda.synchronize()
 
     timer = HipTimer(2 * steps)
-    handle = stream.cuda_stream
     first = torch.empty_like(dC)
     if w.op != "sgemm":
         dC.fill_(float("nan"))   # the first timed call must write every element itself
@@ -261,7 +312,8 @@ def time_workload(w, steps: int, warmup: int):
     timer.close()
     out = first.cpu()
     del dA, dB, dC, first
-    return {"ms": ms, "wall_s": wall, "inputs": (A, B, C), "first": out}
+    return {"ms": ms, "wall_s": wall, "inputs": (A, B, C), "first": out,
+            "settle": {"calls": settle_calls, "group_median_ms": settle_ms}}
 
 
 def call_stats(ms):
@@ -337,12 +389,12 @@ def main():
     # --steps after --warmup.
     runs = {}
     if args.headline_first:
-        runs[w.name] = time_workload(w, steps, args.warmup)
+        runs[w.name] = time_workload(w, steps, args.warmup, args.settle_seconds)
     for name in extras:
         runs[name] = time_workload(inputs.WORKLOADS[name], max(steps, EXTRA_MIN_STEPS),
-                                   max(args.warmup, EXTRA_MIN_WARMUP))
+                                   max(args.warmup, EXTRA_MIN_WARMUP), args.settle_seconds)
     if not args.headline_first:
-        runs[w.name] = time_workload(w, steps, args.warmup)
+        runs[w.name] = time_workload(w, steps, args.warmup, args.settle_seconds)
     lib.gemm_destroy()
 
     def dtype_of(wl):
@@ -356,7 +408,7 @@ def main():
         tf = cost.gemm_flops(wl.M, wl.N, wl.K) / (st["mean"] * 1e-3) / 1e12
         entry = {"workload": name, "steps": len(r["ms"]), "tflops": round(tf, 3),
                  "pct_of_peak": round(100.0 * tf / cost.PEAK_TFLOPS[dt], 2),
-                 "peak_tflops": cost.PEAK_TFLOPS[dt], "call_ms": st,
+                 "peak_tflops": cost.PEAK_TFLOPS[dt], "call_ms": st, "settle": r["settle"],
                  "kernel": kernel_label(wl, dt)}
         if not args.no_parity:
             A, B, C = r["inputs"]
@@ -381,6 +433,7 @@ def main():
         "n_gpus": 1,
         "steps": steps,
         "warmup": args.warmup,
+        "settle": main_run["settle"],
         "ms_per_step": round(main_run["wall_s"] / steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -394,7 +447,9 @@ def main():
                    "tile_order": args.swizzle or "default",
                    "timing": "per-call HIP events (no system-scope fence) on the launch "
                              "stream, C reset before each call outside the events; "
-                             "ms_per_step is wall time per step including that reset"},
+                             "untimed settling calls until the call time stops falling, "
+                             "then the warm-up calls; ms_per_step is wall time per step "
+                             "including that reset"},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "call_ms": st,
         "parity_max_err": None if par is None else par["max_err"],
