@@ -630,6 +630,7 @@ __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::F
       if (issue)
         dma16_sbase_u(x < T::A_PER_WAVE ? a_issue : b_issue, dma.off[x],
                     st_issue + hdma_lds_slot<T>(x, wave));
+      __builtin_amdgcn_sched_barrier(0);   // one copy between two MFMAs
     }
   } else {
     // Few MFMAs per k step (the 128 x 256 tile): loads first, so the reads are
@@ -640,6 +641,7 @@ __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::F
       if (issue)
         dma16_sbase_u(x < T::A_PER_WAVE ? a_issue : b_issue, dma.off[x],
                     st_issue + hdma_lds_slot<T>(x, wave));
+      __builtin_amdgcn_sched_barrier(0);   // one copy between two MFMAs
     }
     hload_frags<T>(y1, next, 1, wm, wn, lane);
 #pragma unroll

@@ -662,6 +662,7 @@ __device__ __forceinline__ void sdma_tile(const SgemmArgs& p, f32x16 (&acc)[T::F
     for (int x = 0; x < T::LOADS_PER_TILE; ++x) {
       smfma<T>(acc, x1, TAIL + x);
       if (issue) sdma_issue<T>(p, plan, a_tile, b_tile, kt_issue, st_issue, wave, x);
+      __builtin_amdgcn_sched_barrier(0);   // one copy between two MFMAs
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -724,6 +725,7 @@ __device__ __forceinline__ void sdma_tile_pair(const SgemmArgs& p, f32x16 (&acc)
         sdma_issue<T>(p, plan, a_tile, b_tile, kt_issue,
                       lds_base + (kt_issue % T::STAGES) * T::STAGE_BYTES, wave,
                       x % T::LOADS_PER_TILE);
+      __builtin_amdgcn_sched_barrier(0);   // one copy between two MFMAs
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -787,6 +789,7 @@ __device__ __forceinline__ void sdma_tile2(const SgemmArgs& p, f32x16 (&acc)[T::
   for (int x = 0; x < T::LOADS_PER_TILE; ++x) {
     smfma<T>(acc, x1, TAIL + x);
     if (issue) sdma_issue<T>(p, plan, a_tile, b_tile, kt_issue, st_issue, wave, x);
+    __builtin_amdgcn_sched_barrier(0);   // one copy between two MFMAs
   }
   __builtin_amdgcn_sched_barrier(0);
 }
