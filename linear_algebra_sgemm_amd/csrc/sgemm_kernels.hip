@@ -492,6 +492,10 @@ struct SDmaTile {
   static_assert((STAGES - 2) * LOADS_PER_TILE <= 63, "in-flight copies must fit vmcnt");
   static_assert(FM * FN * 16 <= 256 / WAVES_PER_SIMD, "accumulators must leave room for operands");
   static_assert(!PAIR || (STAGES == 4 && !LEAN), "two tiles in use and two in flight");
+  // A ragged K's last values go through the pipeline before the main loop on the
+  // tiles narrower than 256 x 256 (measured faster there); the 256 x 256 tiles
+  // take them after the loop.
+  static constexpr bool TAIL_FIRST = BM * BN < 256 * 256;
 };
 
 // Per-lane byte offsets of a wave's copies relative to the K tile's A or B base
@@ -794,49 +798,54 @@ __device__ __forceinline__ void sdma_tile2(const SgemmArgs& p, f32x16 (&acc)[T::
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// The last K - K % 32 < 32 values of k on a ragged K: both stages 0 and 1 are
-// filled with bounds-checked loads and plain LDS stores, in the layout the
-// copies produce (zeros for k >= K, clamped rows and columns as in SDmaPlan),
-// and the MFMAs of the two 16-wide K tiles follow.  Called by every wave after
-// the main loop.
+// The last K - k0 < 32 values of k on a ragged K: one 16-wide K tile at a time
+// through stage STAGES - 1, filled with bounds-checked loads and plain LDS
+// stores in the layout the copies produce (zeros for k >= K, clamped rows and
+// columns as in SDmaPlan), then the MFMAs of that tile.  TAIL_FIRST tiles call
+// it before the main loop, right after the prologue's copies are issued (that
+// stage is then free), so the latency of these loads overlaps theirs; at the
+// end of the K loop it was exposed (1000x3000x777 took longer than the same
+// product with K = 800).  The main loop's first copy into that stage goes out
+// after the first K tile's barrier, which a wave reaches only after its MFMAs
+// here have consumed their fragments.  The other tiles call it after the main
+// loop, behind a barrier.
 template <class T>
-__device__ __forceinline__ void sdma_k_tail(const SgemmArgs& p, f32x16 (&acc)[T::FM][T::FN],
-                                            uint8_t* lds, int k0, int m0, int n0, int wm, int wn,
-                                            int lane) {
-  lds_barrier();   // every wave is done reading the stages
+__device__ __forceinline__ void sdma_k_tail(const SgemmArgs& p,
+                                                  f32x16 (&acc)[T::FM][T::FN], uint8_t* lds,
+                                                  int k0, int m0, int n0, int wm, int wn,
+                                                  int lane) {
+  uint8_t* const st = lds + (T::STAGES - 1) * T::STAGE_BYTES;
   const int tid = threadIdx.x;
-  // A: BM rows x 8 chunks of 4 k (two tiles of four chunks).
-  for (int c = tid; c < T::BM * 8; c += T::THREADS) {
-    const int r = c / 8, t = (c % 8) / 4, chunk = c % 4;
-    const int row = m0 + r < p.M ? m0 + r : p.M - 1;
-    const int k = k0 + 16 * t + 4 * chunk;
-    f32x4 v;
+  for (int kb = k0; kb < p.K; kb += T::BK) {
+    if (kb > k0) lds_barrier();   // every wave is done reading the previous tail tile
+    // A: BM rows x 4 chunks of 4 k.
+    for (int c = tid; c < T::BM * 4; c += T::THREADS) {
+      const int r = c / 4, chunk = c % 4;
+      const int row = m0 + r < p.M ? m0 + r : p.M - 1;
+      const int k = kb + 4 * chunk;
+      f32x4 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = k + e < p.K ? p.A[(size_t)row * p.lda + k + e] : 0.0f;
-    *reinterpret_cast<f32x4*>(lds + t * T::STAGE_BYTES + r * 64 +
-                              16 * (chunk ^ row64_swizzle(r))) = v;
-  }
-  // B: 32 rows of k x BN / 4 chunks of 4 columns.
-  for (int c = tid; c < 32 * (T::BN / 4); c += T::THREADS) {
-    const int kr = c / (T::BN / 4), cc = 4 * (c % (T::BN / 4));
-    const int t = kr / 16;
-    const int k = k0 + kr;
-    const int col = n0 + cc < p.nb ? n0 + cc : p.nb - 4;
-    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (k < p.K) v = *reinterpret_cast<const f32x4*>(p.B + (size_t)k * p.ldb + col);
-    *reinterpret_cast<f32x4*>(lds + t * T::STAGE_BYTES + T::A_BYTES + T::b_row(kr % 16) +
-                              4 * cc) = v;
-  }
-  lds_barrier();
-  SFrags<T> f;
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
+      for (int e = 0; e < 4; ++e) v[e] = k + e < p.K ? p.A[(size_t)row * p.lda + k + e] : 0.0f;
+      *reinterpret_cast<f32x4*>(st + r * 64 + 16 * (chunk ^ row64_swizzle(r))) = v;
+    }
+    // B: 16 rows of k x BN / 4 chunks of 4 columns.
+    for (int c = tid; c < T::BK * (T::BN / 4); c += T::THREADS) {
+      const int kr = c / (T::BN / 4), cc = 4 * (c % (T::BN / 4));
+      const int k = kb + kr;
+      const int col = n0 + cc < p.nb ? n0 + cc : p.nb - 4;
+      f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (k < p.K) v = *reinterpret_cast<const f32x4*>(p.B + (size_t)k * p.ldb + col);
+      *reinterpret_cast<f32x4*>(st + T::A_BYTES + T::b_row(kr) + 4 * cc) = v;
+    }
+    lds_barrier();
+    SFrags<T> f;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      sload_frags<T>(f, lds + t * T::STAGE_BYTES, g, wm, wn, lane);
+      sload_frags<T>(f, st, g, wm, wn, lane);
 #pragma unroll
       for (int x = 0; x < 4 * T::FM * T::FN; ++x) smfma<T>(acc, f, x);
     }
+  }
 }
 
 template <class T, bool SPLIT, bool EDGE>
@@ -885,14 +894,18 @@ sgemm_dma_kernel(SgemmArgs p) {
   const float* b_tile = p.B + n0;
   const SDmaPlan<T> plan(p, wave, lane, m0, n0);
   SFrags<T> f0, f1, f2, f3;
+#pragma unroll
+  for (int st = 0; st < T::STAGES - 1; ++st)
+    if (st < ktiles) {
+#pragma unroll
+      for (int x = 0; x < T::LOADS_PER_TILE; ++x)
+        sdma_issue<T>(p, plan, a_tile, b_tile, st, lds_base + st * T::STAGE_BYTES, wave, x);
+    }
+  if constexpr (EDGE && T::TAIL_FIRST) {
+    if (ktiles * T::BK < p.K)
+      sdma_k_tail<T>(p, acc, lds, ktiles * T::BK, m0, n0, wm, wn, lane);
+  }
   if (ktiles > 0) {
-#pragma unroll
-    for (int st = 0; st < T::STAGES - 1; ++st)
-      if (st < ktiles) {
-#pragma unroll
-        for (int x = 0; x < T::LOADS_PER_TILE; ++x)
-          sdma_issue<T>(p, plan, a_tile, b_tile, st, lds_base + st * T::STAGE_BYTES, wave, x);
-      }
     swait_tiles<T>(ktiles - 1 < T::STAGES - 2 ? ktiles - 1 : T::STAGES - 2);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -936,8 +949,11 @@ sgemm_dma_kernel(SgemmArgs p) {
                           b_tile, wave, wm, wn, lane);
     }
   }
-  if constexpr (EDGE) {
-    if (ktiles * T::BK < p.K) sdma_k_tail<T>(p, acc, lds, ktiles * T::BK, m0, n0, wm, wn, lane);
+  if constexpr (EDGE && !T::TAIL_FIRST) {
+    if (ktiles * T::BK < p.K) {
+      lds_barrier();   // every wave is done reading the stages
+      sdma_k_tail<T>(p, acc, lds, ktiles * T::BK, m0, n0, wm, wn, lane);
+    }
   }
   if constexpr (SPLIT) {
     // Raw partial sums into this K chunk's slice of the workspace.
