@@ -692,7 +692,10 @@ __device__ __forceinline__ void sdma_tile_pair(const SgemmArgs& p, f32x16 (&acc)
   constexpr int PRE = 2;
   constexpr int R0 = (NR + NM - PRE - 1) / (NM - PRE);
   constexpr int NCOPY = BAR ? 2 * T::LOADS_PER_TILE : 0;
-  constexpr int TAIL = NM - NCOPY;
+  // Where a wave has more copies than MFMAs to spread them over (the 64 x 64
+  // tile), they go out together after the group's MFMAs (BURST).
+  constexpr bool BURST = !(NM - NCOPY >= NR / 2 && NM - NCOPY >= 1);
+  constexpr int TAIL = BURST ? NM : NM - NCOPY;
   constexpr int R1 = (NR + TAIL - 1) / TAIL;
   static_assert(TAIL >= NR / 2 && TAIL >= 1, "enough MFMAs to spread the reads over");
   smfma<T>(acc, x0, 0);
@@ -723,13 +726,13 @@ __device__ __forceinline__ void sdma_tile_pair(const SgemmArgs& p, f32x16 (&acc)
   if constexpr (BAR) {
 #pragma unroll
     for (int x = 0; x < NCOPY; ++x) {
-      smfma<T>(acc, x1, TAIL + x);
+      if constexpr (!BURST) smfma<T>(acc, x1, TAIL + x);
       const int kt_issue = kt + 3 + x / T::LOADS_PER_TILE;
       if (STEADY || kt_issue < ktiles)
         sdma_issue<T>(p, plan, a_tile, b_tile, kt_issue,
                       lds_base + (kt_issue % T::STAGES) * T::STAGE_BYTES, wave,
                       x % T::LOADS_PER_TILE);
-      __builtin_amdgcn_sched_barrier(0);   // one copy between two MFMAs
+      if constexpr (!BURST) __builtin_amdgcn_sched_barrier(0);   // one copy between two MFMAs
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -1017,10 +1020,10 @@ using SDmaTall = SDmaTile<128, 256, 3, 2, 2, 2, false, true>;
 using SDmaEight = SDmaTile<256, 256, 4, 2, 2, 4, false, false, true>;
 // 128 x 128 with four waves of 64 x 64, 4 stages of 16.5 KiB, two workgroups per CU:
 // outputs with too few 256 x 256 tiles to fill the CUs.
-using SDmaSmall = SDmaTile<128, 128, 4, 2, 2, 2>;
+using SDmaSmall = SDmaTile<128, 128, 4, 2, 2, 2, false, false, true>;
 // 64 x 64 with four waves of 32 x 32, 4 stages of 8.5 KiB, up to four workgroups
 // per CU: small and mid-size outputs (about 100 to 1000 tiles), spread evenly.
-using SDmaMini = SDmaTile<64, 64, 4, 4, 2, 2>;
+using SDmaMini = SDmaTile<64, 64, 4, 4, 2, 2, false, false, true>;
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
