@@ -897,6 +897,22 @@ sgemm_dma_kernel(SgemmArgs p) {
   const float* b_tile = p.B + n0;
   const SDmaPlan<T> plan(p, wave, lane, m0, n0);
   SFrags<T> f0, f1, f2, f3;
+  // A wave of the 64 x 64 tile holds one 32 x 32 block: it loads its 16 values of
+  // C per lane before the K loop (when beta != 0), so their latency overlaps the
+  // loop instead of the epilogue.  Issued before the copies: the K loop's
+  // count-based waits then also cover them.
+  constexpr bool PRE_C = T::FM * T::FN == 1 && !SPLIT;
+  float cpre[16] = {};
+  if constexpr (PRE_C) {
+    if (p.beta != 0.0f) {
+      const int col = n0 + wn * T::WTN + lane % 32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * T::WTM + T::MF::row(r, lane);
+        cpre[r] = (!EDGE || (row < p.M && col < p.N)) ? p.C[(size_t)row * p.ldc + col] : 0.0f;
+      }
+    }
+  }
 #pragma unroll
   for (int st = 0; st < T::STAGES - 1; ++st)
     if (st < ktiles) {
@@ -972,6 +988,18 @@ sgemm_dma_kernel(SgemmArgs p) {
           if (!EDGE || (row < p.M && col < p.N)) W[(size_t)row * p.N + col] = acc[i][j][r];
         }
       }
+    return;
+  }
+  if constexpr (PRE_C) {
+    const int col = n0 + wn * T::WTN + lane % 32;
+    const float alpha = p.alpha, beta = p.beta;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * T::WTM + T::MF::row(r, lane);
+      if (EDGE && (row >= p.M || col >= p.N)) continue;
+      const float v = alpha * acc[0][0][r];
+      p.C[(size_t)row * p.ldc + col] = beta != 0.0f ? __builtin_fmaf(beta, cpre[r], v) : v;
+    }
     return;
   }
   if (EDGE && (m0 + T::BM > p.M || n0 + T::BN > p.N))
