@@ -450,10 +450,6 @@ struct SDmaTile {
   // first group under those of the second; for the tile whose accumulators
   // leave no room for four sets.
   static constexpr bool LEAN = LEAN_;
-  // PAIR: one barrier per two K tiles (sdma_tile_pair): at the barrier before an
-  // even tile kt, tiles kt + 1 and kt + 2 have landed and the copies of kt + 3
-  // and kt + 4 go out; the odd tile runs without wait or barrier.
-  static constexpr bool PAIR = PAIR_;
   // The same tile copying A with 4-byte copies.
   using WithADw =
       SDmaTile<BM_, BN_, STAGES_, WAVES_PER_SIMD_, WAVES_M_, WAVES_N_, true, LEAN_, PAIR_>;
@@ -477,6 +473,13 @@ struct SDmaTile {
   static constexpr int A_PER_WAVE = A_INSTR / WAVES;
   static constexpr int B_PER_WAVE = B_INSTR / WAVES;
   static constexpr int LOADS_PER_TILE = A_PER_WAVE + B_PER_WAVE;
+  // PAIR: one barrier per two K tiles (sdma_tile_pair): at the barrier before an
+  // even tile kt, tiles kt + 1 and kt + 2 have landed and the copies of kt + 3
+  // and kt + 4 go out; the odd tile runs without wait or barrier.  Taken where
+  // the doubled copies still fit one per MFMA in a group, or on the 64 x 64
+  // tile (its copies go out in one burst either way); the 128 x 128 tile copying
+  // A 4 bytes at a time (20 copies, 16 MFMAs per group) measured 10 % slower with it.
+  static constexpr bool PAIR = PAIR_ && (2 * LOADS_PER_TILE <= 4 * FM * FN || BM * BN <= 64 * 64);
   // Byte offset of row r (0 .. BK - 1) of B inside the stage's B region.
   static __device__ __forceinline__ int b_row(int r) {
     return (r / B_RPC) * B_SLOT + (r % B_RPC) * (BN * 4);
@@ -897,22 +900,6 @@ sgemm_dma_kernel(SgemmArgs p) {
   const float* b_tile = p.B + n0;
   const SDmaPlan<T> plan(p, wave, lane, m0, n0);
   SFrags<T> f0, f1, f2, f3;
-  // A wave of the 64 x 64 tile holds one 32 x 32 block: it loads its 16 values of
-  // C per lane before the K loop (when beta != 0), so their latency overlaps the
-  // loop instead of the epilogue.  Issued before the copies: the K loop's
-  // count-based waits then also cover them.
-  constexpr bool PRE_C = T::FM * T::FN == 1 && !SPLIT;
-  float cpre[16] = {};
-  if constexpr (PRE_C) {
-    if (p.beta != 0.0f) {
-      const int col = n0 + wn * T::WTN + lane % 32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * T::WTM + T::MF::row(r, lane);
-        cpre[r] = (!EDGE || (row < p.M && col < p.N)) ? p.C[(size_t)row * p.ldc + col] : 0.0f;
-      }
-    }
-  }
 #pragma unroll
   for (int st = 0; st < T::STAGES - 1; ++st)
     if (st < ktiles) {
@@ -988,18 +975,6 @@ sgemm_dma_kernel(SgemmArgs p) {
           if (!EDGE || (row < p.M && col < p.N)) W[(size_t)row * p.N + col] = acc[i][j][r];
         }
       }
-    return;
-  }
-  if constexpr (PRE_C) {
-    const int col = n0 + wn * T::WTN + lane % 32;
-    const float alpha = p.alpha, beta = p.beta;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * T::WTM + T::MF::row(r, lane);
-      if (EDGE && (row >= p.M || col >= p.N)) continue;
-      const float v = alpha * acc[0][0][r];
-      p.C[(size_t)row * p.ldc + col] = beta != 0.0f ? __builtin_fmaf(beta, cpre[r], v) : v;
-    }
     return;
   }
   if (EDGE && (m0 + T::BM > p.M || n0 + T::BN > p.N))
