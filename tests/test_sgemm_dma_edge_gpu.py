@@ -22,10 +22,11 @@ pytestmark = pytest.mark.gpu
 
 DMA_TILES = (7, 8, 9, 10, 11)
 # (M, N, K): ragged M and N, K below 32, K % 32 in 1..31, K a multiple of 32 on ragged M / N,
-# tiles smaller than one block, several tiles with a ragged last row and column
+# tiles smaller than one block, several tiles with a ragged last row and column, and K % 32 > 16
+# after whole K tiles (a tail of two 16-wide K tiles)
 SHAPES = [(300, 520, 100), (257, 260, 33), (64, 64, 16), (1, 4, 1), (129, 132, 31),
           (511, 516, 64), (700, 900, 777), (256, 256, 40), (1000, 1000, 1000),
-          (260, 4, 4100)]
+          (260, 4, 4100), (200, 196, 95), (130, 260, 1009)]
 
 
 @pytest.fixture(scope="module", autouse=True)
