@@ -655,39 +655,49 @@ __device__ __forceinline__ void hdma_tile(const HgemmArgs& p, f32x16 (&acc)[T::F
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// The last K % (2 BK) values of k on a ragged K: stages 0 and 1 are filled with
-// bounds-checked loads and plain LDS stores, chunk for chunk where the copies
-// would put them (zeros for k >= K), and the MFMAs of those two K tiles follow.
-// Called by every wave after the main loop.
+// The last K - k0 < 2 BK values of k on a ragged K, taken before the main loop:
+// one BK-wide K tile at a time through stage STAGES - 1, which the prologue's
+// copies leave free, filled chunk for chunk where the copies would put them --
+// a 16-byte load where the chunk lies wholly below K, 2-byte loads and zeros
+// for k >= K where it does not -- then the MFMAs of that tile.  Called by every
+// wave right after the prologue's copies are issued, so the latency of these
+// loads overlaps theirs (after the main loop it was exposed, with a 2-byte load
+// per element and always two K tiles: 2048 x 2048 x 2040 took 23 % longer than
+// 2048^3).  The main loop's first copy into that stage goes out after the first
+// K tile's barrier, which a wave reaches only after its MFMAs here have
+// consumed their fragments.
 template <class T>
 __device__ __forceinline__ void hdma_k_tail(const HgemmArgs& p, f32x16 (&acc)[T::FN][T::FM],
                                             uint8_t* lds, int k0, int m0, int n0, int wave,
                                             int wm, int wn, int lane) {
-  lds_barrier();   // every wave is done reading the stages
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
+  uint8_t* const st = lds + (T::STAGES - 1) * T::STAGE_BYTES;
+  for (int kb = k0; kb < p.K; kb += T::BK) {
+    if (kb > k0) lds_barrier();   // every wave is done reading the previous tail tile
 #pragma unroll
     for (int v = 0; v < T::LOADS_PER_TILE; ++v) {
       uint32_t slot;
       int k_first, k_step;
-      const uint16_t* src =
-          hdma_source<T>(p, m0, n0, k0 + t * T::BK, v, wave, lane, slot, k_first, k_step);
-      uint16_t h[8];
+      const uint16_t* src = hdma_source<T>(p, m0, n0, kb, v, wave, lane, slot, k_first, k_step);
+      u32x4 val;
+      if (k_first + 7 * k_step < p.K) {
+        val = *reinterpret_cast<const u32x4*>(src);
+      } else {
+        uint16_t h[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = k_first + k_step * e < p.K ? src[e] : (uint16_t)0;
-      *reinterpret_cast<u32x4*>(lds + t * T::STAGE_BYTES + slot + 16 * lane) =
-          __builtin_bit_cast(u32x4, h);
+        for (int e = 0; e < 8; ++e) h[e] = k_first + k_step * e < p.K ? src[e] : (uint16_t)0;
+        val = __builtin_bit_cast(u32x4, h);
+      }
+      *reinterpret_cast<u32x4*>(st + slot + 16 * lane) = val;
     }
-  lds_barrier();
-  HFrags<T> f;
+    lds_barrier();
+    HFrags<T> f;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int st = 0; st < T::KSTEPS; ++st) {
-      hload_frags<T>(f, lds + t * T::STAGE_BYTES, st, wm, wn, lane);
+    for (int ks = 0; ks < T::KSTEPS; ++ks) {
+      hload_frags<T>(f, st, ks, wm, wn, lane);
 #pragma unroll
       for (int x = 0; x < T::FM * T::FN; ++x) hmfma<T>(acc, f, x);
     }
+  }
 }
 
 // Bias of the wave's output columns, n-blocks j0 .. j0 + JB - 1: lane l needs,
@@ -1111,18 +1121,21 @@ __device__ __forceinline__ void hdma_workgroup(HgemmArgs p, int wg, int chunk, u
   // consumed in tile kt - 1), which the direct loads of tile kt + STAGES - 1
   // then refill.  K is a multiple of 2 BK, so the loop body covers two tiles.
   // On a ragged K (EDGE only) the loop covers the largest multiple of 2 BK in K
-  // and hdma_k_tail adds the rest.
+  // and hdma_k_tail adds the rest first.
   const int ktiles = EDGE ? (p.K / (2 * T::BK)) * 2 : p.K / T::BK;
   // Wave-uniform tile bases (k = 0) and the per-lane offsets of the direct loads.
   const uint16_t* a_tile = p.A + (size_t)m0 * p.lda;
   const uint16_t* b_tile = p.B + n0;
   const HDmaOffsets<T> dma(p, wave, lane, m0, n0);
   HFrags<T> f0, f1, f2, f3;
-  if (ktiles > 0) {
 #pragma unroll
-    for (int st = 0; st < T::STAGES - 1; ++st)
-      if (st < ktiles) hdma_issue_tile<T>(p, dma, a_tile, b_tile, st, lds_base + st * T::STAGE_BYTES,
-                                          wave);
+  for (int st = 0; st < T::STAGES - 1; ++st)
+    if (st < ktiles) hdma_issue_tile<T>(p, dma, a_tile, b_tile, st, lds_base + st * T::STAGE_BYTES,
+                                        wave);
+  if constexpr (EDGE) {
+    if (ktiles * T::BK < p.K) hdma_k_tail<T>(p, acc, lds, ktiles * T::BK, m0, n0, wave, wm, wn, lane);
+  }
+  if (ktiles > 0) {
     wait_tiles_in_flight<T>(ktiles - 1 < T::STAGES - 2 ? ktiles - 1 : T::STAGES - 2);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -1143,9 +1156,6 @@ __device__ __forceinline__ void hdma_workgroup(HgemmArgs p, int wg, int chunk, u
                         wave, wm, wn, lane);
     hdma_tile<T, false>(p, acc, kt + 1, ktiles, f2, f3, f0, f1, lds, lds_base, dma, a_tile,
                         b_tile, wave, wm, wn, lane);
-  }
-  if constexpr (EDGE) {
-    if (ktiles * T::BK < p.K) hdma_k_tail<T>(p, acc, lds, ktiles * T::BK, m0, n0, wave, wm, wn, lane);
   }
   if constexpr (SPLIT) {
     // Lane l holds, for n-block j, m-block i and q = 0..3, columns 8 q + 4 (l / 32)
