@@ -102,7 +102,7 @@ def trace_table(stats_csv: str):
 
 def trace_markdown(workload: str, stats_csv: str, command: str, note: str = "") -> str:
     lines = ["# Kernel trace: workload `%s`" % workload, "",
-             "Command ($REPO = repository root on the GPU box):", "", "    " + command, ""]
+             "Command ($REPO = repository root on the MI355X machine that ran it):", "", "    " + command, ""]
     if note:
         lines += [note, ""]
     lines += ["`%s` (durations in ns):" % os.path.basename(stats_csv), "",
@@ -210,7 +210,7 @@ def counters_markdown(workload: str, op: str, flops: int, algo_bytes: int, copy_
     write_pass = next((d for d in passes if any("WRITE_SIZE" in x["counters"] for x in d.values())),
                       None)
     lines = ["# Counters: workload `%s`" % workload, "",
-             "Each counter set ran in its own pass ($REPO = repository root on the GPU box):", ""]
+             "Each counter set ran in its own pass ($REPO = repository root on the MI355X machine that ran them):", ""]
     lines += ["    " + c for c in commands]
     lines += [""]
     if note:
@@ -294,7 +294,7 @@ def tile_order_markdown(cases, commands, note: str = "") -> str:
     library kernels' summed average duration per call."""
     from . import cost, inputs
     lines = ["# Tile order A/B: HBM traffic and kernel time per call", "",
-             "Commands ($REPO = repository root on the GPU box; W = workload, G,R = rows per "
+             "Commands ($REPO = repository root on the MI355X machine that ran them; W = workload, G,R = rows per "
              "group and XCD renumbering, as passed to bench.py --swizzle):", ""]
     lines += ["    " + c for c in commands]
     lines += [""]

@@ -224,7 +224,7 @@ def flops(dims):
 def write_report(path, all_results, header, command, margin):
     out = ["# Size sweep and tuned configurations", "",
            "Written by `linear_algebra_sgemm_amd/tune.py` (%s)." % header, "",
-           "Command ($REPO = repository root on the GPU box):", "", "    " + command, "",
+           "Command ($REPO = repository root on the MI355X machine that ran it):", "", "    " + command, "",
            "TFLOP/s = 2·M·N·K / mean GPU time per call (HIP events around back-to-back calls "
            "queued behind other GPU work, so host launch time is excluded; median of three "
            "batches). FP32: α = 1, β = 0.5. Half: fp16, bias + GELU(tanh). "
