@@ -219,35 +219,48 @@ SETTLE_DROP = 0.005
 SETTLE_MAX_S = 3.0
 
 
+def settle_groups(time_group, max_s: float, clock=time.perf_counter):
+    """The settling rule: time_group() runs one group of SETTLE_GROUP untimed calls and
+    returns their times (ms); groups run until a group's median is no longer
+    SETTLE_DROP below the previous group's (after at least SETTLE_MIN_GROUPS groups) or
+    max_s seconds have passed.  Returns the number of calls and each group's median."""
+    if max_s <= 0:
+        return 0, []
+    medians = []
+    t0 = clock()
+    calls = 0
+    while True:
+        medians.append(statistics.median(time_group()))
+        calls += SETTLE_GROUP
+        settled = (len(medians) >= SETTLE_MIN_GROUPS and
+                   medians[-1] >= (1.0 - SETTLE_DROP) * medians[-2])
+        if settled or clock() - t0 > max_s:
+            break
+    return calls, [round(m, 4) for m in medians]
+
+
 def settle(call, reset, handle, max_s: float):
-    """Untimed calls until the per-call time has stopped falling; returns their count
-    and the median call time (ms) of each group."""
+    """Untimed calls of one workload until the per-call time has stopped falling
+    (settle_groups), each call between two HIP events on the launch stream."""
     import torch
 
     if max_s <= 0:
         return 0, []
     timer = HipTimer(2 * SETTLE_GROUP)
-    medians = []
-    t0 = time.perf_counter()
-    calls = 0
+
+    def time_group():
+        for i in range(SETTLE_GROUP):
+            reset()
+            timer.record(2 * i, handle)
+            call()
+            timer.record(2 * i + 1, handle)
+        torch.cuda.synchronize()
+        return [timer.elapsed_ms(2 * i, 2 * i + 1) for i in range(SETTLE_GROUP)]
+
     try:
-        while True:
-            for i in range(SETTLE_GROUP):
-                reset()
-                timer.record(2 * i, handle)
-                call()
-                timer.record(2 * i + 1, handle)
-            torch.cuda.synchronize()
-            calls += SETTLE_GROUP
-            medians.append(statistics.median(timer.elapsed_ms(2 * i, 2 * i + 1)
-                                             for i in range(SETTLE_GROUP)))
-            settled = (len(medians) >= SETTLE_MIN_GROUPS and
-                       medians[-1] >= (1.0 - SETTLE_DROP) * medians[-2])
-            if settled or time.perf_counter() - t0 > max_s:
-                break
+        return settle_groups(time_group, max_s)
     finally:
         timer.close()
-    return calls, [round(m, 4) for m in medians]
 
 
 def time_workload(w, steps: int, warmup: int, settle_s: float = SETTLE_MAX_S):
