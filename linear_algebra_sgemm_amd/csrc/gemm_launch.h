@@ -53,7 +53,8 @@ inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 // (rows of B 16-byte aligned and B readable in whole 4-float chunks, rows of A
 // 4-byte aligned, else tile 4); 9 = tile 7 with eight waves, two per SIMD; 10 = 128x128 with
 // direct-to-LDS copies at two workgroups per CU; 11 = 64x64 with direct-to-LDS
-// copies at up to four workgroups per CU (else tile 2); 12 = 32x32
+// copies at up to four workgroups per CU (else tile 2); 9, 10 and 11 meet at one
+// barrier per two K tiles where their copies allow it; 12 = 32x32
 // register-staged from 16x16x4 MFMA blocks, K step 32 (small outputs); 13 =
 // 16x16 output tiles with K split over the workgroup's four waves, operands
 // loaded straight into registers (small outputs; any shape, never split-K).
@@ -62,7 +63,8 @@ inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 // 3 stages, two workgroups per CU, 5 = 256x256 direct-to-LDS, 5 stages, 6 = 256x256
 // direct-to-LDS with eight waves, 7 = tile 6 on the columns that fill whole
 // rounds of workgroups and 128 x 256 direct-to-LDS tiles on the rest, in one
-// persistent launch of one workgroup per CU where K is at least 5 steps (3 to 7 need
+// persistent launch of one workgroup per CU where K spans at least six 32-wide K
+// tiles (3 to 7 need
 // rows of A and B 16-byte aligned and B readable in whole 8-half chunks, 7 also
 // whole tiles; other operands fall back to 0); 8 = 128x128 direct-to-LDS, 4
 // stages, two workgroups per CU (other operands fall back to 1).
