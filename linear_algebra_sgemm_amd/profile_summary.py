@@ -54,12 +54,23 @@ XCDS = 8
 MIN_CLOCK_NS = 100e3
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def code_only(text: str) -> str:
+    """C++ source without its comments and with runs of whitespace collapsed: what the
+    compiler sees, so that an edit of a comment leaves the digest alone.  (The sources
+    hold no string literal with a comment marker in it.)"""
+    return " ".join(_COMMENT.sub(" ", text).split())
+
+
 def source_digest(op: str) -> str:
-    """First 16 hex digits of the SHA-256 of the op's deciding sources, in order."""
+    """First 16 hex digits of the SHA-256 of the op's deciding sources (code only,
+    comments removed), in order."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[op]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

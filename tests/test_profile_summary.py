@@ -74,3 +74,11 @@ def test_counter_summaries_belong_to_the_current_sources(path):
     traffic = bench.profiled_traffic(name, w.op)
     assert traffic is not None, "%s is stale: re-profile this workload" % path
     assert traffic > 0
+
+
+def test_digest_ignores_comments_but_not_code():
+    src = "int f(int x) {  // add one\n  return x + 1; /* the\n result */\n}\n"
+    same = "int f(int x) {\n  return x + 1;   // a different comment\n}\n"
+    other = "int f(int x) {  // add one\n  return x + 2;\n}\n"
+    assert ps.code_only(src) == ps.code_only(same)
+    assert ps.code_only(src) != ps.code_only(other)
