@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import re
 import statistics
@@ -213,15 +214,23 @@ def parity(w, A, B, C, got):
 # has just run power-limited 16-bit work starts the next workload at a lower clock;
 # five warm-up calls do not cover that (4096^3 FP32: 1.08 ms for the first calls,
 # 0.94 ms once settled).
+#
+# The first group has SETTLE_GROUP calls; every later one enough calls for about
+# SETTLE_GROUP_MS of call time (at most SETTLE_GROUP_MAX calls).  The clock rises over
+# tens of milliseconds of load, not over a number of calls, so a short call needs
+# large groups for the rule to see the rise: 1000 x 3000 x 777 took 51.5 us per call
+# after three groups of ten calls, and 47 us after about 70 ms of calls.
 SETTLE_GROUP = 10
+SETTLE_GROUP_MS = 20.0
+SETTLE_GROUP_MAX = 2000
 SETTLE_MIN_GROUPS = 3
 SETTLE_DROP = 0.005
 SETTLE_MAX_S = 3.0
 
 
 def settle_groups(time_group, max_s: float, clock=time.perf_counter):
-    """The settling rule: time_group() runs one group of SETTLE_GROUP untimed calls and
-    returns their times (ms); groups run until a group's median is no longer
+    """The settling rule: time_group() runs one group of untimed calls and returns
+    their times (ms); groups run until a group's median is no longer
     SETTLE_DROP below the previous group's (after at least SETTLE_MIN_GROUPS groups) or
     max_s seconds have passed.  Returns the number of calls and each group's median."""
     if max_s <= 0:
@@ -230,13 +239,20 @@ def settle_groups(time_group, max_s: float, clock=time.perf_counter):
     t0 = clock()
     calls = 0
     while True:
-        medians.append(statistics.median(time_group()))
-        calls += SETTLE_GROUP
+        times = time_group()
+        medians.append(statistics.median(times))
+        calls += len(times)
         settled = (len(medians) >= SETTLE_MIN_GROUPS and
                    medians[-1] >= (1.0 - SETTLE_DROP) * medians[-2])
         if settled or clock() - t0 > max_s:
             break
     return calls, [round(m, 4) for m in medians]
+
+
+def settle_group_size(call_ms: float) -> int:
+    """Calls in a settling group after the first, for calls of call_ms each."""
+    want = int(math.ceil(SETTLE_GROUP_MS / max(call_ms, 1e-6)))
+    return min(SETTLE_GROUP_MAX, max(SETTLE_GROUP, want))
 
 
 def settle(call, reset, handle, max_s: float):
@@ -246,21 +262,27 @@ def settle(call, reset, handle, max_s: float):
 
     if max_s <= 0:
         return 0, []
-    timer = HipTimer(2 * SETTLE_GROUP)
+    state = {"n": SETTLE_GROUP, "timer": HipTimer(2 * SETTLE_GROUP)}
 
     def time_group():
-        for i in range(SETTLE_GROUP):
+        n, timer = state["n"], state["timer"]
+        for i in range(n):
             reset()
             timer.record(2 * i, handle)
             call()
             timer.record(2 * i + 1, handle)
         torch.cuda.synchronize()
-        return [timer.elapsed_ms(2 * i, 2 * i + 1) for i in range(SETTLE_GROUP)]
+        ms = [timer.elapsed_ms(2 * i, 2 * i + 1) for i in range(n)]
+        want = settle_group_size(statistics.median(ms))
+        if want != n:
+            timer.close()
+            state["n"], state["timer"] = want, HipTimer(2 * want)
+        return ms
 
     try:
         return settle_groups(time_group, max_s)
     finally:
-        timer.close()
+        state["timer"].close()
 
 
 def time_workload(w, steps: int, warmup: int, settle_s: float = SETTLE_MAX_S):

@@ -52,3 +52,17 @@ def test_settling_stops_at_its_time_limit():
 
 def test_settling_can_be_switched_off():
     assert bench.settle_groups(_fake_groups([]), max_s=0) == (0, [])
+
+
+def test_settling_groups_span_a_fixed_call_time():
+    # later groups hold enough calls for SETTLE_GROUP_MS of call time, within bounds
+    assert bench.settle_group_size(5.0) == bench.SETTLE_GROUP
+    assert bench.settle_group_size(0.0625) == 320   # 20 ms of 62.5 us calls
+    assert bench.settle_group_size(1e-5) == bench.SETTLE_GROUP_MAX
+    # the call count is the sum of the group sizes
+    sizes = iter([10, 400, 400, 400])
+
+    def time_group():
+        return [0.05] * next(sizes)
+    calls, med = bench.settle_groups(time_group, max_s=60)
+    assert calls == 10 + 400 + 400 and len(med) == 3
