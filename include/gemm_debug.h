@@ -25,7 +25,7 @@ extern "C" {
  * tiles at two workgroups per compute unit, 11 = 64 x 64 direct-to-LDS tiles
  * at up to four workgroups per compute unit (tile 2 where the operands do not
  * allow direct copies), 12 = 32 x 32 tiles built from 16 x 16 x 4 MFMA blocks
- * with a K step of 32 (small outputs), 13 = 16 x 16 tiles whose four waves
+ * with a K step of 32 (small outputs), 13 = 16 x 16 tiles whose eight waves
  * split K between them (small outputs; never split across workgroups); the
  * half products also have 3 = 256 x 256 and 4 = 128 x 256 direct-to-LDS kernels
  * 5 = the 256 x 256 one with a five-stage pipeline, 6 = the 256 x 256 one

@@ -101,6 +101,13 @@ long round_use(long tiles, int cus, int per_cu) {
 
 // Built-in tile rule, measured on MI355X (the size sweep over powers of two and
 // a sweep of ragged shapes):
+//  * Outputs of at most two 16x16 tiles per CU with K at most 2048: the 16x16
+//    tile whose eight waves split K (tile 13), ragged or not; per call, against
+//    the choice before it: 250 x 250 x 400: 4.5 vs 20.1 us (64x64 register-
+//    staged); 200 x 120 x 2000: 8.3 vs 35.2 (32x32); 300 x 520 x 777: 15.6 vs
+//    16.8; 60 x 2000 x 2000: 21.0 vs 34.3; 330 x 330 x 777: 12.5 vs 14.2.  Past
+//    two tiles per CU it loses where K is long (500 x 500 x 777: 20.2 vs 17.0
+//    for 32x32; 700 x 700 x 400: 13.2 vs 12.8 for 64x64 direct).
 //  * The direct-to-LDS kernels wherever their copies are legal (rows of B
 //    16-byte aligned and readable in whole 4-float chunks, rows of A 4-byte
 //    aligned: `operands_ok`, which holds after packing too) and their 256x256
@@ -138,13 +145,15 @@ long round_use(long tiles, int cus, int per_cu) {
 //    register-staged 64x64 tile and 94 for 128x128 direct at 192 tiles;
 //    1000 x 3000 x 777: 83 vs 69; 1500^3: 89 vs 73 for the best register-staged
 //    tile; 256^3: 4.8 vs 3.8), else register-staged.  But where there are at
-//    most a quarter as many 64x64 tiles as CUs and K is at most 2048, the
+//    most a quarter as many 64x64 tiles as CUs and K is at most 1024, the
 //    32x32 tile of 16x16x4 blocks: its shorter per-wave MFMA chain sets the
-//    time there (per call, 256^3: 7.1 us vs 9.2; 512^3: 10.1 vs 13.9; 256 x 256
-//    x 1024: 14.7 vs 22.1; ragged too, bounds-checked: 300 x 520 x 100: 9.5 vs
-//    12.6, 500 x 500 x 777: 20.8 vs 26.1; but 1024 x 1024 x 256, 256 tiles of
-//    64x64: 11.8 vs 10.5).
+//    time there (per call, 512^3: 10.1 us vs 13.9; ragged too, bounds-checked:
+//    300 x 520 x 100: 9.5 vs 12.6, 500 x 500 x 777: 17.0 vs 20.6; but 1024 x
+//    1024 x 256, 256 tiles of 64x64: 11.8 vs 10.5; and its time grows with K
+//    faster than the 64x64 tile's: 500 x 500 x 2000: 34.7 vs 20.0).
 int sgemm_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
+  // Small outputs first: see the rule's description above.
+  if (ceil_div(M, 16) * ceil_div(N, 16) <= 2L * cus && K <= 2048) return 13;
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_tall = ceil_div(M, 128) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
@@ -177,7 +186,7 @@ int sgemm_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   if (t_tall >= 2L * cus && (!direct || (M % 128 == 0 && N % 256 == 0 && K % 16 == 0))) return 4;
   if (t_med >= 2L * cus && (!direct || (M % 128 == 0 && N % 128 == 0 && K % 16 == 0))) return 1;
   const long t_small = ceil_div(M, 64) * ceil_div(N, 64);
-  if (direct && 4 * t_small <= cus && K <= 2048) return 12;
+  if (direct && 4 * t_small <= cus && K <= 1024) return 12;
   return direct ? 11 : 2;
 }
 
@@ -262,7 +271,7 @@ SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_spl
            : (tuned && force_tile < 0) ? tuned_splits
                                        : sgemm_rule_splits(M, N, K, p.tile, cus);
   // Small outputs that would split K across workgroups (a second launch adds the
-  // partials): the 16x16 tile, whose four waves split K inside the workgroup,
+  // partials): the 16x16 tile, whose waves split K inside the workgroup,
   // where its tiles fit one round (at most one per CU) and K is at most 2048.
   // Kernel time, split choice + reduction -> tile 13: 192 x 192 x 768: 4.7 + 4.5 ->
   // 5.1 us; 256 x 256 x 1024: 5.1 + 4.6 -> 6.5; 256 x 256 x 2048: 6.0 + 4.6 -> 10.1

@@ -56,7 +56,7 @@ inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 // copies at up to four workgroups per CU (else tile 2); 9, 10 and 11 meet at one
 // barrier per two K tiles where their copies allow it; 12 = 32x32
 // register-staged from 16x16x4 MFMA blocks, K step 32 (small outputs); 13 =
-// 16x16 output tiles with K split over the workgroup's four waves, operands
+// 16x16 output tiles with K split over the workgroup's eight waves, operands
 // loaded straight into registers (small outputs; any shape, never split-K).
 // HGEMM: 0 = 256x256, 1 = 128x128, 2 = 64x64 (register-staged, K step 64),
 // 3 = 256x256 direct-to-LDS, 4 stages of K step 32, 4 = 128x256 direct-to-LDS,

@@ -57,7 +57,7 @@ TILE_NAMES = {
         5: "256x256 (16x16 MFMA)", 6: "128x256 (2 WG/CU, 16x16 MFMA)", 7: "256x256 direct",
         8: "128x256 direct (2 WG/CU)", 9: "256x256 direct, 8 waves",
         10: "128x128 direct (2 WG/CU)", 11: "64x64 direct (4 WG/CU)",
-        12: "32x32 (16x16 MFMA, BK 32)", 13: "16x16, K split over 4 waves"},
+        12: "32x32 (16x16 MFMA, BK 32)", 13: "16x16, K split over 8 waves"},
     1: {0: "256x256 reg", 1: "128x128 reg", 2: "64x64 reg", 3: "256x256 direct",
         4: "128x256 direct", 5: "256x256 direct, 5 stages", 6: "256x256 direct, 8 waves",
         7: "256x256 direct, 8 waves + 128x256 tail", 8: "128x128 direct (2 WG/CU)"},

@@ -153,8 +153,14 @@ def test_config_rule(so):
         (0, 4096, 4096, 4002, 256, (9, 1)),   # lda = 4002: A copied 4 bytes at a time
         (0, 4096, 4090, 4096, 256, (9, 1)),   # N not a multiple of 4: B packed first
         (0, 64, 4090, 64, 256, (2, 1)),       # packing B would cost more than it saves
-        (0, 256, 256, 256, 256, (12, 1)),     # 16 tiles of 64x64: the 32x32 tile, unsplit
-        (0, 256, 256, 1024, 256, (12, 1)),
+        (0, 256, 256, 256, 256, (13, 1)),     # 256 tiles of 16x16: one per CU, K in the waves
+        (0, 256, 256, 1024, 256, (13, 1)),
+        (0, 250, 250, 400, 256, (13, 1)),     # ragged, not packable: still the 16x16 tile
+        (0, 60, 2000, 2000, 256, (13, 1)),    # 500 tiles of 16x16: two per CU
+        (0, 330, 330, 777, 256, (13, 1)),
+        (0, 256, 256, 4096, 256, (11, 8)),    # K > 2048: 64x64 direct in K chunks
+        (0, 700, 700, 400, 256, (11, 1)),     # 1936 tiles of 16x16: more than two per CU
+        (0, 500, 500, 2000, 256, (11, 3)),    # 64 tiles of 64x64, K > 1024: not the 32x32 tile
         (0, 512, 512, 512, 256, (12, 1)),     # 64 tiles of 64x64
         (0, 512, 512, 480, 256, (12, 1)),
         (0, 512, 512, 500, 256, (12, 1)),     # K not a multiple of 32: still 32x32

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 # 256x256, 128x128, 64x64, 256x256 (K step 32), 128x256; 5, 6: 256x256 and 128x256 with
 # 16x16x4 MFMA blocks; 7, 8: 256x256 and 128x256 with direct-to-LDS copies
-TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13)   # 9: tile 7 with eight waves; 10, 11: 128x128, 64x64 direct; 12: 32x32; 13: 16x16, K over 4 waves
+TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13)   # 9: tile 7 with eight waves; 10, 11: 128x128, 64x64 direct; 12: 32x32; 13: 16x16, K over 8 waves
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -269,10 +269,17 @@ def test_long_k_repeated():
 @pytest.mark.parametrize("M,N,K,lda,ldb,ldc", [(256, 256, 256, None, None, None),
                                                (100, 70, 1001, 1003, 73, 75),
                                                (17, 129, 2048, 2049, None, 130),
-                                               (16, 16, 4, None, None, None)])
+                                               (16, 16, 4, None, None, None),
+                                               (48, 80, 320, None, None, None),
+                                               (64, 32, 128, 132, 40, 33),
+                                               (32, 16, 1024, 1028, 17, None),
+                                               (16, 48, 32, None, None, None)])
 def test_wave_split_tile_padded_and_odd(M, N, K, lda, ldb, ldc, tile_forced):
-    """Tile 13 (16 x 16 tiles, K split over the four waves, operands loaded straight
+    """Tile 13 (16 x 16 tiles, K split over the eight waves, operands loaded straight
     into registers): ragged sizes, odd leading dimensions (rows of A not 16-byte
-    aligned, so the scalar loads run), NaN padding that must never be read."""
+    aligned, so the scalar loads run), NaN padding that must never be read; whole
+    tiles (M, N multiples of 16, K of 32, rows of A 16-byte aligned) need no
+    out-of-range values replaced, with K = 320 giving the waves one or two chunks
+    each and K = 32 leaving seven waves without one."""
     lib.gemm_debug_force_tile(0, 13)
     check_full(M, N, K, 1.5, -0.75, seed=M + N + K, lda=lda, ldb=ldb, ldc=ldc, label="tile 13")
