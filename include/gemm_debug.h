@@ -34,7 +34,9 @@ extern "C" {
  * compute unit walking both lists (whole tiles only, else the
  * 256 x 256 register-staged kernel; 7 becomes 6 where no such split exists),
  * 8 = 128 x 128 direct-to-LDS tiles at two workgroups per compute unit (tile 1
- * where the operands do not allow direct copies).
+ * where the operands do not allow direct copies) and 9 = 16 x 16 tiles whose
+ * eight waves split K between them (any operands; small outputs; never split
+ * across workgroups).
  * Whether the aligned fast path or the
  * bounds-checked path runs still follows the shape and alignment.  Returns
  * GEMM_STATUS_INVALID_VALUE for an unknown op or tile.  Pure host state: no

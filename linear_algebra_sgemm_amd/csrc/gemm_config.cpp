@@ -309,7 +309,15 @@ SgemmPlan plan_sgemm(int M, int N, int K, int cus, int force_tile, int force_spl
 namespace {
 
 int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
-  // Built-in rule (from the size sweep).  Where the direct-to-LDS copies are
+  // Built-in rule (from the size sweep).  Small outputs first, whatever the
+  // operands: the 16x16 tile whose eight waves split K (tile 9) for at most one
+  // such tile per CU with K <= 4096, or four per CU with K <= 2048; per call
+  // (FP16, bias + GELU), against the earlier choice: 250 x 250 x 400: 4.4 us vs
+  // 37.4 (64x64 register-staged, bounds-checked); 500 x 500 x 400: 9.0 vs 37.0;
+  // 128 x 128 x 2048: 5.1 vs 9.5 (64x64 in 8 chunks); 256 x 256 x 4096: 9.1 vs
+  // 11.9 (128x128 direct in 8); 1000 x 200 x 777: 16.0 vs 27.3; but 60 x 2000 x
+  // 2000: 18.6 vs 13.2 for 128x128 direct, and 700 x 700 x 400 (1936 tiles):
+  // 18.8 vs 15.7.  Where the direct-to-LDS copies are
   // legal (`operands_ok`: rows of A and B 16-byte aligned, B readable in whole
   // 8-half chunks, as given or after packing):
   //  * 256x256 tiles with eight waves once they give every CU one, or once the
@@ -323,9 +331,10 @@ int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   //    at two per CU), the 128x128 direct-to-LDS tile (2048^3: 640 vs 404 for
   //    64x64; 1024 x 4096 x 4096: 776 vs 528 for 128x128 register-staged;
   //    2048 x 2048 x 8192: 823 vs 641; 1000^3: 129 vs 68 for 128x256 direct;
-  //    1024^3: 185 vs 155); with K split (below) it also takes outputs down to
-  //    16 such tiles once K reaches 4096 (512 x 512 x 8192 in 8 chunks: 225 vs
-  //    188 for 64x64 in 16; 512 x 512 x 4096 in 4: 151 vs 137).
+  //    1024^3: 185 vs 155); with K split (below) it also takes smaller outputs
+  //    once K reaches 4096 (512 x 512 x 8192 in 8 chunks: 225 vs 188 for 64x64
+  //    in 16; 512 x 512 x 4096 in 4: 151 vs 137; 300 x 500 x 4096, 12 tiles:
+  //    26 us vs 62 for 64x64 in 22 chunks; 128 x 128 x 8192: 13.6 vs 16.7).
   //  * Smaller outputs: the register-staged 64x64 tile, which spreads them over
   //    the most CUs with split-K -- unless it would run bounds-checked (ragged
   //    M, N or K) and there are 16 tiles of 128x256: then 128x256 direct-to-LDS
@@ -334,11 +343,13 @@ int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   // Otherwise (operands the copies cannot take) the register-staged 256x256
   // tile where 256x256 tiles give every CU one and K >= 512, else 128x128 tiles
   // once they give every CU two, else 64x64.
+  const long t16 = ceil_div(M, 16) * ceil_div(N, 16);
+  if ((t16 <= cus && K <= 4096) || (t16 <= 4L * cus && K <= 2048)) return 9;
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
   const bool direct = operands_ok;
   if (direct && K >= 128 && (t_large >= cus || t_med > 2L * cus)) return K >= 2048 ? 7 : 6;
-  if (direct && t_med <= 2L * cus && (4 * t_med >= cus || (K >= 4096 && t_med >= 16))) return 8;
+  if (direct && t_med <= 2L * cus && (4 * t_med >= cus || K >= 4096)) return 8;
   if (!direct && t_large >= cus && K >= 512) return 0;
   const int reg = t_med >= 2L * cus ? 1 : 2;
   const int bm = half_tile_bm(reg);

@@ -67,9 +67,11 @@ inline int readable_cols(int nb, int N) { return nb > 0 ? nb : N; }
 // tiles (3 to 7 need
 // rows of A and B 16-byte aligned and B readable in whole 8-half chunks, 7 also
 // whole tiles; other operands fall back to 0); 8 = 128x128 direct-to-LDS, 4
-// stages, two workgroups per CU (other operands fall back to 1).
+// stages, two workgroups per CU (other operands fall back to 1); 9 = 16x16
+// output tiles with K split over the workgroup's eight waves, operands loaded
+// straight into registers (small outputs; any shape, never split-K).
 constexpr int kSgemmTileCount = 14;
-constexpr int kHgemmTileCount = 9;
+constexpr int kHgemmTileCount = 10;
 
 // K granularity of each SGEMM tile configuration: the K step (32 for tiles 3
 // and 12), or for the direct-to-LDS tiles (7-11) their two-tile loop body
@@ -137,10 +139,10 @@ constexpr int half_tile_bm(int tile) { return tile == 0 ? 256 : tile == 1 ? 128 
 constexpr int kHalfBK = 64;
 // Output tile of every half configuration (rows, columns).
 constexpr int half_tile_rows(int tile) {
-  return tile <= 2 ? half_tile_bm(tile) : tile == 4 || tile == 8 ? 128 : 256;
+  return tile <= 2 ? half_tile_bm(tile) : tile == 4 || tile == 8 ? 128 : tile == 9 ? 16 : 256;
 }
 constexpr int half_tile_cols(int tile) {
-  return tile <= 2 ? half_tile_bm(tile) : tile == 8 ? 128 : 256;
+  return tile <= 2 ? half_tile_bm(tile) : tile == 8 ? 128 : tile == 9 ? 16 : 256;
 }
 
 // The plan for an M x N x K half product on `cus` compute units (`operands_ok`:
@@ -153,9 +155,9 @@ HalfPlan plan_half(int M, int N, int K, int cus, int force_tile, int force_split
 // plan_half with the operand conditions read from the call.
 HalfPlan plan_half_call(const HgemmCall& c, int cus, int force_tile, int force_splits,
                         size_t ws_floats);
-// The configuration that actually runs for `tile`: the direct-to-LDS ones (3,
-// 4) become the register-staged 256x256 one (0) when the shape or operands do
-// not suit them.
+// The configuration that actually runs for `tile`: the direct-to-LDS ones (3
+// to 7) become the register-staged 256x256 one (0), and 8 the register-staged
+// 128x128 one (1), when the operands do not suit them; 9 runs anywhere.
 // 7 (eight-wave 256 x 256 tiles with a 128 x 256 tail) becomes 6 when no split
 // of the columns fills whole rounds of `cus` workgroups with the head and one
 // round with the tail.

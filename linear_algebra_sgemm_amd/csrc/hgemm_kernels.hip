@@ -32,6 +32,9 @@ struct EltF16 {
   static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
   // fp32 -> binary16, round to nearest even (v_cvt_f16_f32)
   static __device__ __forceinline__ uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
@@ -42,6 +45,9 @@ struct EltBF16 {
   typedef __bf16 vec8 __attribute__((ext_vector_type(8)));
   static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   // fp32 -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32)
   static __device__ __forceinline__ uint16_t bits(float x) {
@@ -96,6 +102,8 @@ struct HgemmArgs {
   // ws + y * M * N (M x N, row stride N).
   int k_chunk;
   float* ws;
+  // K-split kernel: rows of A 16-byte aligned (lda a multiple of 8, A aligned).
+  int a_vec;
 };
 
 template <class T, bool EDGE>
@@ -1392,11 +1400,143 @@ int hgemm_resolve_tile(int tile, int M, int N, int K, bool operands_ok, int cus)
   // every shape, runs.  The head/tail column split needs whole 256x256 tiles, K
   // a multiple of 64 and a split that fills the last round; else the eight-wave
   // tile runs alone.  The 128x128 direct-to-LDS tile falls back to its
-  // register-staged twin.
-  if (tile >= 3 && !operands_ok) return tile == 8 ? 1 : 0;
+  // register-staged twin.  The 16x16 K-split tile (9) takes any operands.
+  if (tile >= 3 && tile != 9 && !operands_ok) return tile == 8 ? 1 : 0;
   if (tile == 7 && !(M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && hgemm_tail_split(M, N, cus) > 0))
     return 6;
   return tile;
+}
+
+// ---------------------------------------------------------------------------
+// Small outputs: one 16 x 16 output tile per workgroup, its K range split over
+// eight waves and added in wave order through LDS (the split-K of lecture 24,
+// section 8.3, inside one workgroup; the FP32 library's 16 x 16 tile in 16-bit
+// form).  Operands go straight from global memory into registers; each wave
+// takes every eighth chunk of 128 values of k and runs one
+// v_mfma_f32_16x16x32 per 32 of them.  In MFMA step s lane l supplies row
+// (or column) l % 16 at k = kb + 32 (l / 16) + 8 s + j, j = 0 .. 7, so a lane's
+// 32 values of A in a chunk are contiguous in its row (four 16-byte loads) and
+// A and B agree on which k each product uses; B's values are 2-byte loads down
+// the column.  Every load is unconditional: row, column and k are clamped into
+// the matrices and values outside are replaced by zero, and all of a chunk's
+// loads go out before its first MFMA.  The epilogue (alpha, bias, activation,
+// rounding) runs once per output element after the partial sums are added.
+// ---------------------------------------------------------------------------
+constexpr int kHksTile = 16;
+constexpr int kHksWaves = 8;
+constexpr int kHksSteps = 4;                      // MFMAs per wave per chunk
+constexpr int kHksChunk = 32 * kHksSteps;         // k per wave per chunk
+constexpr int kHksSpan = kHksWaves * kHksChunk;   // k of one chunk of every wave
+
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+template <class E>
+__global__ void __launch_bounds__(kHksWaves * kWave)
+    __attribute__((amdgpu_waves_per_eu(kHksWaves / 4))) hgemm_wave_ksplit_kernel(HgemmArgs p) {
+  typedef typename E::vec8 vec8;
+  __shared__ float part[kHksWaves][kHksTile * kHksTile];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int m0 = (blockIdx.x / p.tiles_n) * kHksTile;
+  const int n0 = (blockIdx.x % p.tiles_n) * kHksTile;
+  const int l16 = lane % 16, g = lane / 16;
+  const int row = m0 + l16, col = n0 + l16;
+  const bool row_ok = row < p.M, col_ok = col < p.N;
+  const uint16_t* arow = p.A + (size_t)(row_ok ? row : 0) * p.lda;
+  // B's values by 32-bit byte offsets from its base (the launcher checks that
+  // 2 K ldb fits), so that each load takes the base from scalar registers and
+  // needs one offset register, not a 64-bit address per value of k.
+  const char* const bbase = reinterpret_cast<const char*>(p.B);
+  const uint32_t bcol = 2u * (uint32_t)(col_ok ? col : 0);
+  const uint32_t bstride = 2u * (uint32_t)p.ldb;
+  auto bload = [&](int k) -> uint16_t {
+    return *reinterpret_cast<const uint16_t*>(bbase + ((uint32_t)k * bstride + bcol));
+  };
+  f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int kb = wave * kHksChunk; kb < p.K; kb += kHksSpan) {
+    const int ka = kb + 32 * g;
+    if (p.a_vec && kb + kHksChunk <= p.K) {
+      u16x8 a[kHksSteps], b[kHksSteps];
+#pragma unroll
+      for (int st = 0; st < kHksSteps; ++st)
+        a[st] = *reinterpret_cast<const u16x8*>(arow + ka + 8 * st);
+#pragma unroll
+      for (int st = 0; st < kHksSteps; ++st)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[st][j] = bload(ka + 8 * st + j);
+      __builtin_amdgcn_sched_barrier(0);   // every load before the first MFMA
+#pragma unroll
+      for (int st = 0; st < kHksSteps; ++st) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          a[st][j] = row_ok ? a[st][j] : (uint16_t)0;
+          b[st][j] = col_ok ? b[st][j] : (uint16_t)0;
+        }
+        // two accumulators, so consecutive MFMAs do not wait for each other
+        f32x4& acc = st % 2 ? acc1 : acc0;
+        acc = E::mfma16(__builtin_bit_cast(vec8, a[st]), __builtin_bit_cast(vec8, b[st]), acc);
+      }
+    } else {
+      // The chunk that reaches past K, or rows of A off 16-byte boundaries:
+      // 2-byte loads with k clamped, one MFMA step at a time.
+#pragma unroll
+      for (int st = 0; st < kHksSteps; ++st) {
+        u16x8 a, b;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int k0 = ka + 8 * st + j;
+          const int k = k0 < p.K ? k0 : p.K - 1;
+          a[j] = arow[k];
+          b[j] = bload(k);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bool in_k = ka + 8 * st + j < p.K;
+          a[j] = row_ok && in_k ? a[j] : (uint16_t)0;
+          b[j] = col_ok && in_k ? b[j] : (uint16_t)0;
+        }
+        f32x4& acc = st % 2 ? acc1 : acc0;
+        acc = E::mfma16(__builtin_bit_cast(vec8, a), __builtin_bit_cast(vec8, b), acc);
+      }
+    }
+  }
+  // lane l holds column l % 16, rows 4 (l / 16) + r of this wave's partial tile
+#pragma unroll
+  for (int r = 0; r < 4; ++r) part[wave][(4 * g + r) * kHksTile + l16] = acc0[r] + acc1[r];
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int i = m0 + t / kHksTile, j = n0 + t % kHksTile;
+  if (t < kHksTile * kHksTile && i < p.M && j < p.N) {
+    float sum = part[0][t];
+#pragma unroll
+    for (int w = 1; w < kHksWaves; ++w) sum += part[w][t];
+    // x = alpha * sum + bias[col]; y = act(x); C = 16-bit(y)
+    float x = __builtin_fmaf(p.alpha, sum, p.bias != nullptr ? p.bias[j] : 0.0f);
+    if (p.act == 1) x = gelu_tanh(x);
+    p.C[(size_t)i * p.ldc + j] = E::bits(x);
+  }
+}
+
+template <class E>
+static hipError_t launch_hksplit(const HgemmCall& c, hipStream_t s) {
+  HgemmArgs p{};
+  p.M = c.M; p.N = c.N; p.K = c.K;
+  p.alpha = c.alpha;
+  p.A = c.A; p.lda = c.lda; p.B = c.B; p.ldb = c.ldb;
+  p.bias = c.bias; p.act = c.act;
+  p.C = c.C; p.ldc = c.ldc;
+  p.tiles_m = (c.M + kHksTile - 1) / kHksTile;
+  p.tiles_n = (c.N + kHksTile - 1) / kHksTile;
+  p.group_m = 1;
+  p.nb = c.N;
+  p.k_chunk = c.K;
+  p.ws = nullptr;
+  p.a_vec = c.lda % 8 == 0 && (reinterpret_cast<uintptr_t>(c.A) & 15u) == 0;
+  if (2 * (int64_t)c.K * c.ldb >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(hgemm_wave_ksplit_kernel<E>, dim3(p.tiles_m * p.tiles_n),
+                     dim3(kHksWaves * kWave), 0, s, p);
+  return hipGetLastError();
 }
 
 HalfPlan plan_half_call(const HgemmCall& c, int cus, int force_tile, int force_splits,
@@ -1419,6 +1559,7 @@ static hipError_t launch_half(const HgemmCall& c, const HalfPlan& plan, int cus,
     }
   }
   switch (plan.tile) {
+    case 9: return launch_hksplit<E>(c, s);
     case 0: return launch_htile<HTileLarge<E>>(c, 4, s);
     case 1: return launch_htile<HTileMedium<E>>(c, 8, s);
     case 2: return launch_htile<HTileSmall<E>>(c, 8, s);

@@ -50,7 +50,7 @@ DEFAULT_REPORT = os.path.join(ROOT, "profiles", "size_sweep.md")
 
 OPS = {"sgemm": 0, "half": 1}
 SGEMM_TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13)
-HALF_TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8)
+HALF_TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9)
 SPLITS = (1, 2, 4, 8, 16, 32)
 TILE_NAMES = {
     0: {0: "256x256", 1: "128x128", 2: "64x64", 3: "256x256 (BK 32)", 4: "128x256 (2 WG/CU)",
@@ -60,7 +60,8 @@ TILE_NAMES = {
         12: "32x32 (16x16 MFMA, BK 32)", 13: "16x16, K split over 8 waves"},
     1: {0: "256x256 reg", 1: "128x128 reg", 2: "64x64 reg", 3: "256x256 direct",
         4: "128x256 direct", 5: "256x256 direct, 5 stages", 6: "256x256 direct, 8 waves",
-        7: "256x256 direct, 8 waves + 128x256 tail", 8: "128x128 direct (2 WG/CU)"},
+        7: "256x256 direct, 8 waves + 128x256 tail", 8: "128x128 direct (2 WG/CU)",
+        9: "16x16, K split over 8 waves"},
 }
 
 

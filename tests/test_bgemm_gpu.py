@@ -16,7 +16,7 @@ from tests.gpu_helpers import FP16_TOL, hgemm_error, note, run_hgemm
 
 pytestmark = pytest.mark.gpu
 
-TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8)
+TILES = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -123,3 +123,24 @@ def test_workload_ffn_every_element():
     err, where = hgemm_error(w.M, w.N, w.K, w.alpha, A, w.K, B, w.N, bias, lib.ACT_GELU_TANH,
                              got, w.N)
     assert err <= FP16_TOL, "max normalised error %.3g at %s" % (err, where)
+
+
+WAVE_SPLIT_CASES = [(256, 256, 256, None, None, None),
+                    (100, 70, 1001, 1003, 73, 75),
+                    (17, 129, 2500, 2504, None, 130),
+                    (16, 16, 8, None, None, None),
+                    (48, 80, 1152, None, None, None),
+                    (33, 40, 129, 136, 48, 41)]
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", WAVE_SPLIT_CASES)
+def test_wave_split_tile_padded_and_odd(M, N, K, lda, ldb, ldc, tile_forced):
+    """Tile 9 (16 x 16 tiles, K split over eight waves, operands loaded straight into
+    registers): ragged sizes; rows of A off 16-byte boundaries (lda 1003: the 2-byte
+    loads run); K = 1152 and 2500 give the waves one to three chunks and a tail; NaN
+    padding that must never be read; with and without bias and GELU."""
+    lib.gemm_debug_force_tile(1, 9)
+    check_full(M, N, K, 1.25, lib.ACT_GELU_TANH, seed=M + N + K, lda=lda, ldb=ldb, ldc=ldc,
+               label="tile 9")
+    check_full(M, N, K, -0.5, lib.ACT_NONE, seed=M + N + K + 1, with_bias=False, lda=lda,
+               ldb=ldb, ldc=ldc, label="tile 9, no bias")
