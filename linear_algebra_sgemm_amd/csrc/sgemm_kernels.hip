@@ -191,9 +191,11 @@ struct Stage {
 // so their latencies overlap instead of adding up: a whole block row on whole
 // tiles, one block at a time in the bounds-checked form (EDGE), whose row and
 // column checks hold registers of their own.
+// `pre` (when given): this lane's values of C, loaded earlier, in the order of
+// the accumulators (block i, j, element r at ((i FN + j) ACC + r)).
 template <class T, bool EDGE, class ACC>
 __device__ __forceinline__ void sgemm_store(const SgemmArgs& p, const ACC& acc, int r0, int c0,
-                                            int lane) {
+                                            int lane, const float* pre = nullptr) {
   using MF = typename T::MF;
   constexpr int JB = EDGE ? 1 : T::FN;
   const int lb = lane % T::BLK;
@@ -212,7 +214,10 @@ __device__ __forceinline__ void sgemm_store(const SgemmArgs& p, const ACC& acc, 
           for (int r = 0; r < MF::ACC; ++r) {
             const int row = r0 + i * T::BLK + MF::row(r, lane);
             const bool ok = !EDGE || (row < p.M && col < p.N);
-            cv[jj][r] = ok ? p.C[(size_t)row * p.ldc + col] : 0.0f;
+            if (pre != nullptr)
+              cv[jj][r] = pre[(i * T::FN + j0 + jj) * MF::ACC + r];
+            else
+              cv[jj][r] = ok ? p.C[(size_t)row * p.ldc + col] : 0.0f;
           }
         }
       }
@@ -545,6 +550,13 @@ struct SDmaTile {
   // tiles narrower than 256 x 256 (measured faster there); the 256 x 256 tiles
   // take them after the loop.
   static constexpr bool TAIL_FIRST = BM * BN < 256 * 256;
+  // PRE_C: a wave of one 32 x 32 block (the 64 x 64 tile) loads its 16 values
+  // of C per lane at the start, ahead of the first copies, and keeps them in
+  // registers for the epilogue: all workgroups of a round reach the epilogue
+  // together, where the reads of C would wait a full memory round trip
+  // (1000 x 3000 x 777: 1.3 us of a 46 us call).  The larger tiles have no
+  // registers to spare for it.
+  static constexpr bool PRE_C = FM * FN == 1;
 };
 
 // Per-lane byte offsets of a wave's copies relative to the K tile's A or B base
@@ -945,6 +957,26 @@ sgemm_dma_kernel(SgemmArgs p) {
   const float* a_tile = p.A + (size_t)m0 * p.lda;
   const float* b_tile = p.B + n0;
   const SDmaPlan<T> plan(p, wave, lane, m0, n0);
+  // C ahead of the copies (PRE_C): row and column clamped into the matrix, so the
+  // loads are unconditional; values outside are never stored.  Being the oldest
+  // loads, they are complete by the first copy wait (loads finish in issue order).
+  float cpre[T::PRE_C ? 16 * T::FM * T::FN : 1];
+  if constexpr (T::PRE_C && !SPLIT) {
+    if (p.beta != 0.0f) {
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+          const int col = n0 + wn * T::WTN + j * 32 + lane % 32;
+          const int cc = col < p.N ? col : p.N - 1;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wm * T::WTM + i * 32 + mfma32_row(r, lane);
+            cpre[(i * T::FN + j) * 16 + r] = p.C[(size_t)(row < p.M ? row : p.M - 1) * p.ldc + cc];
+          }
+        }
+    }
+  }
   SFrags<T> f0, f1, f2, f3;
 #pragma unroll
   for (int st = 0; st < T::STAGES - 1; ++st)
@@ -1023,10 +1055,11 @@ sgemm_dma_kernel(SgemmArgs p) {
       }
     return;
   }
+  const float* pre = T::PRE_C ? cpre : nullptr;
   if (EDGE && (m0 + T::BM > p.M || n0 + T::BN > p.N))
-    sgemm_store<T, true>(p, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
+    sgemm_store<T, true>(p, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane, pre);
   else
-    sgemm_store<T, false>(p, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
+    sgemm_store<T, false>(p, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane, pre);
 }
 
 // Second half of split-K: C = alpha * (sum of the `splits` partials, added in
