@@ -1533,7 +1533,9 @@ static hipError_t launch_hksplit(const HgemmCall& c, hipStream_t s) {
   p.k_chunk = c.K;
   p.ws = nullptr;
   p.a_vec = c.lda % 8 == 0 && (reinterpret_cast<uintptr_t>(c.A) & 15u) == 0;
-  if (2 * (int64_t)c.K * c.ldb >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+  // B's byte offsets must fit 32 bits; past that the register-staged 64x64 tile,
+  // which takes any shape, runs instead.
+  if (2 * (int64_t)c.K * c.ldb >= (int64_t(1) << 32)) return launch_htile<HTileSmall<E>>(c, 8, s);
   hipLaunchKernelGGL(hgemm_wave_ksplit_kernel<E>, dim3(p.tiles_m * p.tiles_n),
                      dim3(kHksWaves * kWave), 0, s, p);
   return hipGetLastError();
