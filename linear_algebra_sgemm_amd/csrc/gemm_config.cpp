@@ -101,13 +101,17 @@ long round_use(long tiles, int cus, int per_cu) {
 
 // Built-in tile rule, measured on MI355X (the size sweep over powers of two and
 // a sweep of ragged shapes):
-//  * Outputs of at most two 16x16 tiles per CU with K at most 2048: the 16x16
-//    tile whose eight waves split K (tile 13), ragged or not; per call, against
-//    the choice before it: 250 x 250 x 400: 4.5 vs 20.1 us (64x64 register-
-//    staged); 200 x 120 x 2000: 8.3 vs 35.2 (32x32); 300 x 520 x 777: 15.6 vs
-//    16.8; 60 x 2000 x 2000: 21.0 vs 34.3; 330 x 330 x 777: 12.5 vs 14.2.  Past
-//    two tiles per CU it loses where K is long (500 x 500 x 777: 20.2 vs 17.0
-//    for 32x32; 700 x 700 x 400: 13.2 vs 12.8 for 64x64 direct).
+//  * Outputs of at most one 16x16 tile per CU with K at most 4096, or two per
+//    CU with K at most 2048: the 16x16 tile whose eight waves split K (tile
+//    13), ragged or not; per call, against the choice before it: 250 x 250 x
+//    400: 4.5 vs 20.1 us (64x64 register-staged); 200 x 120 x 2000: 8.3 vs 35.2
+//    (32x32); 300 x 520 x 777: 15.6 vs 16.8; 60 x 2000 x 2000: 21.0 vs 34.3;
+//    330 x 330 x 777: 12.5 vs 14.2; 128 x 128 x 4096: 11.0 vs 15.4 (64x64
+//    direct in 8 chunks); 256 x 256 x 4096: 13.2 vs 16.2.  Past two tiles per CU
+//    it loses where K is long (500 x 500 x 777: 20.2 vs 17.0 for 32x32; 700 x
+//    700 x 400: 13.2 vs 12.8 for 64x64 direct), and at 4096 already past one
+//    (256 x 512 x 4096: 24.0 vs 17.9), as at K = 8192 (128 x 128: 21.2 vs 14.1
+//    for 32x32 in 16 chunks).
 //  * The direct-to-LDS kernels wherever their copies are legal (rows of B
 //    16-byte aligned and readable in whole 4-float chunks, rows of A 4-byte
 //    aligned: `operands_ok`, which holds after packing too) and their 256x256
@@ -153,7 +157,8 @@ long round_use(long tiles, int cus, int per_cu) {
 //    faster than the 64x64 tile's: 500 x 500 x 2000: 34.7 vs 20.0).
 int sgemm_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   // Small outputs first: see the rule's description above.
-  if (ceil_div(M, 16) * ceil_div(N, 16) <= 2L * cus && K <= 2048) return 13;
+  const long t16 = ceil_div(M, 16) * ceil_div(N, 16);
+  if ((t16 <= cus && K <= 4096) || (t16 <= 2L * cus && K <= 2048)) return 13;
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_tall = ceil_div(M, 128) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);

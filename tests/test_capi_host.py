@@ -158,7 +158,9 @@ def test_config_rule(so):
         (0, 250, 250, 400, 256, (13, 1)),     # ragged, not packable: still the 16x16 tile
         (0, 60, 2000, 2000, 256, (13, 1)),    # 500 tiles of 16x16: two per CU
         (0, 330, 330, 777, 256, (13, 1)),
-        (0, 256, 256, 4096, 256, (11, 8)),    # K > 2048: 64x64 direct in K chunks
+        (0, 256, 256, 4096, 256, (13, 1)),    # one 16x16 tile per CU: K up to 4096 in the waves
+        (0, 256, 512, 4096, 256, (11, 8)),    # two per CU and K > 2048: 64x64 direct in K chunks
+        (0, 128, 128, 8192, 256, (11, 16)),   # K > 4096
         (0, 700, 700, 400, 256, (11, 1)),     # 1936 tiles of 16x16: more than two per CU
         (0, 500, 500, 2000, 256, (11, 3)),    # 64 tiles of 64x64, K > 1024: not the 32x32 tile
         (0, 512, 512, 512, 256, (12, 1)),     # 64 tiles of 64x64
