@@ -191,16 +191,18 @@ def parity(w, A, B, C, got):
     import oracle
     M, N, K = w.M, w.N, w.K
     t0 = time.perf_counter()
+    floor = 0.0
     if w.op == "sgemm":
         ref, den = oracle.sgemm(M, N, K, w.alpha, A.numpy(), K, B.numpy(), N, w.beta, C.numpy(), N)
         tol = 1e-5
     else:
         bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+        fmt = "bf16" if w.op == "bgemm_bias_gelu" else "f16"
         ref, den = oracle.hgemm_bias_act(M, N, K, w.alpha, bits(A), K, bits(B), N, C.numpy(),
-                                         oracle.ACT_GELU_TANH,
-                                         fmt="bf16" if w.op == "bgemm_bias_gelu" else "f16")
+                                         oracle.ACT_GELU_TANH, fmt=fmt)
         tol = 1e-2
-    e = oracle.normalized_error(got.float().numpy(), ref, den)
+        floor = oracle.OUTPUT_FLOOR[fmt]
+    e = oracle.normalized_error(got.float().numpy(), ref, den, floor)
     k = int(np.argmax(e))
     return {"max_err": float(e[k // N, k % N]), "where": [k // N, k % N], "tol": tol,
             "entries": M * N, "pass": bool(e.max() <= tol),

@@ -218,16 +218,24 @@ bf16_to_double = _default.bf16_to_double
 gelu_tanh = _default.gelu_tanh
 
 
-def normalized_error(got, ref, den):
-    """Per-element |got - ref| / den, the parity measure.
+# Half the spacing of the subnormal numbers of each 16-bit output format: the
+# least error with which a value below the format's normal range can be stored.
+OUTPUT_FLOOR = {"f16": 2.0 ** -25, "bf16": 2.0 ** -134}
 
-    Where den == 0 the entry must match exactly (error 0, else inf); a
-    non-finite output gives inf.  The maximum over all entries is compared with
-    the tolerance of the precision under test."""
+
+def normalized_error(got, ref, den, out_floor=0.0):
+    """Per-element max(|got - ref| - out_floor, 0) / den, the parity measure.
+
+    out_floor is OUTPUT_FLOOR[fmt] for a 16-bit output: an entry whose exact value
+    lies below the format's normal range cannot be stored closer than that, so
+    only the error beyond it counts (0 for FP32).  Where den == 0 the entry must
+    match within out_floor (error 0, else inf); a non-finite output gives inf.
+    The maximum over all entries is compared with the tolerance of the precision
+    under test."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     den = np.asarray(den, dtype=np.float64)
-    diff = np.abs(got - ref)
+    diff = np.maximum(np.abs(got - ref) - out_floor, 0.0)
     pos = den > 0
     with np.errstate(divide="ignore", invalid="ignore"):
         e = np.where(pos, diff / np.where(pos, den, 1.0), np.where(diff == 0, 0.0, np.inf))

@@ -58,7 +58,7 @@ def hgemm_error(M, N, K, alpha, A, lda, B, ldb, bias, act, got, ldc):
                                      lda, B.view(torch.int16).numpy().view(np.uint16), ldb,
                                      None if bias is None else bias.numpy(), act, fmt=fmt)
     g = got.cpu().float().numpy().reshape(-1, ldc)[:M, :N]
-    e = oracle.normalized_error(g, ref, den)
+    e = oracle.normalized_error(g, ref, den, oracle.OUTPUT_FLOOR[fmt])
     return float(e.max()) if e.size else 0.0, np.unravel_index(int(e.argmax()), e.shape) if e.size else None
 
 

@@ -68,7 +68,9 @@ def main():
             ref, den = oracle.hgemm_bias_act(M, N, K, w.alpha, bits(A), K, bits(B), N, C.numpy(),
                                              oracle.ACT_GELU_TANH, fmt=fmt)
             tol, dtype = 1e-2, fmt
-        e = oracle.normalized_error(got, ref, den).reshape(-1)
+        e = oracle.normalized_error(got, ref, den,
+                                    oracle.OUTPUT_FLOOR[dtype] if dtype in oracle.OUTPUT_FLOOR
+                                    else 0.0).reshape(-1)
         k = int(np.argmax(e))
         ki, kj = divmod(k, N)
         q = np.quantile(e, [0.5, 0.99, 0.9999])

@@ -4,6 +4,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 import oracle
@@ -70,3 +71,28 @@ def test_pins_catch_planted_mistake(name, tmp_path):
         return  # crashed: caught
     bad = json.loads(proc.stdout.strip().splitlines()[-1])
     assert bad, "no pin noticed the planted mistake %s" % name
+
+
+def test_measure_counts_16_bit_output_rounding_only_below_the_normal_range():
+    # binary16: the exact value 2^-26 cannot be stored; 0 is the nearest value the
+    # format has, and its error 2^-26 lies within half the subnormal spacing.
+    floor = oracle.OUTPUT_FLOOR["f16"]
+    assert floor == 2.0 ** -25
+    tiny_ref, tiny_den = np.array([2.0 ** -26]), np.array([2.0 ** -25])
+    assert oracle.normalized_error([0.0], tiny_ref, tiny_den, floor)[0] == 0.0
+    # without the floor the same entry reads 0.5: the measure alone would ask for
+    # a value the format does not have
+    assert oracle.normalized_error([0.0], tiny_ref, tiny_den)[0] == 0.5
+    # an error beyond the floor still counts in full past it
+    e = oracle.normalized_error([0.0], np.array([2.0 ** -20]), np.array([2.0 ** -20]), floor)[0]
+    assert e == (2.0 ** -20 - 2.0 ** -25) / 2.0 ** -20
+    # in the normal range the floor changes nothing measurable: a 1e-3 error of a
+    # value of 1 reads 1e-3 to within 2^-25
+    e = oracle.normalized_error([1.001], np.array([1.0]), np.array([1.0]), floor)[0]
+    assert abs(e - 1e-3) < 1e-7
+    # bfloat16 has the exponent range of binary32: its floor is far below any value
+    # these products produce
+    assert oracle.OUTPUT_FLOOR["bf16"] == 2.0 ** -134
+    # den == 0: exact, or within the floor
+    assert oracle.normalized_error([2.0 ** -26], np.array([0.0]), np.array([0.0]), floor)[0] == 0.0
+    assert oracle.normalized_error([2.0 ** -24], np.array([0.0]), np.array([0.0]), floor)[0] == np.inf
