@@ -339,7 +339,10 @@ int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   //    1024^3: 185 vs 155); with K split (below) it also takes smaller outputs
   //    once K reaches 4096 (512 x 512 x 8192 in 8 chunks: 225 vs 188 for 64x64
   //    in 16; 512 x 512 x 4096 in 4: 151 vs 137; 300 x 500 x 4096, 12 tiles:
-  //    26 us vs 62 for 64x64 in 22 chunks; 128 x 128 x 8192: 13.6 vs 16.7).
+  //    26 us vs 62 for 64x64 in 22 chunks; 128 x 128 x 8192: 13.6 vs 16.7), and
+  //    from 16 tiles already once K reaches 1024 (64 x 4096 x 2049: 17.6 us vs
+  //    43.7 for the eight-wave 256x256 tile below; 100 x 4096 x 3000: 20.2 vs
+  //    55.5; 200 x 3000 x 2500: 27.8 vs 61.0; 96 x 6000 x 3000: 23.1 vs 56.8).
   //  * Smaller outputs: the register-staged 64x64 tile, which spreads them over
   //    the most CUs with split-K -- unless it would run bounds-checked (ragged
   //    M, N or K) and there are 16 tiles of 128x256: then 128x256 direct-to-LDS
@@ -354,7 +357,8 @@ int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);
   const bool direct = operands_ok;
   if (direct && K >= 128 && (t_large >= cus || t_med > 2L * cus)) return K >= 2048 ? 7 : 6;
-  if (direct && t_med <= 2L * cus && (4 * t_med >= cus || K >= 4096)) return 8;
+  if (direct && t_med <= 2L * cus && (4 * t_med >= cus || K >= 4096 || (t_med >= 16 && K >= 1024)))
+    return 8;
   if (!direct && t_large >= cus && K >= 512) return 0;
   const int reg = t_med >= 2L * cus ? 1 : 2;
   const int bm = half_tile_bm(reg);

@@ -209,6 +209,8 @@ def test_config_rule(so):
         (1, 256, 256, 4096, 256, (9, 1)),      # one 16x16 tile per CU, K <= 4096
         (1, 512, 512, 4096, 256, (8, 8)),      # 1024 tiles of 16x16 and K > 2048: 128x128 direct
         (1, 700, 700, 400, 256, (4, 1)),       # 1936 tiles of 16x16: not the K-split tile
+        (1, 64, 4096, 2049, 256, (8, 4)),      # 32 tiles of 128x128, K >= 1024: direct, split
+        (1, 100, 4096, 3000, 256, (8, 5)),
         (1, 1024, 1024, 4096, 256, (8, 4)),    # 64 tiles of 128x128: direct 128x128 in 4 chunks
         (1, 1024, 1024, 4095, 256, (8, 4)),    # the same with K ragged (A packed: half rows)
         (1, 2048, 1024, 8192, 256, (8, 2)),    # 128 tiles: 2 chunks
