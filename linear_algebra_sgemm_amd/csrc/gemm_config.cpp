@@ -375,13 +375,16 @@ int half_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
 int half_rule_splits(int M, int N, int K, int tile, int cus) {
   if (tile == 8) {
     // The 128x128 direct-to-LDS tile: split outputs of at most half as many
-    // tiles as CUs to about one workgroup per CU, in chunks of at least 512
+    // tiles as CUs to about one workgroup per CU, in chunks of at least 1024
     // (1024 x 1024 x 4096, 64 tiles: 209 TFLOP/s unsplit, 301 in 2, 358 in 4,
-    // 293 in 8; 2048 x 1024 x 8192, 128 tiles: 453, 620 in 2, 604 in 4).
+    // 293 in 8; 2048 x 1024 x 8192, 128 tiles: 453, 620 in 2, 604 in 4; per
+    // call, against chunks of 512: 128 x 8192 x 1024 unsplit 10.5 us vs 14.6 in
+    // 2, 128 x 4096 x 4096 in 4 18.6 vs 20.0 in 8, 128 x 2048 x 8192 in 8 19.2
+    // vs 20.6 in 16).
     const long tiles = ceil_div(M, 128) * ceil_div(N, 128);
     if (2 * tiles > cus) return 1;
     long s = cus / tiles;
-    if (s > K / 512) s = K / 512;
+    if (s > K / 1024) s = K / 1024;
     if (s > 16) s = 16;
     return s < 1 ? 1 : (int)s;
   }

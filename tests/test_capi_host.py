@@ -202,19 +202,19 @@ def test_config_rule(so):
         (1, 4096, 2048, 4096, 256, (8, 1)),   # 512 tiles of 128x128: one round at two per CU
         (1, 4096, 4096, 256, 256, (6, 1)),    # K = 256: still the eight-wave tile
         (1, 4096, 4096, 64, 256, (1, 1)),     # K < 128: register-staged 128x128
-        (1, 300, 500, 4096, 256, (8, 8)),      # 12 tiles of 128x128, K >= 4096: direct, 8 chunks
+        (1, 300, 500, 4096, 256, (8, 4)),      # 12 tiles of 128x128, K >= 4096: direct, chunks of 1024
         (1, 256, 256, 256, 256, (9, 1)),       # 256 tiles of 16x16: K split over the waves
         (1, 250, 250, 400, 256, (9, 1)),       # ragged, any operands
         (1, 500, 500, 400, 256, (9, 1)),       # 1024 tiles of 16x16, K <= 2048
         (1, 256, 256, 4096, 256, (9, 1)),      # one 16x16 tile per CU, K <= 4096
-        (1, 512, 512, 4096, 256, (8, 8)),      # 1024 tiles of 16x16 and K > 2048: 128x128 direct
+        (1, 512, 512, 4096, 256, (8, 4)),      # 1024 tiles of 16x16 and K > 2048: 128x128 direct
         (1, 700, 700, 400, 256, (4, 1)),       # 1936 tiles of 16x16: not the K-split tile
-        (1, 64, 4096, 2049, 256, (8, 4)),      # 32 tiles of 128x128, K >= 1024: direct, split
-        (1, 100, 4096, 3000, 256, (8, 5)),
+        (1, 64, 4096, 2049, 256, (8, 2)),      # 32 tiles of 128x128, K >= 1024: direct, split
+        (1, 100, 4096, 3000, 256, (8, 2)),
         (1, 1024, 1024, 4096, 256, (8, 4)),    # 64 tiles of 128x128: direct 128x128 in 4 chunks
-        (1, 1024, 1024, 4095, 256, (8, 4)),    # the same with K ragged (A packed: half rows)
+        (1, 1024, 1024, 4095, 256, (8, 3)),    # the same with K ragged (A packed: half rows)
         (1, 2048, 1024, 8192, 256, (8, 2)),    # 128 tiles: 2 chunks
-        (1, 512, 512, 4096, 256, (8, 8)),      # 16 tiles of 128x128, K >= 4096: 8 chunks of 512
+        (1, 512, 512, 4096, 256, (8, 4)),      # 16 tiles of 128x128, K >= 4096: 4 chunks of 1024
         (1, 512, 512, 2048, 256, (9, 1)),      # 1024 tiles of 16x16, K <= 2048
         (1, 512, 512, 256, 256, (9, 1)),       # 1024 tiles of 16x16, short K
     ]
