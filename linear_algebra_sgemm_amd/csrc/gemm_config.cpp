@@ -101,9 +101,11 @@ long round_use(long tiles, int cus, int per_cu) {
 
 // Built-in tile rule, measured on MI355X (the size sweep over powers of two and
 // a sweep of ragged shapes):
-//  * Outputs of at most one 16x16 tile per CU with K at most 4096, or two per
-//    CU with K at most 2048: the 16x16 tile whose eight waves split K (tile
-//    13), ragged or not; per call, against the choice before it: 250 x 250 x
+//  * Outputs of at most one 16x16 tile per CU with K at most 4096, two per CU
+//    with K at most 2048, or four per CU with K at most 512: the 16x16 tile
+//    whose eight waves split K (tile 13), ragged or not (four per CU, against
+//    the 32x32 tile: 300 x 520 x 400: 6.5 vs 9.4 us; 1000 x 200 x 400: 7.6 vs
+//    9.5; 130 x 1000 x 400: 6.2 vs 9.0; but 500 x 500 x 100: 5.5 vs 5.0); per call, against the choice before it: 250 x 250 x
 //    400: 4.5 vs 20.1 us (64x64 register-staged); 200 x 120 x 2000: 8.3 vs 35.2
 //    (32x32); 300 x 520 x 777: 15.6 vs 16.8; 60 x 2000 x 2000: 21.0 vs 34.3;
 //    330 x 330 x 777: 12.5 vs 14.2; 128 x 128 x 4096: 11.0 vs 15.4 (64x64
@@ -158,7 +160,8 @@ long round_use(long tiles, int cus, int per_cu) {
 int sgemm_rule_tile(int M, int N, int K, int cus, bool operands_ok) {
   // Small outputs first: see the rule's description above.
   const long t16 = ceil_div(M, 16) * ceil_div(N, 16);
-  if ((t16 <= cus && K <= 4096) || (t16 <= 2L * cus && K <= 2048)) return 13;
+  if ((t16 <= cus && K <= 4096) || (t16 <= 2L * cus && K <= 2048) || (t16 <= 4L * cus && K <= 512))
+    return 13;
   const long t_large = ceil_div(M, 256) * ceil_div(N, 256);
   const long t_tall = ceil_div(M, 128) * ceil_div(N, 256);
   const long t_med = ceil_div(M, 128) * ceil_div(N, 128);

@@ -152,7 +152,7 @@ def test_config_rule(so):
         (0, 4000, 4000, 4000, 256, (9, 1)),   # ragged M, N, K likewise
         (0, 4096, 4096, 4002, 256, (9, 1)),   # lda = 4002: A copied 4 bytes at a time
         (0, 4096, 4090, 4096, 256, (9, 1)),   # N not a multiple of 4: B packed first
-        (0, 64, 4090, 64, 256, (2, 1)),       # packing B would cost more than it saves
+        (0, 64, 4090, 64, 256, (13, 1)),      # 1024 tiles of 16x16, short K: any operands, no packing
         (0, 256, 256, 256, 256, (13, 1)),     # 256 tiles of 16x16: one per CU, K in the waves
         (0, 256, 256, 1024, 256, (13, 1)),
         (0, 250, 250, 400, 256, (13, 1)),     # ragged, not packable: still the 16x16 tile
@@ -163,9 +163,10 @@ def test_config_rule(so):
         (0, 128, 128, 8192, 256, (11, 16)),   # K > 4096
         (0, 700, 700, 400, 256, (11, 1)),     # 1936 tiles of 16x16: more than two per CU
         (0, 500, 500, 2000, 256, (11, 3)),    # 64 tiles of 64x64, K > 1024: not the 32x32 tile
-        (0, 512, 512, 512, 256, (12, 1)),     # 64 tiles of 64x64
-        (0, 512, 512, 480, 256, (12, 1)),
-        (0, 512, 512, 500, 256, (12, 1)),     # K not a multiple of 32: still 32x32
+        (0, 512, 512, 777, 256, (12, 1)),     # four 16x16 tiles per CU, 512 < K <= 1024: 32x32
+        (0, 512, 512, 512, 256, (13, 1)),     # 1024 tiles of 16x16 (four per CU), K <= 512
+        (0, 512, 512, 480, 256, (13, 1)),
+        (0, 512, 512, 500, 256, (13, 1)),     # K not a multiple of 32
         (0, 512, 576, 512, 256, (11, 1)),     # 72 tiles of 64x64
         (0, 1000, 3000, 777, 256, (11, 1)),   # 752 tiles
         (0, 2048, 2048, 2048, 256, (10, 1)),  # 64 tiles of 256x256, 256 of 128x128: direct 128x128
@@ -187,8 +188,8 @@ def test_config_rule(so):
         (0, 600, 600, 5000, 256, (11, 5)),    # 100 tiles: about two workgroups per CU
         (0, 4096, 4096, 4096, 64, (9, 1)),
         (0, 128, 128, 16384, 256, (11, 16)),  # 4 tiles; 128 chunks by CUs, capped at 16
-        (0, 300, 520, 100, 256, (12, 1)),     # ragged and small: 32x32, bounds-checked
-        (0, 300, 521, 100, 256, (2, 1)),      # N odd and too small to pack: register-staged
+        (0, 300, 520, 100, 256, (13, 1)),     # ragged and small: the K-split tile
+        (0, 300, 521, 100, 256, (13, 1)),     # N odd: the K-split tile takes any operands
         (1, 4096, 14336, 4096, 256, (7, 1)),  # whole 256-tiles, long K: eight waves + tail split
         (1, 4096, 4096, 4096, 256, (6, 1)),   # no partial round: eight waves, no split
         (1, 4096, 4096, 1024, 256, (6, 1)),   # shorter K: eight waves, no split
